@@ -1,0 +1,319 @@
+"""Pins of the CPU oracle against things other than itself: a library
+attention routine (torch SDPA in float64), closed forms, invariants of
+the paging relabeling and of softmax, and hand-derived worked examples.
+
+Each test names what it would catch if the oracle were wrong."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from paged_kv_cache_213_amd import workloads as W
+from tests import helpers as H
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _scatter_dense(Kd, Vd, lens, perm_seed=0, pool_extra=3):
+    """Place dense per-sequence K/V ([Hkv][L][D] float32) into a shuffled
+    block pool -- the inverse of the gather, written as a scatter."""
+    rng = np.random.default_rng(perm_seed)
+    Hkv, _, D = Kd[0].shape
+    nbs = [(L + 15) // 16 for L in lens]
+    NB = sum(nbs) + pool_extra
+    perm = rng.permutation(NB)
+    kc = np.full((NB, Hkv, 16, D), np.nan, np.float32)
+    vc = np.full((NB, Hkv, D, 16), np.nan, np.float32)
+    bt = np.full((len(lens), max(1, max(nbs))), -1, np.int32)
+    cur = 0
+    for i, L in enumerate(lens):
+        for j in range(nbs[i]):
+            b = perm[cur]
+            cur += 1
+            bt[i, j] = b
+            for o in range(16):
+                t = 16 * j + o
+                if t < L:
+                    kc[b, :, o, :] = Kd[i][:, t, :]
+                    vc[b, :, :, o] = Vd[i][:, t, :]
+    return kc, vc, bt, NB
+
+
+def _run(q, kc, vc, bt, lens, scale, hq, hkv, d, qsl=None, q_dtype="f32", kv_dtype="f32", **kw):
+    return oracle.paged_attention(q, kc, vc, bt, np.asarray(lens, np.int32), scale,
+                                  q_dtype=q_dtype, kv_dtype=kv_dtype, num_q_heads=hq,
+                                  num_kv_heads=hkv, head_dim=d, query_start_loc=qsl, **kw)
+
+
+def _sdpa(q, K, V, scale, causal=False):
+    """torch's attention in float64: q [Hq][n][D], K/V [Hkv][L][D]."""
+    qt = torch.from_numpy(np.asarray(q, np.float64))[None]
+    kt = torch.from_numpy(np.asarray(K, np.float64))[None]
+    vt = torch.from_numpy(np.asarray(V, np.float64))[None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, scale=scale, is_causal=causal, enable_gqa=True)
+    return o[0].numpy()
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(2, 1, 64), (8, 2, 32), (6, 3, 16), (4, 4, 8)])
+def test_decode_matches_torch_sdpa(hq, hkv, d):
+    """Catches: gather index errors, wrong GQA head mapping, missing scale,
+    transposed operands, a softmax over the wrong axis."""
+    rng = np.random.default_rng(hq * 100 + d)
+    lens = [1, 7, 16, 17, 50, 33]
+    Kd = [rng.standard_normal((hkv, L, d)).astype(np.float32) for L in lens]
+    Vd = [rng.standard_normal((hkv, L, d)).astype(np.float32) for L in lens]
+    q = rng.standard_normal((len(lens), hq, d)).astype(np.float32)
+    kc, vc, bt, _ = _scatter_dense(Kd, Vd, lens)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    out, lse = _run(q, kc, vc, bt, lens, scale, hq, hkv, d)
+    for i, L in enumerate(lens):
+        ref = _sdpa(q[i][:, None, :], Kd[i], Vd[i], scale)[:, 0, :]
+        np.testing.assert_allclose(out[i], ref, rtol=0, atol=1e-12)
+        # lse against the logsumexp of explicit scores (torch)
+        G = hq // hkv
+        for h in range(hq):
+            s = scale * (torch.from_numpy(Kd[i][h // G].astype(np.float64))
+                         @ torch.from_numpy(q[i, h].astype(np.float64)))
+            assert abs(lse[i, h] - torch.logsumexp(s, 0).item()) < 1e-12
+
+
+def test_full_prefill_span_matches_causal_sdpa():
+    """A span covering the whole context (n = L) is plain causal attention.
+    Catches: off-by-one in the causal boundary, wrong span positions."""
+    rng = np.random.default_rng(5)
+    hq, hkv, d, L = 4, 2, 16, 37
+    Kd = [rng.standard_normal((hkv, L, d)).astype(np.float32)]
+    Vd = [rng.standard_normal((hkv, L, d)).astype(np.float32)]
+    q = rng.standard_normal((L, hq, d)).astype(np.float32)
+    kc, vc, bt, _ = _scatter_dense(Kd, Vd, [L])
+    qsl = np.array([0, L], np.int32)
+    out, _ = _run(q, kc, vc, bt, [L], 0.25, hq, hkv, d, qsl=qsl)
+    ref = _sdpa(np.transpose(q, (1, 0, 2)), Kd[0], Vd[0], 0.25, causal=True)
+    np.testing.assert_allclose(out, np.transpose(ref, (1, 0, 2)), rtol=0, atol=1e-12)
+
+
+def test_partial_span_rows_equal_truncated_decodes():
+    """Row j of a chunk of n tokens at the end of a context of L equals a
+    decode over the first L-n+j+1 keys (the chunk sees only what is
+    present, plus itself)."""
+    rng = np.random.default_rng(6)
+    hq, hkv, d = 4, 1, 32
+    L, n = 45, 11
+    Kd = [rng.standard_normal((hkv, L, d)).astype(np.float32)]
+    Vd = [rng.standard_normal((hkv, L, d)).astype(np.float32)]
+    q = rng.standard_normal((n, hq, d)).astype(np.float32)
+    kc, vc, bt, _ = _scatter_dense(Kd, Vd, [L])
+    out, lse = _run(q, kc, vc, bt, [L], 0.1875, hq, hkv, d, qsl=np.array([0, n], np.int32))
+    for j in range(n):
+        Lj = L - n + j + 1
+        o1, l1 = _run(q[j:j + 1], kc, vc, bt, [Lj], 0.1875, hq, hkv, d)
+        np.testing.assert_array_equal(out[j], o1[0])
+        np.testing.assert_array_equal(lse[j], l1[0])
+        ref = _sdpa(q[j][:, None, :], Kd[0][:, :Lj], Vd[0][:, :Lj], 0.1875)[:, 0, :]
+        np.testing.assert_allclose(out[j], ref, rtol=0, atol=1e-12)
+
+
+def test_block_permutation_is_pure_relabeling():
+    """Moving every block to another physical slot and rewriting the table
+    leaves the result bitwise unchanged."""
+    wl = W.make_config("c1")
+    _, _, post = H.oracle_host(wl)
+    out0, lse0 = oracle.run_workload(wl, post)
+    rng = np.random.default_rng(1)
+    perm = rng.permutation(wl.num_blocks)  # new id of old block b = perm[b]
+    k2 = np.empty_like(post["k_cache"])
+    v2 = np.empty_like(post["v_cache"])
+    k2[perm] = post["k_cache"]
+    v2[perm] = post["v_cache"]
+    bt2 = np.where(wl.block_tables >= 0, perm[np.maximum(wl.block_tables, 0)], -1).astype(np.int32)
+    wl2 = W.custom_workload(wl.context_lens, num_q_heads=2, num_kv_heads=1, head_dim=64,
+                            q_dtype="f32", kv_dtype="f32", block_tables=bt2,
+                            num_blocks=wl.num_blocks)
+    out1, lse1 = oracle.run_workload(wl2, dict(post, k_cache=k2, v_cache=v2))
+    np.testing.assert_array_equal(out0, out1)
+    np.testing.assert_array_equal(lse0, lse1)
+
+
+def test_length_one_returns_the_value_row():
+    """With one key the weight is exactly 1: out = v_0 bitwise."""
+    rng = np.random.default_rng(2)
+    d = 64
+    Kd = [rng.standard_normal((1, 1, d)).astype(np.float32)]
+    Vd = [rng.standard_normal((1, 1, d)).astype(np.float32)]
+    q = rng.standard_normal((1, 3, d)).astype(np.float32)
+    kc, vc, bt, _ = _scatter_dense(Kd, Vd, [1])
+    out, lse = _run(q, kc, vc, bt, [1], 0.125, 3, 1, d)
+    for h in range(3):
+        np.testing.assert_array_equal(out[0, h], Vd[0][0, 0].astype(np.float64))
+        s = 0.125 * float(np.dot(q[0, h].astype(np.float64), Kd[0][0, 0].astype(np.float64)))
+        assert abs(lse[0, h] - s) < 1e-12
+
+
+@pytest.mark.parametrize("L", [2, 16, 33, 300])
+def test_identical_keys_give_mean_of_values(L):
+    rng = np.random.default_rng(L)
+    d = 16
+    k = rng.standard_normal(d).astype(np.float32)
+    Kd = [np.tile(k, (1, L, 1))]
+    Vd = [rng.standard_normal((1, L, d)).astype(np.float32)]
+    q = rng.standard_normal((1, 2, d)).astype(np.float32)
+    kc, vc, bt, _ = _scatter_dense(Kd, Vd, [L])
+    out, lse = _run(q, kc, vc, bt, [L], 0.375, 2, 1, d)
+    mean = Vd[0][0].astype(np.float64).mean(axis=0)
+    for h in range(2):
+        np.testing.assert_allclose(out[0, h], mean, rtol=0, atol=1e-12)
+        s = 0.375 * float(np.dot(q[0, h].astype(np.float64), k.astype(np.float64)))
+        assert abs(lse[0, h] - (s + math.log(L))) < 1e-12
+
+
+def test_zero_scale_gives_mean_of_values():
+    rng = np.random.default_rng(3)
+    L, d = 40, 8
+    Kd = [rng.standard_normal((1, L, d)).astype(np.float32)]
+    Vd = [rng.standard_normal((1, L, d)).astype(np.float32)]
+    q = rng.standard_normal((1, 1, d)).astype(np.float32)
+    kc, vc, bt, _ = _scatter_dense(Kd, Vd, [L])
+    out, lse = _run(q, kc, vc, bt, [L], 0.0, 1, 1, d)
+    np.testing.assert_allclose(out[0, 0], Vd[0][0].astype(np.float64).mean(0), atol=1e-12)
+    assert abs(lse[0, 0] - math.log(L)) < 1e-12
+
+
+def test_needle_in_every_block():
+    """A key aligned with q and scaled up dominates: the output is that
+    key's value row. Moving the needle through every block catches a
+    dropped or duplicated block that a loose tolerance would miss."""
+    rng = np.random.default_rng(4)
+    L, d = 70, 16
+    q = rng.standard_normal((1, 1, d)).astype(np.float32)
+    for t_star in range(0, L, 7):
+        Kd = [0.01 * rng.standard_normal((1, L, d)).astype(np.float32)]
+        Kd[0][0, t_star] = 40.0 * q[0, 0]
+        Vd = [rng.standard_normal((1, L, d)).astype(np.float32)]
+        kc, vc, bt, _ = _scatter_dense(Kd, Vd, [L], perm_seed=t_star)
+        out, _ = _run(q, kc, vc, bt, [L], 1.0, 1, 1, d)
+        np.testing.assert_allclose(out[0, 0], Vd[0][0, t_star], atol=1e-9)
+
+
+@pytest.mark.parametrize("P", [16, 48, 512])
+def test_split_merge_reaches_the_unsplit_result(P):
+    """Partial results over partitions merged by log-sum-exp equal the
+    one-pass result (to rounding), for decodes and a causal span."""
+    wl = W.custom_workload([5, 16, 17, 100, 511, 513, 700, 1], [1, 1, 1, 1, 1, 1, 30, 1],
+                           num_q_heads=4, num_kv_heads=2, head_dim=32, q_dtype="f32",
+                           kv_dtype="f32", seed=9)
+    _, _, post = H.oracle_host(wl)
+    qsl = wl.query_start_loc
+    kw = dict(q_dtype="f32", kv_dtype="f32", num_q_heads=4, num_kv_heads=2, head_dim=32,
+              query_start_loc=qsl)
+    o1, l1 = oracle.paged_attention(post["q"], post["k_cache"], post["v_cache"],
+                                    wl.block_tables, wl.context_lens, wl.scale, **kw)
+    o2, l2 = oracle.paged_attention_split(post["q"], post["k_cache"], post["v_cache"],
+                                          wl.block_tables, wl.context_lens, wl.scale, P, **kw)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=1e-12, atol=1e-12)
+
+
+def test_softmax_shift_invariance_at_huge_scores():
+    """Adding a component to every key that raises all scores by ~1e4
+    leaves the output unchanged (the max is subtracted) and finite."""
+    rng = np.random.default_rng(8)
+    L, d = 50, 8
+    q = np.zeros((1, 1, d), np.float32)
+    q[0, 0, 0] = 1.0
+    q[0, 0, 1:] = rng.standard_normal(d - 1)
+    Kd0 = rng.standard_normal((1, L, d)).astype(np.float32)
+    Kd0[..., 0] = 0.0
+    Kd1 = Kd0.copy()
+    Kd1[..., 0] = 1.0e4  # adds exactly 1e4 to every score
+    Vd = [rng.standard_normal((1, L, d)).astype(np.float32)]
+    outs = []
+    for Kd in (Kd0, Kd1):
+        kc, vc, bt, _ = _scatter_dense([Kd], Vd, [L])
+        o, lse = _run(q, kc, vc, bt, [L], 1.0, 1, 1, d)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        outs.append((o, lse))
+    np.testing.assert_allclose(outs[1][0], outs[0][0], atol=1e-9)
+    assert abs(outs[1][1][0, 0] - outs[0][1][0, 0] - 1e4) < 1e-8
+
+
+def test_empty_context_gives_zero_and_neg_inf():
+    kc = np.full((2, 1, 16, 8), np.nan, np.float32)
+    vc = np.full((2, 1, 8, 16), np.nan, np.float32)
+    bt = np.full((1, 1), -1, np.int32)
+    q = np.ones((1, 2, 8), np.float32)
+    out, lse = _run(q, kc, vc, bt, [0], 0.5, 2, 1, 8)
+    assert np.all(out == 0.0) and np.all(np.isneginf(lse))
+
+
+def test_unused_slots_are_never_read():
+    """NaN in every slot outside the contexts leaves the output finite
+    (the poisoned workloads rely on this)."""
+    for name in ("c1",):
+        wl = W.make_config(name)
+        _, _, post = H.oracle_host(wl)
+        out, lse = oracle.run_workload(wl, post)
+        assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+def _load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_worked_examples_by_hand():
+    """Hand-derived closed forms stored in tests/golden (see the file for
+    each derivation)."""
+    g = _load_golden("worked_examples.json")
+    for case in g["cases"]:
+        D = len(case["q"][0][0])
+        lens = case["context_lens"]
+        Kd = [np.asarray(k, np.float32) for k in case["k"]]
+        Vd = [np.asarray(v, np.float32) for v in case["v"]]
+        q = np.asarray(case["q"], np.float32)
+        kc, vc, bt, _ = _scatter_dense(Kd, Vd, lens)
+        qsl = None if case.get("query_start_loc") is None else np.asarray(case["query_start_loc"], np.int32)
+        hq, hkv = case["num_q_heads"], case["num_kv_heads"]
+        out, lse = _run(q, kc, vc, bt, lens, case["scale"], hq, hkv, D, qsl=qsl)
+        np.testing.assert_allclose(out, np.asarray(case["expect_out"]), rtol=0,
+                                   atol=case["atol"], err_msg=case["name"])
+        if "expect_lse" in case:
+            np.testing.assert_allclose(lse, np.asarray(case["expect_lse"]), rtol=0,
+                                       atol=case["atol"], err_msg=case["name"])
+
+
+def test_fp8_cache_attention_matches_sdpa_on_dequantized_values():
+    """fp8 KV: the oracle's dequantization (code value times the block's
+    scale) agrees with torch's e4m3fn decode times the scale, fed to SDPA."""
+    wl = W.make_config("c5", small=True)
+    _, _, post = H.oracle_host(wl)
+    out, _ = oracle.run_workload(wl, post, seq_subset=np.arange(0, wl.num_seqs, 3))
+    q = H.q_float64(wl, post)
+    for i in range(0, wl.num_seqs, 3):
+        K, V = H.dense_kv_from_host(wl, post, i)
+        ref = _sdpa(q[i][:, None, :], K, V, wl.scale)[:, 0, :]
+        np.testing.assert_allclose(out[i], ref, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_small_configs_match_sdpa(name):
+    """Every configuration's (reduced) batch, including the hybrid span and
+    shared blocks, agrees with SDPA on densely gathered K/V."""
+    wl = W.make_config(name, small=True)
+    _, _, post = H.oracle_host(wl)
+    out, lse = oracle.run_workload(wl, post)
+    q = H.q_float64(wl, post)
+    qsl = wl.query_start_loc
+    pos = wl.token_positions()
+    for i in range(wl.num_seqs):
+        K, V = H.dense_kv_from_host(wl, post, i)
+        assert np.all(np.isfinite(K)) and np.all(np.isfinite(V))
+        rows = range(qsl[i], qsl[i + 1])
+        for r in rows:
+            Lr = int(pos[r]) + 1
+            ref = _sdpa(q[r][:, None, :], K[:, :Lr], V[:, :Lr], wl.scale)[:, 0, :]
+            np.testing.assert_allclose(out[r], ref, rtol=0, atol=1e-10)
