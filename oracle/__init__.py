@@ -15,6 +15,7 @@ patterns, "fp8" arrays are uint8 e4m3fn codes.
 from __future__ import annotations
 
 import ctypes
+import hashlib
 import os
 import subprocess
 
@@ -23,25 +24,42 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _SO = os.path.join(_HERE, "liboracle.so")
+_STAMP = _SO + ".src-sha256"
 _DT = {"f32": 0, "bf16": 1, "fp8": 2}
 _NP = {"f32": np.float32, "bf16": np.uint16, "fp8": np.uint8}
 _lib = None
 
 
+def _src_hash() -> str:
+    with open(_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _fresh() -> bool:
+    """The built library exists and was compiled from the current source."""
+    if not (os.path.exists(_SO) and os.path.exists(_STAMP)):
+        return False
+    with open(_STAMP) as f:
+        return f.read().strip() == _src_hash()
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c with gcc (-O2, no fast-math, OpenMP)."""
-    if force or not os.path.exists(_SO):
+    if force or not _fresh():
+        digest = _src_hash()
         tmp = _SO + f".tmp{os.getpid()}"
         subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
                         "-fno-fast-math", _SRC, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _SO)
+        with open(_STAMP, "w") as f:
+            f.write(digest)
     return _SO
 
 
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        if not _fresh():
             build(force=True)
         lib = ctypes.CDLL(_SO)
         P, I, L, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_long, ctypes.c_float

@@ -254,7 +254,7 @@ static void or_attend_row(const or_args* a, long qrow, int h, const double* K, c
         for (int t = 0; t < nk; ++t) acc += s[t] * V[(long)t * D + d];
         out[d] = acc / Z;
     }
-    *lse = M;
+    *lse = M + log(Z);
 }
 
 /* Attention of one KV-head group of one sequence, all its query tokens. */
