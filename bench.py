@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+One step = one layer's decode step on one batch: append the batch's new K/V
+rows into the paged cache, then paged attention over every sequence's
+context (plan, attention, split merge). The default workload is the
+Llama-3-8B-shaped decode batch (64 sequences, contexts uniform on
+[128, 4096], 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks in a
+shuffled pool 1.25x the blocks needed). Steps rotate over the KV caches of
+``--layers`` distinct layers, so a call never finds its layer's KV in the
+caches left warm by the previous call (32 layers x ~0.7 GB >> the 256 MB
+Infinity Cache), as in a real model.
+
+Prints one JSON line (see the fields at the end of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "KV-read HBM GB/s (% of peak) + decode attention tokens/s, Llama-3-8B shape"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def _threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, budget_s: float = 10.0):
+    """Time the CPU oracle (as it stands) on this workload's batch until
+    about ``budget_s`` of CPU work, on the host's cores."""
+    import oracle
+    from paged_kv_cache_213_amd import workloads as W
+
+    vals = W.materialize(wl, "cpu")
+    q = vals.q.view(__import__("torch").int16).numpy().view(np.uint16) \
+        if wl.q_dtype == "bf16" else vals.q.numpy()
+
+    def bits(t):
+        import torch
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+        return t.contiguous().numpy()
+
+    host = {"q": q}
+    if wl.kv_dtype == "fp8":
+        host["k_scale"] = vals.k_scale.numpy()
+        host["v_scale"] = vals.v_scale.numpy()
+        host["k_cache"] = oracle.fp8_encode_blocks(vals.k_src.numpy(), host["k_scale"])
+        host["v_cache"] = oracle.fp8_encode_blocks(vals.v_src.numpy(), host["v_scale"])
+    else:
+        host["k_cache"] = bits(vals.k_cache).copy()
+        host["v_cache"] = bits(vals.v_cache).copy()
+    oracle.kv_append(host["k_cache"], host["v_cache"], bits(vals.k_new), bits(vals.v_new),
+                     wl.slot_mapping, kv_dtype=wl.kv_dtype, new_dtype=wl.q_dtype,
+                     k_scale=host.get("k_scale"), v_scale=host.get("v_scale"),
+                     num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim)
+    threads = _threads()
+    # grow the sample (a prefix of the batch's sequences, then whole-batch
+    # repeats) until the budget is spent
+    reps, t_total, seqs_done, bytes_done = 0, 0.0, 0, 0
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.kv_elem_bytes
+    n_sub = max(1, min(wl.num_seqs, 4))
+    while t_total < budget_s and reps < 1000:
+        sub = np.arange(n_sub, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.run_workload(wl, host, seq_subset=sub, threads=threads)
+        dt = time.perf_counter() - t0
+        t_total += dt
+        seqs_done += n_sub
+        bytes_done += int(wl.context_lens[:n_sub].astype(np.int64).sum()) * per_tok
+        reps += 1
+        if n_sub < wl.num_seqs and dt < budget_s / 4:
+            n_sub = min(wl.num_seqs, n_sub * 2)
+    return {
+        "value": bytes_done / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{seqs_done} sequence-calls of this batch ({reps} oracle calls, "
+                  f"{t_total:.1f} s, float64 gather-then-softmax, {threads} threads)",
+        "tokens_per_s": seqs_done / t_total,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2", help="c1..c5 (c2 is the headline workload)")
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; the paged-attention path "
+                                   "runs on a single device (sharding is described, not run)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import paged_kv_cache_213_amd as pa
+    from paged_kv_cache_213_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    pa.load_library()  # fails loudly if the HIP library is missing
+
+    wl = W.make_config(args.config, seed=args.seed)
+    P = wl.partition_size if args.partition_size is None else args.partition_size
+    dev = torch.device("cuda")
+    torch.cuda.set_device(0)
+    vals = W.materialize(wl, dev)
+    if wl.kv_dtype == "fp8":
+        raise SystemExit("fp8 workloads: build the cache with kv_append first (not wired yet)")
+    layers = max(1, args.layers)
+    kc = [vals.k_cache] + [vals.k_cache.clone() for _ in range(layers - 1)]
+    vc = [vals.v_cache] + [vals.v_cache.clone() for _ in range(layers - 1)]
+    qs = [vals.q] + [vals.q.clone() for _ in range(layers - 1)]
+    bt = torch.from_numpy(wl.block_tables).to(dev)
+    cl = torch.from_numpy(wl.context_lens).to(dev)
+    qsl = torch.from_numpy(wl.query_start_loc).to(dev)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    out = torch.empty_like(vals.q)
+    lse = torch.empty(wl.num_tokens, wl.num_q_heads, dtype=torch.float32, device=dev)
+    shape = pa.make_shape(vals.q, vals.k_cache, bt, P)
+    nbytes = pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len,
+                                wl.max_query_len)
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        L_ = i % layers
+        if ev is not None:
+            ev[0].record(stream)
+        pa.kv_append(kc[L_], vc[L_], vals.k_new, vals.v_new, slots)
+        if ev is not None:
+            ev[1].record(stream)
+        if wl.is_decode:
+            pa.decode(qs[L_], kc[L_], vc[L_], bt, cl, wl.scale, max_context_len=wl.max_context_len,
+                      partition_size=P, out=out, lse=lse, workspace=ws)
+        else:
+            pa.hybrid(qs[L_], kc[L_], vc[L_], bt, cl, qsl, wl.scale,
+                      max_context_len=wl.max_context_len, max_query_len=wl.max_query_len,
+                      partition_size=P, out=out, lse=lse, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if not torch.isfinite(out.float()).all():
+        raise SystemExit("non-finite attention output")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    att_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    ms_per_step = wall * 1e3 / args.steps
+    kv_bytes = wl.kv_bytes_logical()
+    value = kv_bytes / (ms_per_step / 1e3) / 1e9
+    att_mean = float(att_ms.mean())
+    achieved = kv_bytes / (att_mean / 1e3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 KV, bf16 q"}[wl.kv_dtype],
+        "data": "synthetic (seeded N(0,1) values, shuffled block pool)",
+        "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(wl.num_tokens / (ms_per_step / 1e3), 1),
+        "kv_tokens_per_s": round(float(wl.context_lens.sum()) / (ms_per_step / 1e3), 1),
+        "config": {
+            "workload": f"{wl.name}: {W.CONFIG_TITLES[wl.name]}",
+            "num_seqs": wl.num_seqs,
+            "num_q_tokens": wl.num_tokens,
+            "q_heads": wl.num_q_heads,
+            "kv_heads": wl.num_kv_heads,
+            "head_dim": wl.head_dim,
+            "block_size": 16,
+            "sum_context_len": int(wl.context_lens.sum()),
+            "kv_bytes_per_call": kv_bytes,
+            "partition_size": P or 512,
+            "layers_rotated": layers,
+            "seed": wl.seed,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "attention call (plan + attention + split merge), HIP events",
+            "launch_ms_mean": round(att_mean, 5),
+            "launch_ms_p10_p50_p90": [round(float(np.percentile(att_ms, p)), 5)
+                                      for p in (10, 50, 90)],
+            "append_ms_mean": round(float(app_ms.mean()), 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

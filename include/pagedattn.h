@@ -1,0 +1,151 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged-attention library.
+ *
+ * The library computes attention of each sequence's query tokens over a KV
+ * cache held in fixed 16-token physical blocks that a per-sequence block
+ * table maps from logical positions ("03 -- Engines Papers", section 2:
+ * key trick, block table, and the kernel that must gather K/V from
+ * non-contiguous blocks; "The LLM inference engine playbook", Theme 3).
+ * Query heads are grouped onto KV heads (GQA; "References", GQA entry).
+ * A batch may mix single-token decodes with chunked-prefill spans
+ * ("03 -- Engines Papers", section 3). Long contexts are split into
+ * fixed-size partitions whose partial results are merged by log-sum-exp
+ * (the split-K decode pattern of the playbook's Theme 4; the LSE merge of
+ * "03 -- Engines Papers", section 12). The cache may be stored as FP8 E4M3
+ * with one scale per (block, KV head) (playbook, Themes 3 and 6).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array argument is a DEVICE pointer owned by the caller. The
+ *   library never allocates, frees or synchronizes; every call only
+ *   enqueues kernels on `stream` (a hipStream_t passed as void*, NULL =
+ *   the null stream) and returns. Scratch memory is the caller's
+ *   `workspace`, sized by pa_workspace_bytes.
+ * - Return value: PA_OK (0) or a negative pa_status. Arguments are checked
+ *   on the host before anything is enqueued; a failed check enqueues
+ *   nothing. Data-dependent contract breaches (a block id out of range, a
+ *   context longer than 16 * max_blocks_per_seq, two tokens appending to
+ *   one slot, an append into a block shared with another sequence) are
+ *   NOT detected by the kernels.
+ * - Layouts (row-major, contiguous):
+ *     q, out       [T][Hq][D]           dtype q_dtype (out has q's dtype)
+ *     k_cache      [num_blocks][Hkv][16][D]   token rows of D values
+ *     v_cache      [num_blocks][Hkv][D][16]   D rows of 16 token values
+ *     k_scale, v_scale [num_blocks][Hkv] float32 (FP8 caches only, else NULL)
+ *     block_tables [num_seqs][max_blocks_per_seq] int32
+ *     context_lens [num_seqs] int32: keys each sequence attends over, which
+ *                  INCLUDE its query tokens of this step (append first)
+ *     query_start_loc [num_seqs + 1] int32, exclusive prefix sums of the
+ *                  per-sequence query counts n_i; qsl[0] = 0, qsl[S] = T
+ *     lse          [T][Hq] float32, natural log of the softmax normalizer
+ * - Semantics: sequence i's n_i query tokens are the LAST n_i positions of
+ *   its context; query j (0-based in the span) sits at position
+ *   L_i - n_i + j and sees keys 0 .. L_i - n_i + j inclusive. Query head h
+ *   reads KV head h / (Hq / Hkv). A stored FP8 byte c in block b, KV head g
+ *   means e4m3fn(c) * scale[b][g]. A sequence with context length 0 yields
+ *   a zero output row and lse = -inf.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_BLOCK_SIZE 16
+
+typedef enum pa_dtype {
+    PA_F32 = 0,        /* IEEE binary32 */
+    PA_BF16 = 1,       /* bfloat16 */
+    PA_FP8_E4M3FN = 2  /* OCP FP8 E4M3FN (bias 7, max 448, no inf) */
+} pa_dtype;
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_EINVAL = -1,     /* bad pointer, shape, dtype combination or size */
+    PA_EWORKSPACE = -2, /* workspace NULL or smaller than pa_workspace_bytes */
+    PA_EHIP = -3,       /* a HIP runtime call or kernel launch failed */
+    PA_ENOTSUP = -4     /* valid request this build does not implement */
+} pa_status;
+
+/* Problem shape shared by all calls on one cache. Supported today:
+ * head_dim in {64, 128}; block_size == 16; Hq % Hkv == 0 with
+ * G = Hq / Hkv <= 16; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
+ * (BF16, FP8_E4M3FN)}; partition_size 0 (library default, 512 tokens) or a
+ * positive multiple of 16. */
+typedef struct pa_shape {
+    int32_t num_q_heads;        /* Hq */
+    int32_t num_kv_heads;       /* Hkv */
+    int32_t head_dim;           /* D */
+    int32_t block_size;         /* must be PA_BLOCK_SIZE */
+    int32_t num_blocks;         /* physical blocks in the pool */
+    int32_t max_blocks_per_seq; /* row stride of block_tables */
+    int32_t q_dtype;            /* pa_dtype of q, out, and new K/V rows */
+    int32_t kv_dtype;           /* pa_dtype of the caches */
+    int32_t partition_size;     /* split-KV partition in tokens, 0 = default */
+} pa_shape;
+
+/* Bytes of device workspace the attention calls need for this batch
+ * (work list, per-token partition counts, split partials). Returns 0 when
+ * the shape is invalid. num_q_tokens = T (num_seqs for a decode call);
+ * max_query_len = largest n_i (1 for a decode call). */
+size_t pa_workspace_bytes(const pa_shape* shape, int num_seqs, int num_q_tokens,
+                          int max_context_len, int max_query_len);
+
+/* Decode: one query token per sequence (T = num_seqs, token i belongs to
+ * sequence i). Computes out (and lse if non-NULL) for every sequence.
+ * max_context_len must be >= every context_lens[i] (it sizes the launch;
+ * the library never reads lengths back to the host). Paged KV storage and
+ * its gather: "03 -- Engines Papers", section 2; split-K decode with a
+ * log-sum-exp merge for long contexts: playbook Theme 4 and the first
+ * page's section 12. */
+int pa_paged_attn_decode(const pa_shape* shape, void* out, float* lse, const void* q,
+                         const void* k_cache, const void* v_cache, const float* k_scale,
+                         const float* v_scale, const int32_t* block_tables,
+                         const int32_t* context_lens, int num_seqs, int max_context_len,
+                         float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Hybrid batch: sequences with n_i >= 1 query tokens each (chunked-prefill
+ * spans and decodes together, "03 -- Engines Papers", section 3), T =
+ * num_q_tokens = query_start_loc[num_seqs]. Each span attends causally over
+ * its paged context as stated above. max_query_len >= every n_i. */
+int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const void* q,
+                         const void* k_cache, const void* v_cache, const float* k_scale,
+                         const float* v_scale, const int32_t* block_tables,
+                         const int32_t* context_lens, const int32_t* query_start_loc,
+                         int num_seqs, int num_q_tokens, int max_query_len,
+                         int max_context_len, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* Append this step's new K/V rows into their slots before attention runs
+ * on the same stream. k_new, v_new: [num_tokens][Hkv][D] in q_dtype.
+ * slot_mapping: [num_tokens] int32, slot = physical_block * 16 + offset
+ * (the logical-to-physical mapping of the block table, "03 -- Engines
+ * Papers", section 2); a negative slot skips its token. Same-dtype caches
+ * receive the values bit for bit; an FP8 cache receives
+ * e4m3fn(fp32(new) / scale[block][head]) rounded to nearest-even and
+ * saturated to +-448 (NaN -> 0x7F), using the block's existing scale.
+ * Slots must be distinct and must not lie in a block another sequence
+ * still shares (copy-on-write, same section). */
+int pa_kv_append(const pa_shape* shape, void* k_cache, void* v_cache, const float* k_scale,
+                 const float* v_scale, const void* k_new, const void* v_new,
+                 const int32_t* slot_mapping, int num_tokens, void* stream);
+
+/* Decode n FP8 E4M3FN bytes to float32 with the device's conversion path
+ * (the one the attention kernels use), for inspecting a cache. */
+int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream);
+
+/* Static text for a status code. */
+const char* pa_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,1 +1,202 @@
-"""MI355X-native paged attention (placeholder; the binding follows)."""
+"""MI355X-native paged attention: Python binding of libpagedattn.so.
+
+This module only marshals torch tensors (device memory) and the current
+stream into the C ABI declared in include/pagedattn.h; every step of the
+computation runs in the library's HIP kernels. If the library is missing
+or cannot be loaded, every call raises -- there is no fallback path.
+
+Layouts (see the header for the full contract):
+  q, out   [T][Hq][D]           float32 or bfloat16
+  k_cache  [num_blocks][Hkv][16][D]
+  v_cache  [num_blocks][Hkv][D][16]
+  k_scale, v_scale [num_blocks][Hkv] float32 (fp8 caches, stored as uint8)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3FN = 0, 1, 2
+PA_OK, PA_EINVAL, PA_EWORKSPACE, PA_EHIP, PA_ENOTSUP = 0, -1, -2, -3, -4
+
+_lib = None
+
+
+class PaShape(ctypes.Structure):
+    _fields_ = [
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("partition_size", ctypes.c_int32),
+    ]
+
+
+class PagedAttentionError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpagedattn.so (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise PagedAttentionError(
+            f"{path} is missing: build it with `python -m paged_kv_cache_213_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    S = ctypes.POINTER(PaShape)
+    lib.pa_workspace_bytes.restype = Z
+    lib.pa_workspace_bytes.argtypes = [S, I, I, I, I]
+    lib.pa_paged_attn_decode.restype = I
+    lib.pa_paged_attn_decode.argtypes = [S, P, P, P, P, P, P, P, P, P, I, I, F, P, Z, P]
+    lib.pa_paged_attn_hybrid.restype = I
+    lib.pa_paged_attn_hybrid.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
+    lib.pa_kv_append.restype = I
+    lib.pa_kv_append.argtypes = [S, P, P, P, P, P, P, P, I, P]
+    lib.pa_fp8_e4m3fn_to_f32.restype = I
+    lib.pa_fp8_e4m3fn_to_f32.argtypes = [P, P, I, P]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [I]
+    lib.pa_version.restype = I
+    lib.pa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != PA_OK:
+        msg = load_library().pa_status_string(rc).decode()
+        raise PagedAttentionError(f"{what} failed: {msg} ({rc})")
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", None)):
+        return PA_FP8_E4M3FN
+    raise PagedAttentionError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise PagedAttentionError("all tensors must live in GPU memory")
+    if not t.is_contiguous():
+        raise PagedAttentionError("all tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def make_shape(q, k_cache, block_tables, partition_size: int = 0) -> PaShape:
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if B != 16 or D2 != D:
+        raise PagedAttentionError(f"k_cache shape {tuple(k_cache.shape)} does not match q")
+    return PaShape(Hq, Hkv, D, 16, NB, block_tables.shape[1], _dtype_code(q),
+                   _dtype_code(k_cache), int(partition_size))
+
+
+def workspace_bytes(shape: PaShape, num_seqs: int, num_q_tokens: int, max_context_len: int,
+                    max_query_len: int) -> int:
+    return int(load_library().pa_workspace_bytes(ctypes.byref(shape), num_seqs, num_q_tokens,
+                                                 max_context_len, max_query_len))
+
+
+def _workspace(nbytes: int, device, workspace):
+    import torch
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise PagedAttentionError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, *,
+           max_context_len: int, k_scale=None, v_scale=None, partition_size: int = 0,
+           out=None, lse=None, workspace=None, stream=None):
+    """Paged attention for one query token per sequence.
+
+    q [S][Hq][D]; block_tables [S][max_blocks] int32; context_lens [S] int32
+    (including the new token). Returns out [S][Hq][D] in q's dtype (and
+    fills ``lse`` [S][Hq] float32 when given)."""
+    import torch
+    lib = load_library()
+    shape = make_shape(q, k_cache, block_tables, partition_size)
+    S = q.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = workspace_bytes(shape, S, S, max_context_len, 1)
+    ws = _workspace(nbytes, q.device, workspace)
+    rc = lib.pa_paged_attn_decode(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q),
+                                  _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                  _ptr(block_tables), _ptr(context_lens), S,
+                                  int(max_context_len), float(scale), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "pa_paged_attn_decode")
+    return out
+
+
+def hybrid(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float, *,
+           max_context_len: int, max_query_len: int, k_scale=None, v_scale=None,
+           partition_size: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """Paged attention for a mixed batch of chunked-prefill spans and
+    decodes. q [T][Hq][D] with T = query_start_loc[-1]."""
+    import torch
+    lib = load_library()
+    shape = make_shape(q, k_cache, block_tables, partition_size)
+    T = q.shape[0]
+    S = context_lens.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = workspace_bytes(shape, S, T, max_context_len, max_query_len)
+    ws = _workspace(nbytes, q.device, workspace)
+    rc = lib.pa_paged_attn_hybrid(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q),
+                                  _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                  _ptr(block_tables), _ptr(context_lens), _ptr(query_start_loc),
+                                  S, T, int(max_query_len), int(max_context_len), float(scale),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "pa_paged_attn_hybrid")
+    return out
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, slot_mapping, *, k_scale=None, v_scale=None,
+              block_tables_width: int = 1, stream=None):
+    """Write new K/V rows [T][Hkv][D] (q's dtype) into their slots."""
+    lib = load_library()
+    T, Hkv, D = k_new.shape
+    NB = k_cache.shape[0]
+    shape = PaShape(Hkv, Hkv, D, 16, NB, max(1, block_tables_width), _dtype_code(k_new),
+                    _dtype_code(k_cache), 0)
+    rc = lib.pa_kv_append(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                          _ptr(v_scale), _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T,
+                          _stream(stream))
+    _check(rc, "pa_kv_append")
+
+
+def fp8_to_f32(codes):
+    """Decode e4m3fn bytes (uint8 tensor on the GPU) with the device path."""
+    import torch
+    lib = load_library()
+    out = torch.empty(codes.shape, dtype=torch.float32, device=codes.device)
+    _check(lib.pa_fp8_e4m3fn_to_f32(_ptr(codes), _ptr(out), codes.numel(), _stream(None)),
+           "pa_fp8_e4m3fn_to_f32")
+    return out

@@ -1,0 +1,217 @@
+// pa_api.hip -- the C ABI: argument checks, workspace layout, launches.
+// Every function here only checks host-known arguments and enqueues
+// kernels on the caller's stream; nothing allocates or synchronizes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace {
+
+using pa::WorkItem;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Layout {
+    int part_size = 0;
+    int max_parts = 0;
+    int tile_tokens = 0;
+    int64_t max_items = 0;
+    size_t off_items = 0, off_tok = 0, off_lse = 0, off_o = 0, total = 0;
+};
+
+int check_shape(const pa_shape* s) {
+    if (!s) return PA_EINVAL;
+    if (s->num_q_heads <= 0 || s->num_kv_heads <= 0) return PA_EINVAL;
+    if (s->num_q_heads % s->num_kv_heads) return PA_EINVAL;
+    if (s->num_q_heads / s->num_kv_heads > 16) return PA_ENOTSUP;
+    if (s->head_dim != 64 && s->head_dim != 128) return PA_EINVAL;
+    if (s->block_size != PA_BLOCK_SIZE) return PA_EINVAL;
+    if (s->num_blocks <= 0 || s->max_blocks_per_seq <= 0) return PA_EINVAL;
+    const bool ok = (s->q_dtype == PA_F32 && s->kv_dtype == PA_F32) ||
+                    (s->q_dtype == PA_BF16 && s->kv_dtype == PA_BF16) ||
+                    (s->q_dtype == PA_BF16 && s->kv_dtype == PA_FP8_E4M3FN);
+    if (!ok) return PA_EINVAL;
+    if (s->partition_size < 0 || s->partition_size % PA_BLOCK_SIZE) return PA_EINVAL;
+    return PA_OK;
+}
+
+// Workspace: [header][work items][per-token partition counts][partials].
+Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_context_len,
+                   bool decode) {
+    Layout l;
+    l.part_size = s->partition_size > 0 ? s->partition_size : pa::kDefaultPartition;
+    l.max_parts = max_context_len > 0 ? cdiv(max_context_len, l.part_size) : 1;
+    const int G = s->num_q_heads / s->num_kv_heads;
+    l.tile_tokens = decode ? 1 : (16 / G > 1 ? 16 / G : 1);
+    const int64_t tiles =
+        decode ? num_seqs : (int64_t)num_seqs + cdiv(num_tokens, l.tile_tokens);
+    l.max_items = tiles * l.max_parts;
+    size_t off = align_up(sizeof(int32_t) * pa::HDR_WORDS);
+    l.off_items = off;
+    off = align_up(off + sizeof(WorkItem) * (size_t)l.max_items);
+    l.off_tok = off;
+    off = align_up(off + sizeof(int32_t) * (size_t)(num_tokens > 0 ? num_tokens : 1));
+    l.off_lse = off;
+    l.off_o = off;
+    if (l.max_parts > 1) {
+        const size_t rows = (size_t)num_tokens * s->num_q_heads * l.max_parts;
+        off = align_up(off + sizeof(float) * rows);
+        l.off_o = off;
+        off = align_up(off + sizeof(float) * rows * s->head_dim);
+    }
+    l.total = off;
+    return l;
+}
+
+int run_attention(const pa_shape* s, void* out, float* lse, const void* q, const void* k_cache,
+                  const void* v_cache, const float* k_scale, const float* v_scale,
+                  const int32_t* block_tables, const int32_t* context_lens,
+                  const int32_t* query_start_loc, int num_seqs, int num_tokens,
+                  int max_query_len, int max_context_len, float scale, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    int rc = check_shape(s);
+    if (rc != PA_OK) return rc;
+    const bool decode = query_start_loc == nullptr;
+    if (num_seqs < 0 || num_tokens < 0 || max_context_len < 0) return PA_EINVAL;
+    if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+    if (!decode && max_query_len < 1) return PA_EINVAL;
+    if ((int64_t)max_context_len > (int64_t)PA_BLOCK_SIZE * s->max_blocks_per_seq)
+        return PA_EINVAL;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_EINVAL;
+    if (s->kv_dtype == PA_FP8_E4M3FN && (!k_scale || !v_scale)) return PA_EINVAL;
+    const Layout l = make_layout(s, num_seqs, num_tokens, max_context_len, decode);
+    if (!workspace || workspace_bytes < l.total) return PA_EWORKSPACE;
+    if (((uintptr_t)workspace % kAlign) != 0) return PA_EINVAL;
+
+    char* ws = (char*)workspace;
+    int32_t* hdr = (int32_t*)ws;
+    WorkItem* items = (WorkItem*)(ws + l.off_items);
+    int32_t* tok_np = (int32_t*)(ws + l.off_tok);
+    hipStream_t st = (hipStream_t)stream;
+
+    pa::PlanArgs pl{context_lens, query_start_loc, num_seqs, num_tokens, max_context_len,
+                    l.part_size,  l.tile_tokens,     l.max_items, items,      hdr,
+                    tok_np};
+    if (pa::launch_plan(pl, st) != hipSuccess) return PA_EHIP;
+
+    pa::AttnArgs aa{};
+    aa.out = out;
+    aa.lse = lse;
+    aa.q = q;
+    aa.k_cache = k_cache;
+    aa.v_cache = v_cache;
+    aa.k_scale = k_scale;
+    aa.v_scale = v_scale;
+    aa.block_tables = block_tables;
+    aa.context_lens = context_lens;
+    aa.qsl = query_start_loc;
+    aa.items = items;
+    aa.hdr = hdr;
+    aa.part_lse = l.max_parts > 1 ? (float*)(ws + l.off_lse) : nullptr;
+    aa.part_o = l.max_parts > 1 ? (float*)(ws + l.off_o) : nullptr;
+    aa.num_q_heads = s->num_q_heads;
+    aa.num_kv_heads = s->num_kv_heads;
+    aa.group = s->num_q_heads / s->num_kv_heads;
+    aa.num_blocks = s->num_blocks;
+    aa.max_blocks_per_seq = s->max_blocks_per_seq;
+    aa.max_context_len = max_context_len;
+    aa.part_size = l.part_size;
+    aa.max_parts = l.max_parts;
+    aa.scale_log2 = scale * 1.44269504088896340736f;
+    if (pa::launch_attention(s->kv_dtype, s->head_dim, aa, l.max_items * s->num_kv_heads, st) !=
+        hipSuccess)
+        return PA_EHIP;
+
+    if (l.max_parts > 1) {
+        pa::MergeArgs ma{out, lse, tok_np, aa.part_lse, aa.part_o, num_tokens, s->num_q_heads,
+                         l.max_parts};
+        if (pa::launch_merge(s->q_dtype, s->head_dim, ma, st) != hipSuccess) return PA_EHIP;
+    }
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_workspace_bytes(const pa_shape* shape, int num_seqs, int num_q_tokens,
+                          int max_context_len, int max_query_len) {
+    if (check_shape(shape) != PA_OK || num_seqs < 0 || num_q_tokens < 0 || max_context_len < 0)
+        return 0;
+    const bool decode = max_query_len <= 1 && num_q_tokens == num_seqs;
+    // a decode-shaped hybrid call may use either layout: size for the larger
+    Layout a = make_layout(shape, num_seqs, num_q_tokens, max_context_len, decode);
+    Layout b = make_layout(shape, num_seqs, num_q_tokens, max_context_len, false);
+    return a.total > b.total ? a.total : b.total;
+}
+
+int pa_paged_attn_decode(const pa_shape* shape, void* out, float* lse, const void* q,
+                         const void* k_cache, const void* v_cache, const float* k_scale,
+                         const float* v_scale, const int32_t* block_tables,
+                         const int32_t* context_lens, int num_seqs, int max_context_len,
+                         float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_attention(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                         context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len, scale,
+                         workspace, workspace_bytes, stream);
+}
+
+int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const void* q,
+                         const void* k_cache, const void* v_cache, const float* k_scale,
+                         const float* v_scale, const int32_t* block_tables,
+                         const int32_t* context_lens, const int32_t* query_start_loc,
+                         int num_seqs, int num_q_tokens, int max_query_len,
+                         int max_context_len, float scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (!query_start_loc) return PA_EINVAL;
+    return run_attention(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                         context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                         max_context_len, scale, workspace, workspace_bytes, stream);
+}
+
+int pa_kv_append(const pa_shape* shape, void* k_cache, void* v_cache, const float* k_scale,
+                 const float* v_scale, const void* k_new, const void* v_new,
+                 const int32_t* slot_mapping, int num_tokens, void* stream) {
+    int rc = check_shape(shape);
+    if (rc != PA_OK) return rc;
+    if (num_tokens < 0) return PA_EINVAL;
+    if (num_tokens == 0) return PA_OK;
+    if (!k_cache || !v_cache || !k_new || !v_new || !slot_mapping) return PA_EINVAL;
+    if (shape->kv_dtype == PA_FP8_E4M3FN && (!k_scale || !v_scale)) return PA_EINVAL;
+    pa::AppendArgs a{k_cache,      v_cache,    k_scale,
+                     v_scale,      k_new,      v_new,
+                     slot_mapping, num_tokens, shape->num_kv_heads,
+                     shape->head_dim, shape->num_blocks};
+    if (pa::launch_append(shape->q_dtype, shape->kv_dtype, a, (hipStream_t)stream) != hipSuccess)
+        return PA_EHIP;
+    return PA_OK;
+}
+
+int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream) {
+    if (n < 0 || (n > 0 && (!in || !out))) return PA_EINVAL;
+    return pa::launch_fp8_decode(in, out, n, (hipStream_t)stream) == hipSuccess ? PA_OK
+                                                                                : PA_EHIP;
+}
+
+const char* pa_status_string(int status) {
+    switch (status) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument";
+    case PA_EWORKSPACE: return "workspace missing or too small";
+    case PA_EHIP: return "HIP runtime or launch error";
+    case PA_ENOTSUP: return "not supported";
+    default: return "unknown status";
+    }
+}
+
+int pa_version(void) { return 100; }
+
+}  // extern "C"

@@ -119,8 +119,9 @@ class Workload:
             return self._slot_mapping
         pos = self.token_positions()
         seq = self.token_seq()
-        blk = self.block_tables[seq, pos // BLOCK].astype(np.int64)
-        return (blk * BLOCK + pos % BLOCK).astype(np.int32)
+        ok = pos >= 0
+        blk = self.block_tables[seq, np.where(ok, pos, 0) // BLOCK].astype(np.int64)
+        return np.where(ok, blk * BLOCK + pos % BLOCK, -1).astype(np.int32)
 
     # ---- byte / flop accounting (measurement, not the method) -----------
     @property
@@ -426,11 +427,17 @@ def materialize(wl: Workload, device="cpu", value_scale: float = 1.0) -> Values:
         v[unused] = float("nan")
 
     # this step's new rows: the values at their slots, then poison the slots
-    slots = wl.slot_mapping.astype(np.int64)
-    sb = torch.as_tensor(slots // BLOCK, device=dev)
-    so = torch.as_tensor(slots % BLOCK, device=dev)
-    k_new = k.permute(0, 2, 1, 3)[sb, so].clone()  # [T][H][D]
-    v_new = v.permute(0, 3, 1, 2)[sb, so].clone()
+    all_slots = wl.slot_mapping.astype(np.int64)
+    has = all_slots >= 0
+    slots = all_slots[has]
+    k_new = torch.zeros(wl.num_tokens, H, D, device=dev)
+    v_new = torch.zeros(wl.num_tokens, H, D, device=dev)
+    if slots.size:
+        sb = torch.as_tensor(slots // BLOCK, device=dev)
+        so = torch.as_tensor(slots % BLOCK, device=dev)
+        idx = torch.as_tensor(np.nonzero(has)[0], device=dev)
+        k_new[idx] = k.permute(0, 2, 1, 3)[sb, so]  # [T][H][D]
+        v_new[idx] = v.permute(0, 3, 1, 2)[sb, so]
     out = Values(q=q, k_new=k_new.to(tdt), v_new=v_new.to(tdt))
 
     if wl.kv_dtype == "fp8":
