@@ -1,17 +1,19 @@
 #!/usr/bin/env python3
 """Benchmark of the paged-attention hot path on one MI355X.
 
-One step = one layer's decode step on one batch: append the batch's new K/V
-rows into the paged cache, then paged attention over every sequence's
-context (plan, attention, split merge). The default workload is the
-Llama-3-8B-shaped decode batch (64 sequences, contexts uniform on
-[128, 4096], 32 query / 8 KV heads, head_dim 128, bf16, 16-token blocks in a
-shuffled pool 1.25x the blocks needed). Steps rotate over the KV caches of
-``--layers`` distinct layers, so a call never finds its layer's KV in the
-caches left warm by the previous call (32 layers x ~0.7 GB >> the 256 MB
-Infinity Cache), as in a real model.
+One step = one decode step of a whole model's attention on one batch: plan
+the batch once (work list shared by every layer), then for each of
+``--layers`` layers append the batch's new K/V rows into that layer's paged
+cache and run paged attention over every sequence's context. Each layer
+has its own cache, so no call finds its KV warm in the caches
+(32 layers x ~0.7 GB >> the 256 MB Infinity Cache). The step is captured
+once in a HIP graph and replayed, so host launch overhead is not timed.
 
-Prints one JSON line (see the fields at the end of main()).
+The default workload is the Llama-3-8B-shaped decode batch: 64 sequences,
+contexts uniform on [128, 4096], 32 query / 8 KV heads, head_dim 128, bf16,
+16-token blocks drawn from a shuffled pool 1.25x the blocks needed.
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -40,20 +42,19 @@ def _threads() -> int:
 def cpu_baseline(wl, budget_s: float = 10.0):
     """Time the CPU oracle (as it stands) on this workload's batch until
     about ``budget_s`` of CPU work, on the host's cores."""
+    import torch
+
     import oracle
     from paged_kv_cache_213_amd import workloads as W
 
     vals = W.materialize(wl, "cpu")
-    q = vals.q.view(__import__("torch").int16).numpy().view(np.uint16) \
-        if wl.q_dtype == "bf16" else vals.q.numpy()
 
     def bits(t):
-        import torch
         if t.dtype == torch.bfloat16:
             return t.contiguous().view(torch.int16).numpy().view(np.uint16)
         return t.contiguous().numpy()
 
-    host = {"q": q}
+    host = {"q": bits(vals.q)}
     if wl.kv_dtype == "fp8":
         host["k_scale"] = vals.k_scale.numpy()
         host["v_scale"] = vals.v_scale.numpy()
@@ -84,27 +85,30 @@ def cpu_baseline(wl, budget_s: float = 10.0):
         if n_sub < wl.num_seqs and dt < budget_s / 4:
             n_sub = min(wl.num_seqs, n_sub * 2)
     return {
-        "value": bytes_done / t_total / 1e9,
+        "value": round(bytes_done / t_total / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{seqs_done} sequence-calls of this batch ({reps} oracle calls, "
-                  f"{t_total:.1f} s, float64 gather-then-softmax, {threads} threads)",
-        "tokens_per_s": seqs_done / t_total,
+        "sample": f"{seqs_done} sequence-layer calls of this batch ({reps} oracle calls over "
+                  f"prefixes of the batch, {t_total:.1f} s, float64 gather-then-softmax, "
+                  f"{threads} threads)",
+        "tokens_per_s": round(seqs_done / t_total, 2),
     }
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c2", help="c1..c5 (c2 is the headline workload)")
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--partition-size", type=int, default=None)
+    ap.add_argument("--partition-size", type=int, default=0,
+                    help="split-KV piece in tokens (0: balanced over resident waves)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -115,6 +119,7 @@ def main():
         sys.exit(2)
 
     import torch
+
     import paged_kv_cache_213_amd as pa
     from paged_kv_cache_213_amd import workloads as W
 
@@ -124,7 +129,7 @@ def main():
     pa.load_library()  # fails loudly if the HIP library is missing
 
     wl = W.make_config(args.config, seed=args.seed)
-    P = wl.partition_size if args.partition_size is None else args.partition_size
+    P = args.partition_size
     dev = torch.device("cuda")
     torch.cuda.set_device(0)
     vals = W.materialize(wl, dev)
@@ -134,57 +139,81 @@ def main():
     kc = [vals.k_cache] + [vals.k_cache.clone() for _ in range(layers - 1)]
     vc = [vals.v_cache] + [vals.v_cache.clone() for _ in range(layers - 1)]
     qs = [vals.q] + [vals.q.clone() for _ in range(layers - 1)]
+    outs = [torch.empty_like(vals.q) for _ in range(layers)]
     bt = torch.from_numpy(wl.block_tables).to(dev)
     cl = torch.from_numpy(wl.context_lens).to(dev)
-    qsl = torch.from_numpy(wl.query_start_loc).to(dev)
+    qsl = None if wl.is_decode else torch.from_numpy(wl.query_start_loc).to(dev)
     slots = torch.from_numpy(wl.slot_mapping).to(dev)
-    out = torch.empty_like(vals.q)
     lse = torch.empty(wl.num_tokens, wl.num_q_heads, dtype=torch.float32, device=dev)
     shape = pa.make_shape(vals.q, vals.k_cache, bt, P)
     nbytes = pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len,
                                 wl.max_query_len)
     ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+    mq = 1 if wl.is_decode else wl.max_query_len
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(layers)]
 
-    def step(i, ev=None):
-        L_ = i % layers
-        if ev is not None:
-            ev[0].record(stream)
-        pa.kv_append(kc[L_], vc[L_], vals.k_new, vals.v_new, slots)
-        if ev is not None:
-            ev[1].record(stream)
-        if wl.is_decode:
-            pa.decode(qs[L_], kc[L_], vc[L_], bt, cl, wl.scale, max_context_len=wl.max_context_len,
-                      partition_size=P, out=out, lse=lse, workspace=ws)
+    def model_step(stream, timed=False):
+        pa.plan(shape, cl, ws, query_start_loc=qsl, num_q_tokens=wl.num_tokens,
+                max_query_len=mq, max_context_len=wl.max_context_len, stream=stream)
+        for L_ in range(layers):
+            pa.kv_append(kc[L_], vc[L_], vals.k_new, vals.v_new, slots, stream=stream)
+            if timed:
+                ev[L_][0].record(stream)
+            pa.run(shape, qs[L_], kc[L_], vc[L_], bt, cl, wl.scale, ws, query_start_loc=qsl,
+                   max_query_len=mq, max_context_len=wl.max_context_len, out=outs[L_],
+                   lse=lse, stream=stream)
+            if timed:
+                ev[L_][1].record(stream)
+
+    s = torch.cuda.Stream()
+    graph = None
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            model_step(s)  # eager warm-up (also sets the occupancy caches)
+        s.synchronize()
+        if not args.no_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=s):
+                model_step(s)
+
+    def replay():
+        if graph is not None:
+            graph.replay()
         else:
-            pa.hybrid(qs[L_], kc[L_], vc[L_], bt, cl, qsl, wl.scale,
-                      max_context_len=wl.max_context_len, max_query_len=wl.max_query_len,
-                      partition_size=P, out=out, lse=lse, workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
+            with torch.cuda.stream(s):
+                model_step(s)
 
-    for i in range(args.warmup):
-        step(i)
+    for _ in range(args.warmup):
+        replay()
     torch.cuda.synchronize()
-    if not torch.isfinite(out.float()).all():
+    if not all(bool(torch.isfinite(o.float()).all()) for o in outs):
         raise SystemExit("non-finite attention output")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # timed region: exactly `steps` model steps
+    att_ms = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+    for _ in range(args.steps):
+        replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the attention kernel's own duration: events around each layer's launch
+    # in eager steps; a GPU spin first lets the host enqueue ahead of the GPU
+    # so nothing but the kernel runs between an event pair
+    with torch.cuda.stream(s):
+        for _ in range(min(args.steps, 10)):
+            torch.cuda._sleep(2_000_000)
+            model_step(s, timed=True)
+            s.synchronize()
+            att_ms += [e[0].elapsed_time(e[1]) for e in ev[1:]]
+    att_ms = np.array(att_ms)
 
-    app_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    att_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     ms_per_step = wall * 1e3 / args.steps
     kv_bytes = wl.kv_bytes_logical()
-    value = kv_bytes / (ms_per_step / 1e3) / 1e9
+    value = layers * kv_bytes / (ms_per_step / 1e3) / 1e9
     att_mean = float(att_ms.mean())
     achieved = kv_bytes / (att_mean / 1e3) / 1e9
-
+    layer_ms = ms_per_step / layers
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -200,7 +229,8 @@ def main():
         "data": "synthetic (seeded N(0,1) values, shuffled block pool)",
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "tokens_per_s": round(wl.num_tokens / (ms_per_step / 1e3), 1),
-        "kv_tokens_per_s": round(float(wl.context_lens.sum()) / (ms_per_step / 1e3), 1),
+        "tokens_per_s_per_layer_call": round(wl.num_tokens / (layer_ms / 1e3), 1),
+        "kv_tokens_per_s_per_layer_call": round(float(wl.context_lens.sum()) / (layer_ms / 1e3), 1),
         "config": {
             "workload": f"{wl.name}: {W.CONFIG_TITLES[wl.name]}",
             "num_seqs": wl.num_seqs,
@@ -210,9 +240,10 @@ def main():
             "head_dim": wl.head_dim,
             "block_size": 16,
             "sum_context_len": int(wl.context_lens.sum()),
-            "kv_bytes_per_call": kv_bytes,
-            "partition_size": P or 512,
-            "layers_rotated": layers,
+            "kv_bytes_per_layer": kv_bytes,
+            "layers_per_step": layers,
+            "partition_size": P,
+            "graph": graph is not None,
             "seed": wl.seed,
         },
         "roofline": {
@@ -222,11 +253,10 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": None,
-            "kernel": "attention call (plan + attention + split merge), HIP events",
-            "launch_ms_mean": round(att_mean, 5),
-            "launch_ms_p10_p50_p90": [round(float(np.percentile(att_ms, p)), 5)
+            "kernel": "attention_kernel (one launch per layer), HIP events around each launch",
+            "launch_us_mean": round(att_mean * 1e3, 2),
+            "launch_us_p10_p50_p90": [round(float(np.percentile(att_ms, p)) * 1e3, 2)
                                       for p in (10, 50, 90)],
-            "append_ms_mean": round(float(app_ms.mean()), 5),
         },
     }
     if not args.no_cpu_baseline:

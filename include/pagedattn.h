@@ -8,9 +8,11 @@
  * non-contiguous blocks; "The LLM inference engine playbook", Theme 3).
  * Query heads are grouped onto KV heads (GQA; "References", GQA entry).
  * A batch may mix single-token decodes with chunked-prefill spans
- * ("03 -- Engines Papers", section 3). Long contexts are split into
- * fixed-size partitions whose partial results are merged by log-sum-exp
- * (the split-K decode pattern of the playbook's Theme 4; the LSE merge of
+ * ("03 -- Engines Papers", section 3). The key blocks of the whole batch
+ * are split into pieces of equal size, one per resident wave, so long and
+ * short contexts finish together; a context cut by a piece boundary is
+ * completed by a log-sum-exp merge of its pieces' partial results (the
+ * split-K decode pattern of the playbook's Theme 4; the LSE merge of
  * "03 -- Engines Papers", section 12). The cache may be stored as FP8 E4M3
  * with one scale per (block, KV head) (playbook, Themes 3 and 6).
  *
@@ -74,8 +76,10 @@ typedef enum pa_status {
 /* Problem shape shared by all calls on one cache. Supported today:
  * head_dim in {64, 128}; block_size == 16; Hq % Hkv == 0 with
  * G = Hq / Hkv <= 16; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
- * (BF16, FP8_E4M3FN)}; partition_size 0 (library default, 512 tokens) or a
- * positive multiple of 16. */
+ * (BF16, FP8_E4M3FN)}; partition_size 0 (split each call's key blocks into
+ * equal pieces, one per resident wave, at least 128 tokens each) or a
+ * positive multiple of 16 (pieces of that many tokens). At most 8192 tiles
+ * per call (a tile is up to 16 query rows: G heads of 16 / G tokens). */
 typedef struct pa_shape {
     int32_t num_q_heads;        /* Hq */
     int32_t num_kv_heads;       /* Hkv */
@@ -85,13 +89,14 @@ typedef struct pa_shape {
     int32_t max_blocks_per_seq; /* row stride of block_tables */
     int32_t q_dtype;            /* pa_dtype of q, out, and new K/V rows */
     int32_t kv_dtype;           /* pa_dtype of the caches */
-    int32_t partition_size;     /* split-KV partition in tokens, 0 = default */
+    int32_t partition_size;     /* split-KV piece in tokens, 0 = balanced */
 } pa_shape;
 
-/* Bytes of device workspace the attention calls need for this batch
- * (work list, per-token partition counts, split partials). Returns 0 when
- * the shape is invalid. num_q_tokens = T (num_seqs for a decode call);
- * max_query_len = largest n_i (1 for a decode call). */
+/* Bytes of device workspace the attention calls need for this batch (work
+ * list, per-segment counters, split partials). Returns 0 when the shape is
+ * invalid. num_q_tokens = T (num_seqs for a decode call); max_query_len =
+ * largest n_i (1 for a decode call). The decode and hybrid calls below are
+ * pa_plan followed by pa_paged_attn_run. */
 size_t pa_workspace_bytes(const pa_shape* shape, int num_seqs, int num_q_tokens,
                           int max_context_len, int max_query_len);
 
@@ -119,6 +124,30 @@ int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const voi
                          int num_seqs, int num_q_tokens, int max_query_len,
                          int max_context_len, float scale, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* Plan a batch: turn (query spans, context lengths) into the work list the
+ * attention kernel streams -- tiles of up to 16 query rows, one stream of
+ * 16-token key blocks over all (tile, KV head) segments, cut into pieces
+ * balanced over the device's resident waves (or of partition_size tokens).
+ * Writes only `workspace`. The request trace on "03 -- Engines Papers"
+ * plans once per step from the active sequences before the model runs; a
+ * plan stays valid for every pa_paged_attn_run that passes the same shape,
+ * batch sizes and the same context_lens / query_start_loc contents (every
+ * layer of one step), enqueued after it. query_start_loc NULL = decode
+ * (num_q_tokens == num_seqs). Calls that overlap on one workspace race. */
+int pa_plan(const pa_shape* shape, const int32_t* context_lens, const int32_t* query_start_loc,
+            int num_seqs, int num_q_tokens, int max_query_len, int max_context_len,
+            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Attention with a plan made by pa_plan (same arguments as the plan, plus
+ * the tensors): one kernel launch. Pieces that cut a segment write partial
+ * results to the workspace and the last of them merges by log-sum-exp. */
+int pa_paged_attn_run(const pa_shape* shape, void* out, float* lse, const void* q,
+                      const void* k_cache, const void* v_cache, const float* k_scale,
+                      const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, const int32_t* query_start_loc, int num_seqs,
+                      int num_q_tokens, int max_query_len, int max_context_len, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* Append this step's new K/V rows into their slots before attention runs
  * on the same stream. k_new, v_new: [num_tokens][Hkv][D] in q_dtype.

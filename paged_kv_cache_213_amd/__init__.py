@@ -61,6 +61,10 @@ def load_library(path: str = LIB_PATH):
     lib.pa_paged_attn_decode.argtypes = [S, P, P, P, P, P, P, P, P, P, I, I, F, P, Z, P]
     lib.pa_paged_attn_hybrid.restype = I
     lib.pa_paged_attn_hybrid.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
+    lib.pa_plan.restype = I
+    lib.pa_plan.argtypes = [S, P, P, I, I, I, I, P, Z, P]
+    lib.pa_paged_attn_run.restype = I
+    lib.pa_paged_attn_run.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
     lib.pa_kv_append.restype = I
     lib.pa_kv_append.argtypes = [S, P, P, P, P, P, P, P, I, P]
     lib.pa_fp8_e4m3fn_to_f32.restype = I
@@ -69,6 +73,10 @@ def load_library(path: str = LIB_PATH):
     lib.pa_status_string.argtypes = [I]
     lib.pa_version.restype = I
     lib.pa_version.argtypes = []
+    lib.pa_probe_stream_read.restype = I
+    lib.pa_probe_stream_read.argtypes = [P, Z, P, P]
+    lib.pa_probe_copy.restype = I
+    lib.pa_probe_copy.argtypes = [P, P, Z, P]
     _lib = lib
     return lib
 
@@ -178,6 +186,38 @@ def hybrid(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, sca
     return out
 
 
+def plan(shape: PaShape, context_lens, workspace, *, query_start_loc=None, num_q_tokens: int,
+         max_query_len: int, max_context_len: int, stream=None):
+    """Enqueue the work plan of a batch into ``workspace`` (reusable by every
+    run() on the same batch)."""
+    lib = load_library()
+    S = context_lens.shape[0]
+    rc = lib.pa_plan(ctypes.byref(shape), _ptr(context_lens), _ptr(query_start_loc), S,
+                     int(num_q_tokens), int(max_query_len), int(max_context_len), _ptr(workspace),
+                     workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "pa_plan")
+
+
+def run(shape: PaShape, q, k_cache, v_cache, block_tables, context_lens, scale: float, workspace,
+        *, query_start_loc=None, max_query_len: int, max_context_len: int, k_scale=None,
+        v_scale=None, out=None, lse=None, stream=None):
+    """Attention with a plan enqueued earlier by plan() (one kernel launch)."""
+    import torch
+    lib = load_library()
+    T = q.shape[0]
+    S = context_lens.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    rc = lib.pa_paged_attn_run(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
+                               _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                               _ptr(context_lens), _ptr(query_start_loc), S, T,
+                               int(max_query_len), int(max_context_len), float(scale),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    _check(rc, "pa_paged_attn_run")
+    return out
+
+
 def kv_append(k_cache, v_cache, k_new, v_new, slot_mapping, *, k_scale=None, v_scale=None,
               block_tables_width: int = 1, stream=None):
     """Write new K/V rows [T][Hkv][D] (q's dtype) into their slots."""
@@ -200,3 +240,21 @@ def fp8_to_f32(codes):
     _check(lib.pa_fp8_e4m3fn_to_f32(_ptr(codes), _ptr(out), codes.numel(), _stream(None)),
            "pa_fp8_e4m3fn_to_f32")
     return out
+
+
+# ---- measurement probes (include/pagedattn_probe.h) ---------------------
+
+def probe_stream_read(buf, sink, stream=None):
+    """Enqueue one streaming read of the whole tensor ``buf``."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().pa_probe_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
+           "pa_probe_stream_read")
+
+
+def probe_copy(src, dst, stream=None):
+    """Enqueue a plain copy of ``src`` into ``dst`` (same byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise PagedAttentionError("copy destination too small")
+    _check(load_library().pa_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)),
+           "pa_probe_copy")

@@ -8,7 +8,6 @@
 
 namespace {
 
-using pa::WorkItem;
 
 constexpr size_t kAlign = 256;
 
@@ -19,11 +18,12 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
-    int part_size = 0;
-    int max_parts = 0;
+    int part_blocks = 0;  // blocks per piece, 0 = balanced over resident waves
     int tile_tokens = 0;
-    int64_t max_items = 0;
-    size_t off_items = 0, off_tok = 0, off_lse = 0, off_o = 0, total = 0;
+    int waves = 0;
+    int64_t max_tiles = 0;
+    int64_t max_pieces = 0;
+    size_t off_tiles = 0, off_pieces = 0, off_splits = 0, off_lse = 0, off_o = 0, total = 0;
 };
 
 int check_shape(const pa_shape* s) {
@@ -42,67 +42,112 @@ int check_shape(const pa_shape* s) {
     return PA_OK;
 }
 
-// Workspace: [header][work items][per-token partition counts][partials].
+// Upper bound of resident attention waves when no device can be queried
+// (256 compute units x 32 waves).
+constexpr int kWaveBound = 8192;
+
+// Workspace: [header][tiles][piece starts][cut segments][partials].
 Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_context_len,
                    bool decode) {
     Layout l;
-    l.part_size = s->partition_size > 0 ? s->partition_size : pa::kDefaultPartition;
-    l.max_parts = max_context_len > 0 ? cdiv(max_context_len, l.part_size) : 1;
     const int G = s->num_q_heads / s->num_kv_heads;
     l.tile_tokens = decode ? 1 : (16 / G > 1 ? 16 / G : 1);
-    const int64_t tiles =
-        decode ? num_seqs : (int64_t)num_seqs + cdiv(num_tokens, l.tile_tokens);
-    l.max_items = tiles * l.max_parts;
+    l.part_blocks = s->partition_size / PA_BLOCK_SIZE;
+    const int w = pa::resident_waves(s->kv_dtype, s->head_dim);
+    l.waves = w > 0 ? w : kWaveBound;
+    l.max_tiles = decode ? num_seqs : (int64_t)num_seqs + cdiv(num_tokens, l.tile_tokens);
+    const int64_t blocks_per_tile = cdiv(max_context_len > 0 ? max_context_len : 1, PA_BLOCK_SIZE);
+    const int64_t max_total = l.max_tiles * s->num_kv_heads * blocks_per_tile;
+    l.max_pieces = l.part_blocks > 0 ? (max_total + l.part_blocks - 1) / l.part_blocks
+                                     : (int64_t)l.waves;
+    if (l.max_pieces < 1) l.max_pieces = 1;
     size_t off = align_up(sizeof(int32_t) * pa::HDR_WORDS);
-    l.off_items = off;
-    off = align_up(off + sizeof(WorkItem) * (size_t)l.max_items);
-    l.off_tok = off;
-    off = align_up(off + sizeof(int32_t) * (size_t)(num_tokens > 0 ? num_tokens : 1));
+    l.off_tiles = off;
+    off = align_up(off + sizeof(pa::TileDesc) * (size_t)l.max_tiles);
+    l.off_pieces = off;
+    off = align_up(off + sizeof(pa::PieceStart) * (size_t)l.max_pieces);
+    l.off_splits = off;  // every cut segment holds a piece boundary: <= pieces
+    off = align_up(off + sizeof(pa::SplitSeg) * (size_t)l.max_pieces);
     l.off_lse = off;
+    off = align_up(off + sizeof(float) * (size_t)l.max_pieces * 2 * 16);
     l.off_o = off;
-    if (l.max_parts > 1) {
-        const size_t rows = (size_t)num_tokens * s->num_q_heads * l.max_parts;
-        off = align_up(off + sizeof(float) * rows);
-        l.off_o = off;
-        off = align_up(off + sizeof(float) * rows * s->head_dim);
-    }
+    off = align_up(off + sizeof(float) * (size_t)l.max_pieces * 2 * 16 * s->head_dim);
     l.total = off;
     return l;
 }
 
-int run_attention(const pa_shape* s, void* out, float* lse, const void* q, const void* k_cache,
-                  const void* v_cache, const float* k_scale, const float* v_scale,
-                  const int32_t* block_tables, const int32_t* context_lens,
-                  const int32_t* query_start_loc, int num_seqs, int num_tokens,
-                  int max_query_len, int max_context_len, float scale, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+// Checks shared by plan and run; fills the layout.
+int check_batch(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl,
+                int num_seqs, int num_tokens, int max_query_len, int max_context_len,
+                void* workspace, size_t workspace_bytes, Layout* l) {
     int rc = check_shape(s);
     if (rc != PA_OK) return rc;
-    const bool decode = query_start_loc == nullptr;
     if (num_seqs < 0 || num_tokens < 0 || max_context_len < 0) return PA_EINVAL;
-    if (num_seqs == 0 || num_tokens == 0) return PA_OK;
-    if (!decode && max_query_len < 1) return PA_EINVAL;
+    if (qsl == nullptr && num_tokens != num_seqs) return PA_EINVAL;
+    if (qsl != nullptr && num_seqs > 0 && num_tokens > 0 && max_query_len < 1) return PA_EINVAL;
     if ((int64_t)max_context_len > (int64_t)PA_BLOCK_SIZE * s->max_blocks_per_seq)
         return PA_EINVAL;
-    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_EINVAL;
+    if (num_seqs > 0 && !context_lens) return PA_EINVAL;
+    *l = make_layout(s, num_seqs, num_tokens, max_context_len, qsl == nullptr);
+    if (l->max_tiles > pa::kMaxTiles) return PA_ENOTSUP;
+    if (!workspace || workspace_bytes < l->total) return PA_EWORKSPACE;
+    if (((uintptr_t)workspace % kAlign) != 0) return PA_EINVAL;
+    return PA_OK;
+}
+
+// Checks of the attention inputs and outputs (host-known properties only).
+int check_io(const pa_shape* s, const void* out, const void* q, const void* k_cache,
+             const void* v_cache, const float* k_scale, const float* v_scale,
+             const int32_t* block_tables) {
+    if (!out || !q || !k_cache || !v_cache || !block_tables) return PA_EINVAL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return PA_EINVAL;
     if (s->kv_dtype == PA_FP8_E4M3FN && (!k_scale || !v_scale)) return PA_EINVAL;
-    const Layout l = make_layout(s, num_seqs, num_tokens, max_context_len, decode);
-    if (!workspace || workspace_bytes < l.total) return PA_EWORKSPACE;
-    if (((uintptr_t)workspace % kAlign) != 0) return PA_EINVAL;
+    return PA_OK;
+}
 
+int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl, int num_seqs,
+              int num_tokens, int max_query_len, int max_context_len, void* workspace,
+              size_t workspace_bytes, void* stream) {
+    Layout l;
+    int rc = check_batch(s, context_lens, qsl, num_seqs, num_tokens, max_query_len,
+                         max_context_len, workspace, workspace_bytes, &l);
+    if (rc != PA_OK) return rc;
+    if (num_seqs == 0 || num_tokens == 0) return PA_OK;
     char* ws = (char*)workspace;
-    int32_t* hdr = (int32_t*)ws;
-    WorkItem* items = (WorkItem*)(ws + l.off_items);
-    int32_t* tok_np = (int32_t*)(ws + l.off_tok);
-    hipStream_t st = (hipStream_t)stream;
+    pa::PlanArgs pl{};
+    pl.context_lens = context_lens;
+    pl.qsl = qsl;
+    pl.num_seqs = num_seqs;
+    pl.num_tokens = num_tokens;
+    pl.max_context_len = max_context_len;
+    pl.tile_tokens = l.tile_tokens;
+    pl.num_kv_heads = s->num_kv_heads;
+    pl.part_blocks = l.part_blocks;
+    pl.waves = l.waves;
+    pl.min_blocks = pa::kMinPieceBlocks;
+    pl.max_tiles = (int32_t)l.max_tiles;
+    pl.max_pieces = l.max_pieces;
+    pl.tiles = (pa::TileDesc*)(ws + l.off_tiles);
+    pl.pieces = (pa::PieceStart*)(ws + l.off_pieces);
+    pl.splits = (pa::SplitSeg*)(ws + l.off_splits);
+    pl.hdr = (int32_t*)ws;
+    return pa::launch_plan(pl, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_EHIP;
+}
 
-    pa::PlanArgs pl{context_lens, query_start_loc, num_seqs, num_tokens, max_context_len,
-                    l.part_size,  l.tile_tokens,     l.max_items, items,      hdr,
-                    tok_np};
-    if (pa::launch_plan(pl, st) != hipSuccess) return PA_EHIP;
-
+int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void* k_cache,
+             const void* v_cache, const float* k_scale, const float* v_scale,
+             const int32_t* block_tables, const int32_t* context_lens, const int32_t* qsl,
+             int num_seqs, int num_tokens, int max_query_len, int max_context_len, float scale,
+             void* workspace, size_t workspace_bytes, void* stream) {
+    Layout l;
+    int rc = check_batch(s, context_lens, qsl, num_seqs, num_tokens, max_query_len,
+                         max_context_len, workspace, workspace_bytes, &l);
+    if (rc != PA_OK) return rc;
+    if (num_seqs == 0 || num_tokens == 0) return PA_OK;
+    rc = check_io(s, out, q, k_cache, v_cache, k_scale, v_scale, block_tables);
+    if (rc != PA_OK) return rc;
+    char* ws = (char*)workspace;
     pa::AttnArgs aa{};
     aa.out = out;
     aa.lse = lse;
@@ -113,29 +158,35 @@ int run_attention(const pa_shape* s, void* out, float* lse, const void* q, const
     aa.v_scale = v_scale;
     aa.block_tables = block_tables;
     aa.context_lens = context_lens;
-    aa.qsl = query_start_loc;
-    aa.items = items;
-    aa.hdr = hdr;
-    aa.part_lse = l.max_parts > 1 ? (float*)(ws + l.off_lse) : nullptr;
-    aa.part_o = l.max_parts > 1 ? (float*)(ws + l.off_o) : nullptr;
+    aa.qsl = qsl;
+    aa.tiles = (const pa::TileDesc*)(ws + l.off_tiles);
+    aa.pieces = (const pa::PieceStart*)(ws + l.off_pieces);
+    aa.hdr = (const int32_t*)ws;
+    aa.part_lse = (float*)(ws + l.off_lse);
+    aa.part_o = (float*)(ws + l.off_o);
     aa.num_q_heads = s->num_q_heads;
     aa.num_kv_heads = s->num_kv_heads;
     aa.group = s->num_q_heads / s->num_kv_heads;
     aa.num_blocks = s->num_blocks;
     aa.max_blocks_per_seq = s->max_blocks_per_seq;
     aa.max_context_len = max_context_len;
-    aa.part_size = l.part_size;
-    aa.max_parts = l.max_parts;
     aa.scale_log2 = scale * 1.44269504088896340736f;
-    if (pa::launch_attention(s->kv_dtype, s->head_dim, aa, l.max_items * s->num_kv_heads, st) !=
-        hipSuccess)
+    hipStream_t st = (hipStream_t)stream;
+    if (pa::launch_attention(s->kv_dtype, s->head_dim, aa, l.max_pieces, st) != hipSuccess)
         return PA_EHIP;
-
-    if (l.max_parts > 1) {
-        pa::MergeArgs ma{out, lse, tok_np, aa.part_lse, aa.part_o, num_tokens, s->num_q_heads,
-                         l.max_parts};
-        if (pa::launch_merge(s->q_dtype, s->head_dim, ma, st) != hipSuccess) return PA_EHIP;
-    }
+    pa::MergeArgs ma{};
+    ma.out = out;
+    ma.lse = lse;
+    ma.splits = (const pa::SplitSeg*)(ws + l.off_splits);
+    ma.hdr = (const int32_t*)ws;
+    ma.part_lse = aa.part_lse;
+    ma.part_o = aa.part_o;
+    ma.num_q_heads = s->num_q_heads;
+    ma.group = aa.group;
+    // every piece boundary cuts at most one segment: at most max_pieces - 1
+    if (l.max_pieces > 1 && pa::launch_merge(s->q_dtype, s->head_dim, ma, l.max_pieces - 1, st) !=
+                                hipSuccess)
+        return PA_EHIP;
     return PA_OK;
 }
 
@@ -154,14 +205,41 @@ size_t pa_workspace_bytes(const pa_shape* shape, int num_seqs, int num_q_tokens,
     return a.total > b.total ? a.total : b.total;
 }
 
+int pa_plan(const pa_shape* shape, const int32_t* context_lens, const int32_t* query_start_loc,
+            int num_seqs, int num_q_tokens, int max_query_len, int max_context_len,
+            void* workspace, size_t workspace_bytes, void* stream) {
+    return plan_impl(shape, context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                     max_context_len, workspace, workspace_bytes, stream);
+}
+
+int pa_paged_attn_run(const pa_shape* shape, void* out, float* lse, const void* q,
+                      const void* k_cache, const void* v_cache, const float* k_scale,
+                      const float* v_scale, const int32_t* block_tables,
+                      const int32_t* context_lens, const int32_t* query_start_loc, int num_seqs,
+                      int num_q_tokens, int max_query_len, int max_context_len, float scale,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                    context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                    max_context_len, scale, workspace, workspace_bytes, stream);
+}
+
 int pa_paged_attn_decode(const pa_shape* shape, void* out, float* lse, const void* q,
                          const void* k_cache, const void* v_cache, const float* k_scale,
                          const float* v_scale, const int32_t* block_tables,
                          const int32_t* context_lens, int num_seqs, int max_context_len,
                          float scale, void* workspace, size_t workspace_bytes, void* stream) {
-    return run_attention(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
-                         context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len, scale,
-                         workspace, workspace_bytes, stream);
+    // check everything before enqueueing the plan
+    if (check_shape(shape) != PA_OK) return check_shape(shape);
+    if (num_seqs > 0) {
+        int rc0 = check_io(shape, out, q, k_cache, v_cache, k_scale, v_scale, block_tables);
+        if (rc0 != PA_OK) return rc0;
+    }
+    int rc = plan_impl(shape, context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len,
+                       workspace, workspace_bytes, stream);
+    if (rc != PA_OK) return rc;
+    return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                    context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len, scale,
+                    workspace, workspace_bytes, stream);
 }
 
 int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const void* q,
@@ -171,10 +249,18 @@ int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const voi
                          int num_seqs, int num_q_tokens, int max_query_len,
                          int max_context_len, float scale, void* workspace,
                          size_t workspace_bytes, void* stream) {
+    if (check_shape(shape) != PA_OK) return check_shape(shape);
     if (!query_start_loc) return PA_EINVAL;
-    return run_attention(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
-                         context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
-                         max_context_len, scale, workspace, workspace_bytes, stream);
+    if (num_seqs > 0 && num_q_tokens > 0) {
+        int rc0 = check_io(shape, out, q, k_cache, v_cache, k_scale, v_scale, block_tables);
+        if (rc0 != PA_OK) return rc0;
+    }
+    int rc = plan_impl(shape, context_lens, query_start_loc, num_seqs, num_q_tokens,
+                       max_query_len, max_context_len, workspace, workspace_bytes, stream);
+    if (rc != PA_OK) return rc;
+    return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                    context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                    max_context_len, scale, workspace, workspace_bytes, stream);
 }
 
 int pa_kv_append(const pa_shape* shape, void* k_cache, void* v_cache, const float* k_scale,

@@ -77,6 +77,43 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
     return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xffff0000u);
 }
 
+// K/V bytes are read once per call: stream them with nontemporal loads so
+// they do not evict the block tables, queries and partials from the caches.
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 1
+#endif
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 ld_kv(const uint4* p) {
+#if PA_NT_LOADS
+    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ uint2 ld_kv(const uint2* p) {
+#if PA_NT_LOADS
+    const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)p);
+    return make_uint2(v.x, v.y);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ uint32_t ld_kv(const uint32_t* p) {
+#if PA_NT_LOADS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ float4 ld_kv(const float4* p) {
+    const uint4 v = ld_kv((const uint4*)p);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+}
+
 // ---- per-dtype register images of one 16-token block ---------------------
 
 template <int kv, int D>
@@ -85,21 +122,21 @@ struct Tile;
 // fp32: QK with 16x16x4 f32 MFMA (D/4 steps), PV with 4 steps per 16 dims.
 template <int D>
 struct Tile<KV_F32, D> {
-    float4 k[D / 16];  // K[t][(D/4)g + j], j < D/4
+    float4 k[D / 16];  // load j, element e: K[t][16j + 4g + e]
     float4 v[D / 16];  // V^T[16dt + d][4g .. 4g+3]
     using QReg = float[D / 4];
 
     __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t blk_head,
                                          int lane) {
         const int t = lane & 15, g = lane >> 4;
-        const float4* kp =
-            (const float4*)((const float*)kc + blk_head * 16 * D + t * D + (D / 4) * g);
+        // load j reads 64 contiguous bytes of row t across the 4 lane groups
+        const float* kp = (const float*)kc + blk_head * 16 * D + t * D + 4 * g;
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) k[j] = kp[j];
+        for (int j = 0; j < D / 16; ++j) k[j] = ld_kv((const float4*)(kp + 16 * j));
         const float* vb = (const float*)vc + blk_head * 16 * D;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-            v[dt] = *(const float4*)(vb + (16 * dt + t) * 16 + 4 * g);
+            v[dt] = ld_kv((const float4*)(vb + (16 * dt + t) * 16 + 4 * g));
     }
     __device__ __forceinline__ f32x4 qk(const float* q) const {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -136,20 +173,20 @@ struct Tile<KV_F32, D> {
 // 16x16x16 bf16 MFMA (one per 16 output dims).
 template <int D>
 struct Tile<KV_BF16, D> {
-    uint4 k[D / 32];  // 8 bf16 each: K[t][(D/4)g + 8j .. +8]
+    uint4 k[D / 32];  // 8 bf16 each: K[t][32j + 8g .. +8]
     uint2 v[D / 16];  // 4 bf16 each: V^T[16dt + d][4g .. 4g+3]
 
     __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t blk_head,
                                          int lane) {
         const int t = lane & 15, g = lane >> 4;
-        const uint4* kp = (const uint4*)((const uint16_t*)kc + blk_head * 16 * D + t * D +
-                                         (D / 4) * g);
+        // load j reads 64 contiguous bytes of row t across the 4 lane groups
+        const uint16_t* kp = (const uint16_t*)kc + blk_head * 16 * D + t * D + 8 * g;
 #pragma unroll
-        for (int j = 0; j < D / 32; ++j) k[j] = kp[j];
+        for (int j = 0; j < D / 32; ++j) k[j] = ld_kv((const uint4*)(kp + 32 * j));
         const uint16_t* vb = (const uint16_t*)vc + blk_head * 16 * D;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-            v[dt] = *(const uint2*)(vb + (16 * dt + t) * 16 + 4 * g);
+            v[dt] = ld_kv((const uint2*)(vb + (16 * dt + t) * 16 + 4 * g));
     }
     __device__ __forceinline__ f32x4 qk(const uint4* q) const {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -179,20 +216,20 @@ struct Tile<KV_BF16, D> {
 
 template <int D>
 struct Tile<KV_FP8, D> {
-    uint4 k[D / 64];     // 16 e4m3 bytes each: K[t][(D/4)g + 16j .. +16]
+    uint4 k[D / 64];     // 16 e4m3 bytes each: K[t][64j + 16g .. +16]
     uint32_t v[D / 16];  // 4 e4m3 bytes each: V^T[16dt + d][4g .. 4g+3]
 
     __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t blk_head,
                                          int lane) {
         const int t = lane & 15, g = lane >> 4;
-        const uint4* kp =
-            (const uint4*)((const uint8_t*)kc + blk_head * 16 * D + t * D + (D / 4) * g);
+        // load j reads 64 contiguous bytes of row t across the 4 lane groups
+        const uint8_t* kp = (const uint8_t*)kc + blk_head * 16 * D + t * D + 16 * g;
 #pragma unroll
-        for (int j = 0; j < D / 64; ++j) k[j] = kp[j];
+        for (int j = 0; j < D / 64; ++j) k[j] = ld_kv((const uint4*)(kp + 64 * j));
         const uint8_t* vb = (const uint8_t*)vc + blk_head * 16 * D;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-            v[dt] = *(const uint32_t*)(vb + (16 * dt + t) * 16 + 4 * g);
+            v[dt] = ld_kv((const uint32_t*)(vb + (16 * dt + t) * 16 + 4 * g));
     }
     __device__ __forceinline__ f32x4 qk(const uint4* q) const {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -232,14 +269,17 @@ struct Tile<KV_FP8, D> {
 };
 
 // ---- plan ------------------------------------------------------------------
+//
+// The batch's work is one stream of 16-token key blocks: segment (tile t, KV
+// head h) contributes the nb[t] blocks its rows read, segments ordered
+// t-major, h-minor. The stream is cut into pieces of R consecutive blocks;
+// each wave of the attention grid streams whole pieces. With R chosen as
+// total / resident waves, every wave gets the same number of blocks, so all
+// finish together whatever the spread of context lengths (the split-KV
+// decode of the playbook's Theme 4, balanced by block count). A segment cut
+// by a piece boundary leaves partial results that the merge pass combines.
 
 constexpr int kPlanThreads = 1024;
-
-__device__ __forceinline__ int tile_parts(int L, int n, int k0, int ntok, int P) {
-    const int maxpos = L - n + k0 + ntok - 1;  // last query position of the tile
-    const int parts = (maxpos + 1 + P - 1) / P;
-    return parts > 1 ? parts : 1;
-}
 
 // Block-wide exclusive scan of one int per thread (1024 threads).
 __device__ int block_exclusive_scan(int v, int* total) {
@@ -269,288 +309,396 @@ __device__ int block_exclusive_scan(int v, int* total) {
     return before;
 }
 
-// Items of multi-token spans (heavier, chunked prefill) come first, then
-// decodes; within a class sequences keep their order.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
-    int base = 0;
-    for (int phase = 0; phase < 2; ++phase) {
-        for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
-            const int i = c0 + (int)threadIdx.x;
-            int n = 0, L = 0, qs = 0, cnt = 0;
-            bool mine = false;
-            if (i < a.num_seqs) {
-                qs = a.qsl ? a.qsl[i] : i;
-                n = a.qsl ? a.qsl[i + 1] - qs : 1;
-                L = min(a.context_lens[i], a.max_context_len);
-                if (qs < 0 || n < 0 || qs + n > a.num_tokens) n = 0;  // malformed span
-                mine = n > 0 && ((n > 1) == (phase == 0));
-                if (mine)
-                    for (int k0 = 0; k0 < n; k0 += a.tile_tokens) {
-                        const int nt = min(a.tile_tokens, n - k0);
-                        cnt += tile_parts(L, n, k0, nt, a.part_size);
-                    }
-            }
-            int total;
-            int off = base + block_exclusive_scan(cnt, &total);
-            if (mine) {
-                for (int k0 = 0; k0 < n; k0 += a.tile_tokens) {
-                    const int nt = min(a.tile_tokens, n - k0);
-                    const int np = tile_parts(L, n, k0, nt, a.part_size);
-                    for (int p = 0; p < np; ++p, ++off)
-                        if (off < a.max_items) a.items[off] = WorkItem{i, k0, p, nt};
-                    for (int j = 0; j < nt; ++j) a.tok_np[qs + k0 + j] = np;
-                }
-            }
-            base += total;
+    __shared__ int s_tp[kMaxTiles + 1];  // nb per tile, then its exclusive prefix
+    const int cap = min(a.max_tiles, kMaxTiles);
+
+    // 1. tiles of every sequence's query span, in sequence order
+    int tile_base = 0;
+    for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
+        const int i = c0 + (int)threadIdx.x;
+        int n = 0, L = 0, ntl = 0;
+        if (i < a.num_seqs) {
+            const int qs = a.qsl ? a.qsl[i] : i;
+            n = a.qsl ? a.qsl[i + 1] - qs : 1;
+            L = min(max(a.context_lens[i], 0), a.max_context_len);
+            if (qs < 0 || n < 0 || qs + n > a.num_tokens) n = 0;  // malformed span
+            ntl = n > 0 ? (n + a.tile_tokens - 1) / a.tile_tokens : 0;
+        }
+        int total;
+        const int off = tile_base + block_exclusive_scan(ntl, &total);
+        for (int k = 0; k < ntl; ++k) {
+            const int t = off + k;
+            if (t >= cap) break;
+            const int k0 = k * a.tile_tokens;
+            const int nt = min(a.tile_tokens, n - k0);
+            const int maxpos = L - n + k0 + nt - 1;  // last query position of the tile
+            const int nb = max(1, maxpos >= 0 ? (min(maxpos + 1, L) + 15) >> 4 : 0);
+            a.tiles[t] = TileDesc{i, k0, nt, nb};
+            s_tp[t] = nb;
+        }
+        tile_base += total;
+    }
+    const int ntiles = min(tile_base, cap);
+    __syncthreads();
+
+    // 2. exclusive prefix of blocks over tiles (in LDS)
+    int carry = 0;
+    for (int c0 = 0; c0 < ntiles; c0 += kPlanThreads) {
+        const int t = c0 + (int)threadIdx.x;
+        const int nb = t < ntiles ? s_tp[t] : 0;
+        int total;
+        const int before = block_exclusive_scan(nb, &total);
+        if (t < ntiles) s_tp[t] = carry + before;
+        carry += total;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) s_tp[ntiles] = carry;
+    __syncthreads();
+
+    // 3. piece size and piece starts
+    const int64_t total = (int64_t)a.num_kv_heads * carry;
+    int64_t R = a.part_blocks;
+    if (R <= 0) {
+        R = (total + a.waves - 1) / max(a.waves, 1);
+        R = max(R, (int64_t)a.min_blocks);
+    }
+    int64_t V = (total + R - 1) / R;
+    if (V > a.max_pieces) {  // never for sizes the host planned for
+        R = (total + a.max_pieces - 1) / a.max_pieces;
+        V = (total + R - 1) / R;
+    }
+    for (int64_t v = threadIdx.x; v < V; v += kPlanThreads) {
+        const int64_t b = v * R;
+        const int key = (int)(b / a.num_kv_heads);  // s_tp[t] <= key  <=>  H * s_tp[t] <= b
+        int lo = 0, hi = ntiles - 1;  // last tile whose prefix is <= key
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_tp[mid] <= key) lo = mid; else hi = mid - 1;
+        }
+        const int nb = s_tp[lo + 1] - s_tp[lo];
+        const int64_t r = b - (int64_t)a.num_kv_heads * s_tp[lo];
+        a.pieces[v] = PieceStart{lo, (int)(r / nb), (int)(r % nb), 0};
+    }
+
+    // 4. segments cut by a piece boundary, for the merge pass (a segment is
+    //    cut iff its first and last blocks fall in different pieces)
+    __shared__ int s_nsplit;
+    if (threadIdx.x == 0) s_nsplit = 0;
+    __syncthreads();
+    const int nseg = ntiles * a.num_kv_heads;
+    for (int sg = threadIdx.x; sg < nseg; sg += kPlanThreads) {
+        const int t = sg / a.num_kv_heads, h = sg % a.num_kv_heads;
+        const int nb = s_tp[t + 1] - s_tp[t];
+        const int64_t b0 = (int64_t)a.num_kv_heads * s_tp[t] + (int64_t)h * nb;
+        const int64_t v0 = b0 / R, v1 = (b0 + nb - 1) / R;
+        if (v0 != v1) {
+            const int k = atomicAdd(&s_nsplit, 1);  // list order is irrelevant
+            const TileDesc td = a.tiles[t];
+            const int qs = a.qsl ? a.qsl[td.seq] : td.seq;
+            if (k < a.max_pieces)
+                a.splits[k] = SplitSeg{qs + td.qtok0, td.ntok, h, (int)v0, (int)v1, {0, 0, 0}};
         }
     }
+    __syncthreads();
+    // records past the list are marked empty, so a merge wave needs one load
+    const int nsplit = (int)min((int64_t)s_nsplit, a.max_pieces);
+    for (int64_t k = nsplit + threadIdx.x; k < a.max_pieces; k += kPlanThreads)
+        a.splits[k] = SplitSeg{0, 0, 0, -1, -1, {0, 0, 0}};
     if (threadIdx.x == 0) {
-        a.hdr[HDR_NITEMS] = (int)min((int64_t)base, a.max_items);
-        a.hdr[HDR_COUNTER] = 0;
+        a.hdr[HDR_NTILES] = ntiles;
+        a.hdr[HDR_TOTAL] = (int)total;
+        a.hdr[HDR_R] = (int)R;
+        a.hdr[HDR_NPIECES] = (int)V;
+        a.hdr[HDR_NSPLIT] = nsplit;
     }
 }
 
 // ---- attention ---------------------------------------------------------------
 
-constexpr int kWaves = 4;
+#ifndef PA_PREFETCH
+#define PA_PREFETCH 1
+#endif
+constexpr int PF = PA_PREFETCH;  // K/V blocks in flight per wave beyond the one in use
 
+// Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
+// each block through the block table, S = K q^T on the matrix cores, online
+// softmax in registers, O += V^T P. Then either write the rows' output (the
+// wave saw the whole segment) or write a partial result into the piece's
+// slot for the merge pass.
 template <int kv, int D>
-__global__ __launch_bounds__(64 * kWaves) void attention_kernel(AttnArgs a) {
+__device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td, const int kvh,
+                                            const int j, const int take, const int piece) {
     using T = Tile<kv, D>;
-    constexpr int NW = kWaves;
-    constexpr int TPR = 4 * NW;      // merge threads per row
-    constexpr int DPT = D / TPR;     // merge dims per thread
-    constexpr int LDSW = D + 4;      // padded LDS row
-
-    __shared__ int s_unit;
-    __shared__ float s_m[NW][16];
-    __shared__ float s_l[NW][16];
-    __shared__ __attribute__((aligned(16))) float s_o[NW][16][LDSW];
-
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15;  // query row owned in MFMA layouts
     const int g = lane >> 4;  // lane group
     const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
-    const int total = a.hdr[HDR_NITEMS] * Hkv;
+    const int seq = td.seq;
+    const int L = min(a.context_lens[seq], a.max_context_len);
+    const int qs = a.qsl ? a.qsl[seq] : seq;
+    const int nspan = a.qsl ? a.qsl[seq + 1] - qs : 1;
+    const int nrows = td.ntok * G;
 
-    for (;;) {
-        if (threadIdx.x == 0) s_unit = atomicAdd(&a.hdr[HDR_COUNTER], 1);
-        __syncthreads();
-        const int u = __builtin_amdgcn_readfirstlane(s_unit);
-        if (u >= total) break;
-        const int item_idx = u / Hkv;
-        const int kvh = u - item_idx * Hkv;
-        const WorkItem it = a.items[item_idx];
-        const int seq = it.seq;
-        const int L = min(a.context_lens[seq], a.max_context_len);
-        const int qs = a.qsl ? a.qsl[seq] : seq;
-        const int nspan = a.qsl ? a.qsl[seq + 1] - qs : 1;
-        const int nrows = it.ntok * G;
-        const int tile_maxpos = L - nspan + it.qtok0 + it.ntok - 1;
-        const int kbeg = it.part * a.part_size;
-        const int kend = min(kbeg + a.part_size, tile_maxpos + 1);
-        const int nblk = kend > kbeg ? (kend - kbeg + 15) >> 4 : 0;
-        const int nparts = max(1, (tile_maxpos + 1 + a.part_size - 1) / a.part_size);
+    // this lane's query row: token qj of the tile, head kvh*G + n % G
+    const int qj = n / G;
+    const int qrow = qs + td.qtok0 + qj;
+    const int qhead = kvh * G + (n - qj * G);
+    const bool row_ok = n < nrows;
+    const int pos = row_ok ? L - nspan + td.qtok0 + qj : -1;
 
-        // this lane's query row: token j = n / G, head kvh*G + n % G
-        const int qj = n / G;
-        const int qrow = qs + it.qtok0 + qj;
-        const int qhead = kvh * G + (n - qj * G);
-        const bool row_ok = n < nrows;
-        const int pos = row_ok ? L - nspan + it.qtok0 + qj : -1;
-
-        // q operand (B of S = K q^T): dims (D/4)g + j of row n
-        typename std::conditional<kv == KV_F32, float[D / 4], uint4[D / 32]>::type qreg;
-        if constexpr (kv == KV_F32) {
-            const float* qp = (const float*)a.q + ((int64_t)qrow * Hq + qhead) * D + (D / 4) * g;
+    // q operand (B of S = K q^T), holding row n's dims in the same order as
+    // the K tile: f32 16j + 4g + e; bf16 32m + 8g + e; fp8
+    // 64(m/2) + 16g + 8(m%2) + e for MFMA step m
+    typename std::conditional<kv == KV_F32, float[D / 4], uint4[D / 32]>::type qreg;
+    if constexpr (kv == KV_F32) {
+        const float* qp = (const float*)a.q + ((int64_t)qrow * Hq + qhead) * D + 4 * g;
 #pragma unroll
-            for (int j = 0; j < D / 16; ++j) {
-                float4 x = row_ok ? ((const float4*)qp)[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-                qreg[4 * j] = x.x;
-                qreg[4 * j + 1] = x.y;
-                qreg[4 * j + 2] = x.z;
-                qreg[4 * j + 3] = x.w;
-            }
-        } else {
-            const uint4* qp = (const uint4*)((const uint16_t*)a.q +
-                                             ((int64_t)qrow * Hq + qhead) * D + (D / 4) * g);
-#pragma unroll
-            for (int j = 0; j < D / 32; ++j) qreg[j] = row_ok ? qp[j] : make_uint4(0, 0, 0, 0);
+        for (int m = 0; m < D / 16; ++m) {
+            float4 x = row_ok ? *(const float4*)(qp + 16 * m) : make_float4(0.f, 0.f, 0.f, 0.f);
+            qreg[4 * m] = x.x;
+            qreg[4 * m + 1] = x.y;
+            qreg[4 * m + 2] = x.z;
+            qreg[4 * m + 3] = x.w;
         }
+    } else {
+        const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)qrow * Hq + qhead) * D;
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+            const int d0 = kv == KV_FP8 ? 64 * (m / 2) + 16 * g + 8 * (m % 2) : 32 * m + 8 * g;
+            qreg[m] = row_ok ? *(const uint4*)(qp + d0) : make_uint4(0, 0, 0, 0);
+        }
+    }
 
-        f32x4 o[D / 16];
+    f32x4 o[D / 16];
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float m_run = -INFINITY, l_run = 0.f;
+    for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
 
-        const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
-        const int kb0 = kbeg >> 4;
-        const int nbw = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;  // my blocks
-
-        for (int c0 = 0; c0 < nbw; c0 += 64) {
-            const int cnt = min(64, nbw - c0);
-            // block ids (and fp8 scales) of up to 64 of my blocks, one per lane
-            int my_phys = 0;
-            float my_ks = 1.f, my_vs = 1.f;
-            if (lane < cnt) {
-                // ids outside the pool are clamped into it: wrong tables give
-                // undefined results, never an out-of-bounds access
-                my_phys = min(max(bt_row[kb0 + wave + NW * (c0 + lane)], 0), a.num_blocks - 1);
-                if constexpr (kv == KV_FP8) {
-                    my_ks = a.k_scale[(int64_t)my_phys * Hkv + kvh];
-                    my_vs = a.v_scale[(int64_t)my_phys * Hkv + kvh];
-                }
-            }
-            T cur, nxt;
-            {
-                const int ph = __builtin_amdgcn_readlane(my_phys, 0);
-                cur.load(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
-            }
-            for (int j = 0; j < cnt; ++j) {
-                if (j + 1 < cnt) {
-                    const int ph = __builtin_amdgcn_readlane(my_phys, j + 1);
-                    nxt.load(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
-                }
-                const int jb = kb0 + wave + NW * (c0 + j);  // logical block
-                const int t0 = jb * 16 + 4 * g;             // my first token in it
-                float c = a.scale_log2;
-                float vsc = 1.f;
-                if constexpr (kv == KV_FP8) {
-                    c *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                       __builtin_bit_cast(int, my_ks), j));
-                    vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                        __builtin_bit_cast(int, my_vs), j));
-                }
-                f32x4 s = cur.qk(qreg);
-                float sv[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sv[r] = (t0 + r <= pos) ? s[r] * c : -INFINITY;
-                float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-                mx = wave_max_xor_16_32(mx);
-                const float m_new = fmaxf(m_run, mx);
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = fexp2(m_run - m_use);
-                float p[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) p[r] = fexp2(sv[r] - m_use);
-                l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-                m_run = m_new;
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
-                if (jb * 16 + 16 > L) cur.mask_v(L - t0);  // slots past the context
-                if constexpr (kv == KV_F32) {
-                    cur.pv(p, o);
-                } else {
-                    s16x4 pb;
-                    pb[0] = (short)bf16_bits_rne(p[0] * vsc);
-                    pb[1] = (short)bf16_bits_rne(p[1] * vsc);
-                    pb[2] = (short)bf16_bits_rne(p[2] * vsc);
-                    pb[3] = (short)bf16_bits_rne(p[3] * vsc);
-                    cur.pv(pb, o);
-                }
-                cur = nxt;
+    const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
+    for (int c0 = 0; c0 < take; c0 += 64) {
+        const int cnt = min(64, take - c0);
+        // block ids (and fp8 scales) of up to 64 blocks, one per lane; ids
+        // outside the pool are clamped into it: a wrong table gives undefined
+        // results, never an out-of-bounds access
+        int my_phys = 0;
+        float my_ks = 1.f, my_vs = 1.f;
+        if (lane < cnt) {
+            my_phys = min(max(bt_row[j + c0 + lane], 0), a.num_blocks - 1);
+            if constexpr (kv == KV_FP8) {
+                my_ks = a.k_scale[(int64_t)my_phys * Hkv + kvh];
+                my_vs = a.v_scale[(int64_t)my_phys * Hkv + kvh];
             }
         }
-
-        // combine the waves' states through LDS
-        l_run = wave_sum_xor_16_32(l_run);
-        if (g == 0) {
-            s_m[wave][n] = m_run;
-            s_l[wave][n] = l_run;
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-            *(f32x4*)&s_o[wave][n][16 * dt + 4 * g] = o[dt];
-        __syncthreads();
-
-        const int rn = threadIdx.x / TPR, rc = threadIdx.x % TPR;
-        if (rn < nrows) {
-            float M = -INFINITY;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][rn]);
-            float wt[NW], l = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                wt[w] = s_m[w][rn] == -INFINITY ? 0.f : fexp2(s_m[w][rn] - M);
-                l += wt[w] * s_l[w][rn];
+        // per-block work; ring padding steps past the last block hold a
+        // copy of a valid block and are masked out entirely
+        auto consume = [&](T& cur, int i) {
+            const bool live = i < cnt;
+            const int jb = j + c0 + i;      // logical block
+            const int t0 = jb * 16 + 4 * g; // my first token in it
+            const int lim = live ? pos : -1;
+            float c = a.scale_log2;
+            float vsc = 1.f;
+            if constexpr (kv == KV_FP8) {
+                const int ii = min(i, cnt - 1);
+                c *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                   __builtin_bit_cast(int, my_ks), ii));
+                vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                    __builtin_bit_cast(int, my_vs), ii));
             }
-            float acc[DPT];
+            f32x4 sc = cur.qk(qreg);
+            float sv[4];
 #pragma unroll
-            for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+            for (int r = 0; r < 4; ++r) sv[r] = (t0 + r <= lim) ? sc[r] * c : -INFINITY;
+            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+            mx = wave_max_xor_16_32(mx);
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            const float alpha = fexp2(m_run - m_use);
+            float p[4];
 #pragma unroll
-            for (int w = 0; w < NW; ++w)
+            for (int r = 0; r < 4; ++r) p[r] = fexp2(sv[r] - m_use);
+            l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+            m_run = m_new;
 #pragma unroll
-                for (int e = 0; e < DPT; ++e) acc[e] += wt[w] * s_o[w][rn][rc * DPT + e];
-            const float inv = l > 0.f ? 1.0f / l : 0.f;
-            const int oj = rn / G;
-            const int orow = qs + it.qtok0 + oj;
-            const int ohead = kvh * G + (rn - oj * G);
-            const int64_t rowid = (int64_t)orow * Hq + ohead;
-            if (nparts == 1) {
-                if constexpr (kv == KV_F32) {
-                    float* op = (float*)a.out + rowid * D + rc * DPT;
-#pragma unroll
-                    for (int e = 0; e < DPT; ++e) op[e] = acc[e] * inv;
-                } else {
-                    uint16_t* op = (uint16_t*)a.out + rowid * D + rc * DPT;
-#pragma unroll
-                    for (int e = 0; e < DPT; ++e) op[e] = (uint16_t)bf16_bits_rne(acc[e] * inv);
-                }
-                if (a.lse && rc == 0)
-                    a.lse[rowid] = l > 0.f ? (M + __log2f(l)) * kLn2 : -INFINITY;
+            for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+            // zero V slots past the context (NaN there must not reach P.V)
+            cur.mask_v(live ? L - t0 : 0);
+            if constexpr (kv == KV_F32) {
+                cur.pv(p, o);
             } else {
-                float* pp = a.part_o + (rowid * a.max_parts + it.part) * D + rc * DPT;
+                s16x4 pb;
+                pb[0] = (short)bf16_bits_rne(p[0] * vsc);
+                pb[1] = (short)bf16_bits_rne(p[1] * vsc);
+                pb[2] = (short)bf16_bits_rne(p[2] * vsc);
+                pb[3] = (short)bf16_bits_rne(p[3] * vsc);
+                cur.pv(pb, o);
+            }
+        };
+        auto fetch = [&](T& dst, int i) {
+            const int ph = __builtin_amdgcn_readlane(my_phys, min(i, cnt - 1));
+            dst.load(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
+        };
+        // ring of PF + 1 register tiles: PF blocks stay in flight while one is
+        // consumed. Refills are unconditional (past the end they re-read the
+        // last block, an L2 hit), so the steady state is straight-line code in
+        // which each wait covers exactly one block.
+        T ring[PF + 1];
 #pragma unroll
-                for (int e = 0; e < DPT; ++e) pp[e] = acc[e] * inv;
-                if (rc == 0)
-                    a.part_lse[rowid * a.max_parts + it.part] =
-                        l > 0.f ? M + __log2f(l) : -INFINITY;
+        for (int r = 0; r < PF; ++r) fetch(ring[r], r);
+        for (int i0 = 0; i0 < cnt; i0 += PF + 1) {
+#pragma unroll
+            for (int r = 0; r <= PF; ++r) {
+                fetch(ring[(r + PF) % (PF + 1)], i0 + r + PF);
+                consume(ring[r], i0 + r);
+                // keep the steps in order: the scheduler would otherwise hoist
+                // later steps' products above their loads' waits
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        __syncthreads();
+    }
+
+    // rows' totals: l summed over the four lane groups that share a row
+    l_run = wave_sum_xor_16_32(l_run);
+    const bool whole = j == 0 && take == td.nb;
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    const int64_t rowid = (int64_t)qrow * Hq + qhead;
+    if (whole) {
+        if (row_ok) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                const int d = 16 * dt + 4 * g;
+                if constexpr (kv == KV_F32) {
+                    *(float4*)((float*)a.out + rowid * D + d) = make_float4(
+                        o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+                } else {
+                    uint2 w;
+                    w.x = bf16_bits_rne(o[dt][0] * inv) | (bf16_bits_rne(o[dt][1] * inv) << 16);
+                    w.y = bf16_bits_rne(o[dt][2] * inv) | (bf16_bits_rne(o[dt][3] * inv) << 16);
+                    *(uint2*)((uint16_t*)a.out + rowid * D + d) = w;
+                }
+            }
+            if (a.lse && g == 0)
+                a.lse[rowid] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
+        }
+        return;
+    }
+
+    if (!row_ok) return;  // only the tile's rows carry partials
+    // partials keep the accumulator's register layout: [slot][dt][lane] float4,
+    // so each store instruction writes one contiguous kilobyte
+    const int64_t slot = (int64_t)piece * 2 + (j > 0 ? SLOT_HEAD : SLOT_TAIL);
+    float4* po = (float4*)a.part_o + slot * (D / 16) * 64 + lane;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+        po[dt * 64] = make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+    if (g == 0) a.part_lse[slot * 16 + n] = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;
+
+}
+
+// One wave per workgroup; wave w streams pieces w, w + grid, ...
+template <int kv, int D>
+__global__ __launch_bounds__(64) void attention_kernel(AttnArgs a) {
+    const int V = a.hdr[HDR_NPIECES], R = a.hdr[HDR_R], total = a.hdr[HDR_TOTAL];
+    const int Hkv = a.num_kv_heads;
+    for (int v = blockIdx.x; v < V; v += gridDim.x) {
+        const PieceStart ps = a.pieces[v];
+        int t = ps.tile, kvh = ps.kvh, j = ps.j;
+        int64_t b = (int64_t)v * R;  // stream index of block j of segment (t, kvh)
+        int left = (int)min((int64_t)R, (int64_t)total - b);
+        while (left > 0) {
+            const TileDesc td = a.tiles[t];
+            const int take = min(left, td.nb - j);
+            run_segment<kv, D>(a, td, kvh, j, take, v);
+            left -= take;
+            b += take;
+            j = 0;
+            if (++kvh == Hkv) {
+                kvh = 0;
+                ++t;
+            }
+        }
     }
 }
 
 // ---- merge -------------------------------------------------------------------
 
+// Second pass: one wave per cut segment combines its pieces' partial results
+// by log-sum-exp: M = max_p lse_p, out = sum_p 2^(lse_p - M) o_p / sum_p
+// 2^(lse_p - M) ("03 -- Engines Papers", section 12; playbook Theme 4),
+// taken four pieces at a time with a running rescale so that one round trip
+// of loads covers the usual two to four pieces. Lanes keep the attention
+// kernel's accumulator layout (row lane % 16, dims 16dt + 4(lane / 16) + i).
 template <int qd, int D>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-    const int lane = threadIdx.x & 63;
-    const int64_t rowid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (rowid >= (int64_t)a.num_tokens * a.num_q_heads) return;
-    const int tok = (int)(rowid / a.num_q_heads);
-    const int np = a.tok_np[tok];
-    if (np <= 1) return;  // written directly by the attention kernel
-    const float* lp = a.part_lse + rowid * a.max_parts;
-    float M = -INFINITY;
-    for (int p = lane; p < np; p += 64) M = fmaxf(M, lp[p]);
+__global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
+    const SplitSeg sp = a.splits[blockIdx.x];
+    if (sp.v0 < 0) return;  // past the list of cut segments
+    const int lane = threadIdx.x;
+    const int n = lane & 15, g = lane >> 4;  // the attention kernel's layout
+    const int G = a.group;
+    if (n >= sp.ntok * G) return;  // rows past the tile hold no partials
+    auto slot_of = [&](int v) { return (int64_t)v * 2 + (v == sp.v0 ? SLOT_TAIL : SLOT_HEAD); };
+    float M = -INFINITY, W = 0.f;
+    float4 acc[D / 16];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    constexpr int DPL = D / 64;  // dims per lane
-    float acc[DPL];
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int v = sp.v0; v <= sp.v1; v += 4) {
+        // all four pieces' values are requested before any is used
+        float l4[4];
+        float4 x[4][D / 16];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-    float W = 0.f;
-    const float* po = a.part_o + rowid * a.max_parts * D + lane * DPL;
-    for (int p = 0; p < np; ++p) {
-        const float lv = lp[p];
-        const float w = (lv == -INFINITY) ? 0.f : fexp2(lv - M);
-        W += w;
+        for (int u = 0; u < 4; ++u) {
+            const bool ok = v + u <= sp.v1;
+            const int64_t sl = slot_of(ok ? v + u : sp.v1);
+            l4[u] = ok ? a.part_lse[sl * 16 + n] : -INFINITY;
+            const float4* po = (const float4*)a.part_o + sl * (D / 16) * 64 + lane;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) acc[e] += w * po[(int64_t)p * D + e];
+            for (int dt = 0; dt < D / 16; ++dt) x[u][dt] = po[dt * 64];
+        }
+        // fold the group into the running (M, W, acc) with one rescale
+        float m4 = M;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) m4 = fmaxf(m4, l4[u]);
+        const float rescale = M == -INFINITY ? 0.f : fexp2(M - m4);
+        W *= rescale;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            acc[dt].x *= rescale;
+            acc[dt].y *= rescale;
+            acc[dt].z *= rescale;
+            acc[dt].w *= rescale;
+        }
+        M = m4;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float w = l4[u] == -INFINITY ? 0.f : fexp2(l4[u] - M);
+            W += w;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                acc[dt].x += w * x[u][dt].x;
+                acc[dt].y += w * x[u][dt].y;
+                acc[dt].z += w * x[u][dt].z;
+                acc[dt].w += w * x[u][dt].w;
+            }
+        }
     }
     const float inv = W > 0.f ? 1.0f / W : 0.f;
-    if constexpr (qd == PA_F32) {
-        float* op = (float*)a.out + rowid * D + lane * DPL;
+    const int mj = n / G;
+    const int64_t row = (int64_t)(sp.row0 + mj) * a.num_q_heads + sp.kvh * G + (n - mj * G);
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) op[e] = acc[e] * inv;
-    } else {
-        uint16_t* op = (uint16_t*)a.out + rowid * D + lane * DPL;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) op[e] = (uint16_t)bf16_bits_rne(acc[e] * inv);
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const int d = 16 * dt + 4 * g;
+        if constexpr (qd == PA_F32) {
+            *(float4*)((float*)a.out + row * D + d) =
+                make_float4(acc[dt].x * inv, acc[dt].y * inv, acc[dt].z * inv, acc[dt].w * inv);
+        } else {
+            uint2 w;
+            w.x = bf16_bits_rne(acc[dt].x * inv) | (bf16_bits_rne(acc[dt].y * inv) << 16);
+            w.y = bf16_bits_rne(acc[dt].z * inv) | (bf16_bits_rne(acc[dt].w * inv) << 16);
+            *(uint2*)((uint16_t*)a.out + row * D + d) = w;
+        }
     }
-    if (a.lse && lane == 0) a.lse[rowid] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
+    if (a.lse && g == 0) a.lse[row] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
 }
 
 __global__ void fp8_decode_kernel(const uint8_t* in, float* out, int n) {
@@ -561,63 +709,78 @@ __global__ void fp8_decode_kernel(const uint8_t* in, float* out, int n) {
     out[i] = f.x;
 }
 
-// ---- occupancy-sized persistent grid ----------------------------------------
+// ---- launch configuration ----------------------------------------------------
 
 template <int kv, int D>
-hipError_t launch_attention_t(const AttnArgs& a, int64_t max_units, hipStream_t s) {
-    static int per_cu = -1, num_cu = 0;
-    if (per_cu < 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        e = hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        int occ = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attention_kernel<kv, D>,
-                                                         64 * kWaves, 0);
-        if (e != hipSuccess) return e;
-        per_cu = occ > 0 ? occ : 1;
+int resident_waves_t() {
+    static int cached = -1;  // device properties do not change in a process
+    if (cached < 0) {
+        int dev = 0, num_cu = 0, occ = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attention_kernel<kv, D>, 64, 0) !=
+                hipSuccess)
+            return 0;
+        cached = (occ > 0 ? occ : 1) * num_cu;
     }
-    int64_t grid = (int64_t)per_cu * num_cu;
-    if (max_units < grid) grid = max_units;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((attention_kernel<kv, D>), dim3((unsigned)grid), dim3(64 * kWaves), 0, s,
-                       a);
-    return hipGetLastError();
+    return cached;
 }
 
 }  // namespace
+
+int resident_waves(int kv_dtype, int head_dim) {
+    switch (kv_dtype * 1000 + head_dim) {
+    case PA_F32 * 1000 + 64: return resident_waves_t<KV_F32, 64>();
+    case PA_F32 * 1000 + 128: return resident_waves_t<KV_F32, 128>();
+    case PA_BF16 * 1000 + 64: return resident_waves_t<KV_BF16, 64>();
+    case PA_BF16 * 1000 + 128: return resident_waves_t<KV_BF16, 128>();
+    case PA_FP8_E4M3FN * 1000 + 64: return resident_waves_t<KV_FP8, 64>();
+    case PA_FP8_E4M3FN * 1000 + 128: return resident_waves_t<KV_FP8, 128>();
+    default: return 0;
+    }
+}
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64_t max_units,
+template <int kv, int D>
+hipError_t launch_attention_t(const AttnArgs& a, int64_t max_pieces, hipStream_t s) {
+    int64_t grid = resident_waves_t<kv, D>();
+    if (grid <= 0) return hipErrorInvalidDevice;
+    if (max_pieces < grid) grid = max_pieces;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((attention_kernel<kv, D>), dim3((unsigned)grid), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64_t max_pieces,
                             hipStream_t s) {
     switch (kv_dtype * 1000 + head_dim) {
-    case PA_F32 * 1000 + 64: return launch_attention_t<KV_F32, 64>(a, max_units, s);
-    case PA_F32 * 1000 + 128: return launch_attention_t<KV_F32, 128>(a, max_units, s);
-    case PA_BF16 * 1000 + 64: return launch_attention_t<KV_BF16, 64>(a, max_units, s);
-    case PA_BF16 * 1000 + 128: return launch_attention_t<KV_BF16, 128>(a, max_units, s);
-    case PA_FP8_E4M3FN * 1000 + 64: return launch_attention_t<KV_FP8, 64>(a, max_units, s);
-    case PA_FP8_E4M3FN * 1000 + 128: return launch_attention_t<KV_FP8, 128>(a, max_units, s);
+    case PA_F32 * 1000 + 64: return launch_attention_t<KV_F32, 64>(a, max_pieces, s);
+    case PA_F32 * 1000 + 128: return launch_attention_t<KV_F32, 128>(a, max_pieces, s);
+    case PA_BF16 * 1000 + 64: return launch_attention_t<KV_BF16, 64>(a, max_pieces, s);
+    case PA_BF16 * 1000 + 128: return launch_attention_t<KV_BF16, 128>(a, max_pieces, s);
+    case PA_FP8_E4M3FN * 1000 + 64: return launch_attention_t<KV_FP8, 64>(a, max_pieces, s);
+    case PA_FP8_E4M3FN * 1000 + 128: return launch_attention_t<KV_FP8, 128>(a, max_pieces, s);
     default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, hipStream_t s) {
-    const int64_t rows = (int64_t)a.num_tokens * a.num_q_heads;
-    const dim3 grid((unsigned)((rows + 3) / 4));
-    if (rows == 0) return hipSuccess;
+hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t max_splits,
+                        hipStream_t s) {
+    if (max_splits <= 0) return hipSuccess;
+    const dim3 grid((unsigned)max_splits), block(64);
     if (q_dtype == PA_F32 && head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<PA_F32, 64>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((merge_kernel<PA_F32, 64>), grid, block, 0, s, a);
     else if (q_dtype == PA_F32 && head_dim == 128)
-        hipLaunchKernelGGL((merge_kernel<PA_F32, 128>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((merge_kernel<PA_F32, 128>), grid, block, 0, s, a);
     else if (q_dtype == PA_BF16 && head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<PA_BF16, 64>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((merge_kernel<PA_BF16, 64>), grid, block, 0, s, a);
     else if (q_dtype == PA_BF16 && head_dim == 128)
-        hipLaunchKernelGGL((merge_kernel<PA_BF16, 128>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((merge_kernel<PA_BF16, 128>), grid, block, 0, s, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

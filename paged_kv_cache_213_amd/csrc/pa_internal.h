@@ -9,17 +9,52 @@
 
 namespace pa {
 
-// One unit of attention work before the KV-head fan-out: the query rows of
-// one tile of a sequence's span, over one partition of its keys.
-struct WorkItem {
-    int32_t seq;    // sequence index
+// A tile: up to 16 query rows of one sequence (the G heads of `ntok`
+// consecutive query tokens of its span), and the number of 16-token key
+// blocks those rows need (causal: up to the tile's last query position;
+// at least one, so a tile with no keys still gets a wave that writes its
+// zero rows).
+struct TileDesc {
+    int32_t seq;
     int32_t qtok0;  // first query token of the tile, relative to the span
-    int32_t part;   // partition index: keys [part * P, (part + 1) * P)
-    int32_t ntok;   // query tokens in the tile (1 for a decode)
+    int32_t ntok;   // query tokens in the tile
+    int32_t nb;     // key blocks the tile reads (>= 1)
+};
+
+// Where a piece of the block stream begins: segment (tile, kv head), block j.
+struct PieceStart {
+    int32_t tile;
+    int32_t kvh;
+    int32_t j;
+    int32_t pad;
+};
+
+// A segment cut by piece boundaries: its rows and the pieces holding its
+// partial results (v0 wrote its tail slot, v0+1 .. v1 their head slots).
+struct SplitSeg {
+    int32_t row0;  // first query token row of the tile
+    int32_t ntok;  // query tokens in the tile
+    int32_t kvh;
+    int32_t v0;
+    int32_t v1;
+    int32_t pad[3];
 };
 
 // Header words at the start of the workspace.
-enum { HDR_NITEMS = 0, HDR_COUNTER = 1, HDR_WORDS = 64 };
+enum {
+    HDR_NTILES = 0,
+    HDR_TOTAL = 1,
+    HDR_R = 2,
+    HDR_NPIECES = 3,
+    HDR_NSPLIT = 4,
+    HDR_WORDS = 64
+};
+
+// Partial results: two slots per piece (the segment it enters mid-way, the
+// segment it leaves unfinished), 16 rows each.
+enum { SLOT_HEAD = 0, SLOT_TAIL = 1 };
+
+constexpr int kMaxTiles = 8192;  // tiles per call (the plan keeps them in LDS)
 
 struct PlanArgs {
     const int32_t* context_lens;
@@ -27,12 +62,17 @@ struct PlanArgs {
     int32_t num_seqs;
     int32_t num_tokens;
     int32_t max_context_len;  // contexts are clamped to this
-    int32_t part_size;
     int32_t tile_tokens;
-    int64_t max_items;  // capacity of `items`
-    WorkItem* items;
+    int32_t num_kv_heads;
+    int32_t part_blocks;  // blocks per piece; 0 = balance over `waves`
+    int32_t waves;        // resident waves of the attention grid
+    int32_t min_blocks;   // smallest piece when balancing
+    int32_t max_tiles;
+    int64_t max_pieces;
+    TileDesc* tiles;
+    PieceStart* pieces;
+    SplitSeg* splits;  // [max_pieces] segments the merge pass completes
     int32_t* hdr;
-    int32_t* tok_np;  // per query token: partitions of its tile
 };
 
 struct AttnArgs {
@@ -46,30 +86,29 @@ struct AttnArgs {
     const int32_t* block_tables;
     const int32_t* context_lens;
     const int32_t* qsl;
-    const WorkItem* items;
-    int32_t* hdr;
-    float* part_lse;  // [T][Hq][max_parts], log2 units
-    float* part_o;    // [T][Hq][max_parts][D], normalized
+    const TileDesc* tiles;
+    const PieceStart* pieces;
+    const int32_t* hdr;
+    float* part_lse;  // [pieces][2][16], log2 units
+    float* part_o;    // [pieces][2][D/16][64 lanes] float4, normalized
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t group;
     int32_t num_blocks;
     int32_t max_blocks_per_seq;
     int32_t max_context_len;
-    int32_t part_size;
-    int32_t max_parts;
     float scale_log2;  // softmax scale times log2(e)
 };
 
 struct MergeArgs {
     void* out;
     float* lse;
-    const int32_t* tok_np;
+    const SplitSeg* splits;
+    const int32_t* hdr;
     const float* part_lse;
     const float* part_o;
-    int32_t num_tokens;
     int32_t num_q_heads;
-    int32_t max_parts;
+    int32_t group;
 };
 
 struct AppendArgs {
@@ -88,12 +127,18 @@ struct AppendArgs {
 
 // Launchers (host side), defined next to their kernels.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64_t max_units,
+hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64_t max_pieces,
                             hipStream_t s);
-hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, hipStream_t s);
+// Waves of the attention kernel that fit on the device at once (> 0), or 0
+// if the device cannot be queried.
+int resident_waves(int kv_dtype, int head_dim);
+hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t max_splits,
+                        hipStream_t s);
 hipError_t launch_append(int new_dtype, int kv_dtype, const AppendArgs& a, hipStream_t s);
 hipError_t launch_fp8_decode(const uint8_t* in, float* out, int n, hipStream_t s);
 
-constexpr int kDefaultPartition = 512;
+// Smallest piece (in 16-token blocks) when pieces are balanced over the
+// resident waves: tiny batches are not shredded into one-block pieces.
+constexpr int kMinPieceBlocks = 8;
 
 }  // namespace pa

@@ -9,7 +9,8 @@ import pytest
 import paged_kv_cache_213_amd as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 def _lib():
@@ -20,16 +21,18 @@ def _lib():
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)
-    return sorted(set(names))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("pa_workspace_bytes", "pa_paged_attn_decode", "pa_paged_attn_hybrid",
-                 "pa_kv_append", "pa_status_string", "pa_version", "pa_fp8_e4m3fn_to_f32"):
+                 "pa_kv_append", "pa_status_string", "pa_version", "pa_fp8_e4m3fn_to_f32",
+                 "pa_probe_stream_read", "pa_probe_copy", "pa_plan", "pa_paged_attn_run"):
         assert want in names
 
 
@@ -110,13 +113,20 @@ def test_argument_checks_before_launch():
     assert lib.pa_fp8_e4m3fn_to_f32(None, None, -1, None) == pa.PA_EINVAL
 
 
-def test_workspace_grows_with_split():
+def test_workspace_sizes():
+    """Balanced split (partition_size 0): pieces are bounded by the resident
+    waves, so the workspace does not grow with context length. An explicit
+    partition size P gives one piece per P tokens of every (tile, KV head)."""
     lib = _lib()
     s = _shape(max_blocks_per_seq=4096)
     short = lib.pa_workspace_bytes(ctypes.byref(s), 64, 64, 500, 1)
     long_ = lib.pa_workspace_bytes(ctypes.byref(s), 64, 64, 32768, 1)
-    # split partials: T * Hq * parts * (D + 1) floats
-    assert long_ - short >= 64 * 32 * 64 * 129 * 4 - 64 * 32 * 129 * 4
+    assert short == long_
+    s512 = _shape(max_blocks_per_seq=4096, partition_size=512)
+    a = lib.pa_workspace_bytes(ctypes.byref(s512), 64, 64, 512, 1)
+    b = lib.pa_workspace_bytes(ctypes.byref(s512), 64, 64, 32768, 1)
+    # pieces: 64 seqs x 8 heads x 64 partitions; partials 2 x 16 rows x (D + 1) floats
+    assert b - a >= (64 * 8 * 63) * 2 * 16 * 129 * 4
 
 
 def test_missing_library_fails_loudly(tmp_path):

@@ -221,9 +221,11 @@ def test_needle_through_every_block():
         assert torch.allclose(got, want, atol=2e-2, rtol=0), pos
 
 
-def test_cow_aliased_sequences_are_bitwise_equal():
-    """Two sequences with identical block tables and identical queries
-    read the same physical blocks and produce identical outputs."""
+def test_cow_aliased_sequences_agree():
+    """Two sequences with identical block tables and identical queries read
+    the same physical blocks and agree to the bf16 tolerance. (Not bitwise:
+    where the balanced split cuts a sequence depends on its position in the
+    batch, which changes the rounding of the merge.)"""
     wl = W.make_config("c4", small=True)
     vals, pre = prepare(wl)
     t = dev_tensors(wl, vals, pre)
@@ -240,7 +242,7 @@ def test_cow_aliased_sequences_are_bitwise_equal():
                     max_context_len=wl.max_context_len, max_query_len=wl.max_query_len,
                     partition_size=512)
     torch.cuda.synchronize()
-    assert torch.equal(out[qa].view(torch.int16), out[qb].view(torch.int16))
+    H.assert_parity(out_f64(out[qa:qa + 1]), out_f64(out[qb:qb + 1]), "bf16", "aliased rows")
 
 
 def test_large_scores_stay_finite_and_match():
@@ -274,3 +276,59 @@ def test_fp32_hybrid_span():
                            q_dtype="f32", kv_dtype="f32", seed=11, partition_size=32)
     e, _, _ = _check_step(wl)
     assert e["max_tol_err"] <= 1e-5
+
+
+def test_plan_reused_across_layers():
+    """One plan serves every layer of a step: runs on two different caches
+    (and a repeat of the first, after the arrival counters reset) equal the
+    all-in-one decode call on each cache, bit for bit."""
+    wl = W.make_config("c3", small=True)
+    vals, pre = prepare(wl)
+    t1 = dev_tensors(wl, vals, pre)
+    t2 = dict(t1, k_cache=t1["k_cache"].clone(), v_cache=(t1["v_cache"].float() * 0.5).to(
+        t1["v_cache"].dtype), q=(t1["q"].float() * -1.0).to(t1["q"].dtype))
+    ref1, _ = gpu_step(wl, t1, partition_size=0)
+    pa.kv_append(t2["k_cache"], t2["v_cache"], t2["k_new"], t2["v_new"], t2["slots"])
+    ref2, _ = gpu_step(wl, t2, partition_size=0, append=False)
+    shape = pa.make_shape(t1["q"], t1["k_cache"], t1["bt"], 0)
+    ws = torch.zeros(pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len, 1),
+                     dtype=torch.uint8, device="cuda")
+    pa.plan(shape, t1["cl"], ws, num_q_tokens=wl.num_tokens, max_query_len=1,
+            max_context_len=wl.max_context_len)
+    outs = []
+    for t in (t1, t2, t1):
+        outs.append(pa.run(shape, t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], wl.scale,
+                           ws, max_query_len=1, max_context_len=wl.max_context_len))
+    torch.cuda.synchronize()
+    for got, want in zip(outs, (ref1, ref2, ref1)):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
+def test_graph_replays_match_eager():
+    """A captured plan + append + run replays to the eager result every time,
+    with eager work and synchronizations between the replays."""
+    wl = W.make_config("c4", small=True)
+    vals, pre = prepare(wl)
+    t = dev_tensors(wl, vals, pre)
+    ref, _ = gpu_step(wl, t)  # eager
+    t2 = dev_tensors(wl, vals, pre)
+    shape = pa.make_shape(t2["q"], t2["k_cache"], t2["bt"], wl.partition_size)
+    ws = torch.zeros(pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len,
+                                        wl.max_query_len), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(t2["q"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        pa.kv_append(t2["k_cache"], t2["v_cache"], t2["k_new"], t2["v_new"], t2["slots"], stream=s)
+        pa.plan(shape, t2["cl"], ws, query_start_loc=t2["qsl"], num_q_tokens=wl.num_tokens,
+                max_query_len=wl.max_query_len, max_context_len=wl.max_context_len, stream=s)
+        pa.run(shape, t2["q"], t2["k_cache"], t2["v_cache"], t2["bt"], t2["cl"], wl.scale, ws,
+               query_start_loc=t2["qsl"], max_query_len=wl.max_query_len,
+               max_context_len=wl.max_context_len, out=out, stream=s)
+    for i in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+        _ = (t2["q"].float() * 2).sum().item()  # unrelated eager work between replays
