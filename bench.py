@@ -109,6 +109,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run the library's plain copy kernel over this many MiB, a "
+                         "kernel of known traffic for calibrating profiler byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -164,6 +167,14 @@ def main():
                    lse=lse, stream=stream)
             if timed:
                 ev[L_][1].record(stream)
+
+    if args.calibrate_copy_mib > 0:
+        nb = args.calibrate_copy_mib << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        pa.probe_copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     s = torch.cuda.Stream()
     graph = None

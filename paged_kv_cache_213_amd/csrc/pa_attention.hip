@@ -490,21 +490,18 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 my_vs = a.v_scale[(int64_t)my_phys * Hkv + kvh];
             }
         }
-        // per-block work; ring padding steps past the last block hold a
-        // copy of a valid block and are masked out entirely
+        // per-block work on block i of the chunk
         auto consume = [&](T& cur, int i) {
-            const bool live = i < cnt;
             const int jb = j + c0 + i;      // logical block
             const int t0 = jb * 16 + 4 * g; // my first token in it
-            const int lim = live ? pos : -1;
+            const int lim = pos;
             float c = a.scale_log2;
             float vsc = 1.f;
             if constexpr (kv == KV_FP8) {
-                const int ii = min(i, cnt - 1);
                 c *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                   __builtin_bit_cast(int, my_ks), ii));
+                                                   __builtin_bit_cast(int, my_ks), i));
                 vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                    __builtin_bit_cast(int, my_vs), ii));
+                                                    __builtin_bit_cast(int, my_vs), i));
             }
             f32x4 sc = cur.qk(qreg);
             float sv[4];
@@ -523,7 +520,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
             // zero V slots past the context (NaN there must not reach P.V)
-            cur.mask_v(live ? L - t0 : 0);
+            cur.mask_v(L - t0);
             if constexpr (kv == KV_F32) {
                 cur.pv(p, o);
             } else {
@@ -536,17 +533,20 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             }
         };
         auto fetch = [&](T& dst, int i) {
-            const int ph = __builtin_amdgcn_readlane(my_phys, min(i, cnt - 1));
+            const int ph = __builtin_amdgcn_readlane(my_phys, i);
             dst.load(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
         };
         // ring of PF + 1 register tiles: PF blocks stay in flight while one is
-        // consumed. Refills are unconditional (past the end they re-read the
-        // last block, an L2 hit), so the steady state is straight-line code in
-        // which each wait covers exactly one block.
+        // consumed. In the steady-state loop every refill is in range, so it
+        // is straight-line code in which each wait covers exactly one block;
+        // the last (at most 2 PF) blocks of the chunk are finished by a short
+        // tail that refills only while blocks remain.
         T ring[PF + 1];
 #pragma unroll
-        for (int r = 0; r < PF; ++r) fetch(ring[r], r);
-        for (int i0 = 0; i0 < cnt; i0 += PF + 1) {
+        for (int r = 0; r < PF; ++r)
+            if (r < cnt) fetch(ring[r], r);
+        int i0 = 0;
+        for (; i0 + 2 * PF < cnt; i0 += PF + 1) {
 #pragma unroll
             for (int r = 0; r <= PF; ++r) {
                 fetch(ring[(r + PF) % (PF + 1)], i0 + r + PF);
@@ -554,6 +554,14 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 // keep the steps in order: the scheduler would otherwise hoist
                 // later steps' products above their loads' waits
                 __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r <= 2 * PF; ++r) {
+            const int i = i0 + r;
+            if (i < cnt) {
+                if (i + PF < cnt) fetch(ring[(r + PF) % (PF + 1)], i + PF);
+                consume(ring[r % (PF + 1)], i);
             }
         }
     }
@@ -597,8 +605,13 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 }
 
 // One wave per workgroup; wave w streams pieces w, w + grid, ...
+#ifdef PA_WAVES_PER_EU
+#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU, 8)))
+#else
+#define PA_OCCUPANCY
+#endif
 template <int kv, int D>
-__global__ __launch_bounds__(64) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) PA_OCCUPANCY void attention_kernel(AttnArgs a) {
     const int V = a.hdr[HDR_NPIECES], R = a.hdr[HDR_R], total = a.hdr[HDR_TOTAL];
     const int Hkv = a.num_kv_heads;
     for (int v = blockIdx.x; v < V; v += gridDim.x) {
