@@ -149,6 +149,23 @@ int pa_paged_attn_run(const pa_shape* shape, void* out, float* lse, const void* 
                       int num_q_tokens, int max_query_len, int max_context_len, float scale,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* The two passes of pa_paged_attn_run as separate calls, for callers that
+ * schedule or time them apart. pa_paged_attn_partial writes the rows of
+ * every (tile, KV head) segment one wave saw whole, and partial results
+ * (log-sum-exp and normalized output) for segments cut by a piece boundary;
+ * pa_paged_attn_merge (the second pass) combines those partials by
+ * log-sum-exp into out / lse. Same batch arguments as the plan. */
+int pa_paged_attn_partial(const pa_shape* shape, void* out, float* lse, const void* q,
+                          const void* k_cache, const void* v_cache, const float* k_scale,
+                          const float* v_scale, const int32_t* block_tables,
+                          const int32_t* context_lens, const int32_t* query_start_loc,
+                          int num_seqs, int num_q_tokens, int max_query_len, int max_context_len,
+                          float scale, void* workspace, size_t workspace_bytes, void* stream);
+int pa_paged_attn_merge(const pa_shape* shape, void* out, float* lse, const int32_t* context_lens,
+                        const int32_t* query_start_loc, int num_seqs, int num_q_tokens,
+                        int max_query_len, int max_context_len, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 /* Append this step's new K/V rows into their slots before attention runs
  * on the same stream. k_new, v_new: [num_tokens][Hkv][D] in q_dtype.
  * slot_mapping: [num_tokens] int32, slot = physical_block * 16 + offset

@@ -65,6 +65,10 @@ def load_library(path: str = LIB_PATH):
     lib.pa_plan.argtypes = [S, P, P, I, I, I, I, P, Z, P]
     lib.pa_paged_attn_run.restype = I
     lib.pa_paged_attn_run.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
+    lib.pa_paged_attn_partial.restype = I
+    lib.pa_paged_attn_partial.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
+    lib.pa_paged_attn_merge.restype = I
+    lib.pa_paged_attn_merge.argtypes = [S, P, P, P, P, I, I, I, I, P, Z, P]
     lib.pa_kv_append.restype = I
     lib.pa_kv_append.argtypes = [S, P, P, P, P, P, P, P, I, P]
     lib.pa_fp8_e4m3fn_to_f32.restype = I
@@ -200,21 +204,28 @@ def plan(shape: PaShape, context_lens, workspace, *, query_start_loc=None, num_q
 
 def run(shape: PaShape, q, k_cache, v_cache, block_tables, context_lens, scale: float, workspace,
         *, query_start_loc=None, max_query_len: int, max_context_len: int, k_scale=None,
-        v_scale=None, out=None, lse=None, stream=None):
-    """Attention with a plan enqueued earlier by plan() (one kernel launch)."""
+        v_scale=None, out=None, lse=None, stream=None, passes: str = "both"):
+    """Attention with a plan enqueued earlier by plan(): the attention pass
+    and the merge pass ("both"), or only "partial" (pass 1) or "merge"."""
     import torch
     lib = load_library()
     T = q.shape[0]
     S = context_lens.shape[0]
     if out is None:
         out = torch.empty_like(q)
-    rc = lib.pa_paged_attn_run(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache),
-                               _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
-                               _ptr(context_lens), _ptr(query_start_loc), S, T,
-                               int(max_query_len), int(max_context_len), float(scale),
-                               _ptr(workspace), workspace.numel() * workspace.element_size(),
-                               _stream(stream))
-    _check(rc, "pa_paged_attn_run")
+    wsb = workspace.numel() * workspace.element_size()
+    if passes == "merge":
+        rc = lib.pa_paged_attn_merge(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(context_lens),
+                                     _ptr(query_start_loc), S, T, int(max_query_len),
+                                     int(max_context_len), _ptr(workspace), wsb, _stream(stream))
+        _check(rc, "pa_paged_attn_merge")
+        return out
+    fn = {"both": lib.pa_paged_attn_run, "partial": lib.pa_paged_attn_partial}[passes]
+    rc = fn(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+            _ptr(k_scale), _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+            _ptr(query_start_loc), S, T, int(max_query_len), int(max_context_len), float(scale),
+            _ptr(workspace), wsb, _stream(stream))
+    _check(rc, "pa_paged_attn_" + ("run" if passes == "both" else passes))
     return out
 
 

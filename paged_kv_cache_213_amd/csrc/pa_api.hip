@@ -19,11 +19,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
     int part_blocks = 0;  // blocks per piece, 0 = balanced over resident waves
-    int tile_tokens = 0;
-    int waves = 0;
+    int narrow_tokens = 0, wide_tokens = 0;
+    int waves[pa::NUM_STREAMS] = {0, 0};
     int64_t max_tiles = 0;
-    int64_t max_pieces = 0;
-    size_t off_tiles = 0, off_pieces = 0, off_splits = 0, off_lse = 0, off_o = 0, total = 0;
+    int64_t max_pieces[pa::NUM_STREAMS] = {0, 0};
+    size_t off_tiles = 0, off_splits = 0, total = 0;
+    size_t off_pieces[pa::NUM_STREAMS] = {0, 0};
+    size_t off_lse[pa::NUM_STREAMS] = {0, 0};
+    size_t off_o[pa::NUM_STREAMS] = {0, 0};
 };
 
 int check_shape(const pa_shape* s) {
@@ -46,32 +49,50 @@ int check_shape(const pa_shape* s) {
 // (256 compute units x 32 waves).
 constexpr int kWaveBound = 8192;
 
-// Workspace: [header][tiles][piece starts][cut segments][partials].
+// Workspace: [header][tiles][cut segments] then, per stream, [piece
+// starts][partial lse][partial outputs].
+// Spans of more than narrow_tokens query tokens get wide tiles; a batch
+// whose max_query_len is below that has none and no wide region.
 Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_context_len,
-                   bool decode) {
+                   int max_query_len, bool decode) {
     Layout l;
     const int G = s->num_q_heads / s->num_kv_heads;
-    l.tile_tokens = decode ? 1 : (16 / G > 1 ? 16 / G : 1);
+    const int wt = pa::wide_tiles(s->kv_dtype);
+    l.narrow_tokens = decode ? 1 : (16 / G > 1 ? 16 / G : 1);
+    l.wide_tokens = (16 * wt) / G > 1 ? (16 * wt) / G : 1;
     l.part_blocks = s->partition_size / PA_BLOCK_SIZE;
-    const int w = pa::resident_waves(s->kv_dtype, s->head_dim);
-    l.waves = w > 0 ? w : kWaveBound;
-    l.max_tiles = decode ? num_seqs : (int64_t)num_seqs + cdiv(num_tokens, l.tile_tokens);
+    const bool spans = !decode && max_query_len > l.narrow_tokens;
+    const int64_t tiles_of[pa::NUM_STREAMS] = {
+        spans ? (int64_t)num_seqs + cdiv(num_tokens, l.wide_tokens) : 0,  // wide: spans
+        (int64_t)num_seqs};                                                // narrow: one each
+    l.max_tiles = tiles_of[0] + tiles_of[1];
     const int64_t blocks_per_tile = cdiv(max_context_len > 0 ? max_context_len : 1, PA_BLOCK_SIZE);
-    const int64_t max_total = l.max_tiles * s->num_kv_heads * blocks_per_tile;
-    l.max_pieces = l.part_blocks > 0 ? (max_total + l.part_blocks - 1) / l.part_blocks
-                                     : (int64_t)l.waves;
-    if (l.max_pieces < 1) l.max_pieces = 1;
     size_t off = align_up(sizeof(int32_t) * pa::HDR_WORDS);
     l.off_tiles = off;
     off = align_up(off + sizeof(pa::TileDesc) * (size_t)l.max_tiles);
-    l.off_pieces = off;
-    off = align_up(off + sizeof(pa::PieceStart) * (size_t)l.max_pieces);
-    l.off_splits = off;  // every cut segment holds a piece boundary: <= pieces
-    off = align_up(off + sizeof(pa::SplitSeg) * (size_t)l.max_pieces);
-    l.off_lse = off;
-    off = align_up(off + sizeof(float) * (size_t)l.max_pieces * 2 * 16);
-    l.off_o = off;
-    off = align_up(off + sizeof(float) * (size_t)l.max_pieces * 2 * 16 * s->head_dim);
+    int64_t splits = 0;
+    for (int st = 0; st < pa::NUM_STREAMS; ++st) {
+        const int w = pa::resident_waves(s->kv_dtype, s->head_dim, st);
+        l.waves[st] = w > 0 ? w : kWaveBound;
+        const int64_t max_total = tiles_of[st] * s->num_kv_heads * blocks_per_tile;
+        int64_t mp = l.part_blocks > 0 ? (max_total + l.part_blocks - 1) / l.part_blocks
+                                       : (int64_t)l.waves[st];
+        if (tiles_of[st] == 0) mp = 0;
+        l.max_pieces[st] = mp;
+        splits += mp;
+    }
+    l.off_splits = off;  // every cut segment holds a piece boundary of its stream
+    off = align_up(off + sizeof(pa::SplitSeg) * (size_t)(splits > 0 ? splits : 1));
+    for (int st = 0; st < pa::NUM_STREAMS; ++st) {
+        const int nt = st == pa::STREAM_WIDE ? wt : 1;
+        const size_t slots = (size_t)l.max_pieces[st] * 2;
+        l.off_pieces[st] = off;
+        off = align_up(off + sizeof(pa::PieceStart) * (size_t)l.max_pieces[st]);
+        l.off_lse[st] = off;
+        off = align_up(off + sizeof(float) * slots * 16 * nt);
+        l.off_o[st] = off;
+        off = align_up(off + sizeof(float) * slots * 16 * nt * s->head_dim);
+    }
     l.total = off;
     return l;
 }
@@ -88,7 +109,7 @@ int check_batch(const pa_shape* s, const int32_t* context_lens, const int32_t* q
     if ((int64_t)max_context_len > (int64_t)PA_BLOCK_SIZE * s->max_blocks_per_seq)
         return PA_EINVAL;
     if (num_seqs > 0 && !context_lens) return PA_EINVAL;
-    *l = make_layout(s, num_seqs, num_tokens, max_context_len, qsl == nullptr);
+    *l = make_layout(s, num_seqs, num_tokens, max_context_len, max_query_len, qsl == nullptr);
     if (l->max_tiles > pa::kMaxTiles) return PA_ENOTSUP;
     if (!workspace || workspace_bytes < l->total) return PA_EWORKSPACE;
     if (((uintptr_t)workspace % kAlign) != 0) return PA_EINVAL;
@@ -121,72 +142,93 @@ int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl
     pl.num_seqs = num_seqs;
     pl.num_tokens = num_tokens;
     pl.max_context_len = max_context_len;
-    pl.tile_tokens = l.tile_tokens;
+    pl.narrow_tokens = l.narrow_tokens;
+    pl.wide_tokens = l.wide_tokens;
     pl.num_kv_heads = s->num_kv_heads;
     pl.part_blocks = l.part_blocks;
-    pl.waves = l.waves;
     pl.min_blocks = pa::kMinPieceBlocks;
     pl.max_tiles = (int32_t)l.max_tiles;
-    pl.max_pieces = l.max_pieces;
     pl.tiles = (pa::TileDesc*)(ws + l.off_tiles);
-    pl.pieces = (pa::PieceStart*)(ws + l.off_pieces);
+    for (int st = 0; st < pa::NUM_STREAMS; ++st) {
+        pl.waves[st] = l.waves[st];
+        pl.max_pieces[st] = l.max_pieces[st];
+        pl.pieces[st] = (pa::PieceStart*)(ws + l.off_pieces[st]);
+    }
     pl.splits = (pa::SplitSeg*)(ws + l.off_splits);
     pl.hdr = (int32_t*)ws;
     return pa::launch_plan(pl, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_EHIP;
 }
 
+// Which passes of the attention a call enqueues.
+enum Passes { PASS_ATTENTION = 1, PASS_MERGE = 2, PASS_BOTH = 3 };
+
 int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void* k_cache,
              const void* v_cache, const float* k_scale, const float* v_scale,
              const int32_t* block_tables, const int32_t* context_lens, const int32_t* qsl,
              int num_seqs, int num_tokens, int max_query_len, int max_context_len, float scale,
-             void* workspace, size_t workspace_bytes, void* stream) {
+             void* workspace, size_t workspace_bytes, void* stream, int passes) {
     Layout l;
     int rc = check_batch(s, context_lens, qsl, num_seqs, num_tokens, max_query_len,
                          max_context_len, workspace, workspace_bytes, &l);
     if (rc != PA_OK) return rc;
     if (num_seqs == 0 || num_tokens == 0) return PA_OK;
-    rc = check_io(s, out, q, k_cache, v_cache, k_scale, v_scale, block_tables);
-    if (rc != PA_OK) return rc;
+    if (passes & PASS_ATTENTION) {
+        rc = check_io(s, out, q, k_cache, v_cache, k_scale, v_scale, block_tables);
+        if (rc != PA_OK) return rc;
+    } else if (!out || !aligned16(out)) {
+        return PA_EINVAL;
+    }
     char* ws = (char*)workspace;
-    pa::AttnArgs aa{};
-    aa.out = out;
-    aa.lse = lse;
-    aa.q = q;
-    aa.k_cache = k_cache;
-    aa.v_cache = v_cache;
-    aa.k_scale = k_scale;
-    aa.v_scale = v_scale;
-    aa.block_tables = block_tables;
-    aa.context_lens = context_lens;
-    aa.qsl = qsl;
-    aa.tiles = (const pa::TileDesc*)(ws + l.off_tiles);
-    aa.pieces = (const pa::PieceStart*)(ws + l.off_pieces);
-    aa.hdr = (const int32_t*)ws;
-    aa.part_lse = (float*)(ws + l.off_lse);
-    aa.part_o = (float*)(ws + l.off_o);
-    aa.num_q_heads = s->num_q_heads;
-    aa.num_kv_heads = s->num_kv_heads;
-    aa.group = s->num_q_heads / s->num_kv_heads;
-    aa.num_blocks = s->num_blocks;
-    aa.max_blocks_per_seq = s->max_blocks_per_seq;
-    aa.max_context_len = max_context_len;
-    aa.scale_log2 = scale * 1.44269504088896340736f;
-    hipStream_t st = (hipStream_t)stream;
-    if (pa::launch_attention(s->kv_dtype, s->head_dim, aa, l.max_pieces, st) != hipSuccess)
-        return PA_EHIP;
-    pa::MergeArgs ma{};
-    ma.out = out;
-    ma.lse = lse;
-    ma.splits = (const pa::SplitSeg*)(ws + l.off_splits);
-    ma.hdr = (const int32_t*)ws;
-    ma.part_lse = aa.part_lse;
-    ma.part_o = aa.part_o;
-    ma.num_q_heads = s->num_q_heads;
-    ma.group = aa.group;
-    // every piece boundary cuts at most one segment: at most max_pieces - 1
-    if (l.max_pieces > 1 && pa::launch_merge(s->q_dtype, s->head_dim, ma, l.max_pieces - 1, st) !=
-                                hipSuccess)
-        return PA_EHIP;
+    hipStream_t hs = (hipStream_t)stream;
+    if (passes & PASS_ATTENTION) {
+        pa::AttnArgs aa{};
+        aa.out = out;
+        aa.lse = lse;
+        aa.q = q;
+        aa.k_cache = k_cache;
+        aa.v_cache = v_cache;
+        aa.k_scale = k_scale;
+        aa.v_scale = v_scale;
+        aa.block_tables = block_tables;
+        aa.context_lens = context_lens;
+        aa.qsl = qsl;
+        aa.tiles = (const pa::TileDesc*)(ws + l.off_tiles);
+        aa.hdr = (const int32_t*)ws;
+        aa.num_q_heads = s->num_q_heads;
+        aa.num_kv_heads = s->num_kv_heads;
+        aa.group = s->num_q_heads / s->num_kv_heads;
+        aa.num_blocks = s->num_blocks;
+        aa.max_blocks_per_seq = s->max_blocks_per_seq;
+        aa.max_context_len = max_context_len;
+        aa.scale_log2 = scale * 1.44269504088896340736f;
+        // spans first (matrix-core heavy), then the single-token tiles
+        for (int st = 0; st < pa::NUM_STREAMS; ++st) {
+            if (l.max_pieces[st] == 0) continue;
+            aa.stream = st;
+            aa.pieces = (const pa::PieceStart*)(ws + l.off_pieces[st]);
+            aa.part_lse = (float*)(ws + l.off_lse[st]);
+            aa.part_o = (float*)(ws + l.off_o[st]);
+            if (pa::launch_attention(s->kv_dtype, s->head_dim, aa, l.max_pieces[st], hs) !=
+                hipSuccess)
+                return PA_EHIP;
+        }
+    }
+    if (passes & PASS_MERGE) {
+        pa::MergeArgs ma{};
+        ma.out = out;
+        ma.lse = lse;
+        ma.splits = (const pa::SplitSeg*)(ws + l.off_splits);
+        ma.hdr = (const int32_t*)ws;
+        for (int st = 0; st < pa::NUM_STREAMS; ++st) {
+            ma.part_lse[st] = (const float*)(ws + l.off_lse[st]);
+            ma.part_o[st] = (const float*)(ws + l.off_o[st]);
+        }
+        ma.num_q_heads = s->num_q_heads;
+        ma.group = s->num_q_heads / s->num_kv_heads;
+        const int64_t records = l.max_pieces[0] + l.max_pieces[1];
+        if (records > 1 && pa::launch_merge(s->q_dtype, s->head_dim, ma, records, hs) != hipSuccess)
+            return PA_EHIP;
+    }
     return PA_OK;
 }
 
@@ -200,8 +242,8 @@ size_t pa_workspace_bytes(const pa_shape* shape, int num_seqs, int num_q_tokens,
         return 0;
     const bool decode = max_query_len <= 1 && num_q_tokens == num_seqs;
     // a decode-shaped hybrid call may use either layout: size for the larger
-    Layout a = make_layout(shape, num_seqs, num_q_tokens, max_context_len, decode);
-    Layout b = make_layout(shape, num_seqs, num_q_tokens, max_context_len, false);
+    Layout a = make_layout(shape, num_seqs, num_q_tokens, max_context_len, max_query_len, decode);
+    Layout b = make_layout(shape, num_seqs, num_q_tokens, max_context_len, max_query_len, false);
     return a.total > b.total ? a.total : b.total;
 }
 
@@ -220,7 +262,27 @@ int pa_paged_attn_run(const pa_shape* shape, void* out, float* lse, const void* 
                       void* workspace, size_t workspace_bytes, void* stream) {
     return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                     context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
-                    max_context_len, scale, workspace, workspace_bytes, stream);
+                    max_context_len, scale, workspace, workspace_bytes, stream, PASS_BOTH);
+}
+
+int pa_paged_attn_partial(const pa_shape* shape, void* out, float* lse, const void* q,
+                          const void* k_cache, const void* v_cache, const float* k_scale,
+                          const float* v_scale, const int32_t* block_tables,
+                          const int32_t* context_lens, const int32_t* query_start_loc,
+                          int num_seqs, int num_q_tokens, int max_query_len, int max_context_len,
+                          float scale, void* workspace, size_t workspace_bytes, void* stream) {
+    return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                    context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                    max_context_len, scale, workspace, workspace_bytes, stream, PASS_ATTENTION);
+}
+
+int pa_paged_attn_merge(const pa_shape* shape, void* out, float* lse, const int32_t* context_lens,
+                        const int32_t* query_start_loc, int num_seqs, int num_q_tokens,
+                        int max_query_len, int max_context_len, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    return run_impl(shape, out, lse, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                    context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                    max_context_len, 0.f, workspace, workspace_bytes, stream, PASS_MERGE);
 }
 
 int pa_paged_attn_decode(const pa_shape* shape, void* out, float* lse, const void* q,
@@ -239,7 +301,7 @@ int pa_paged_attn_decode(const pa_shape* shape, void* out, float* lse, const voi
     if (rc != PA_OK) return rc;
     return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                     context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len, scale,
-                    workspace, workspace_bytes, stream);
+                    workspace, workspace_bytes, stream, PASS_BOTH);
 }
 
 int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const void* q,
@@ -260,7 +322,7 @@ int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const voi
     if (rc != PA_OK) return rc;
     return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                     context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
-                    max_context_len, scale, workspace, workspace_bytes, stream);
+                    max_context_len, scale, workspace, workspace_bytes, stream, PASS_BOTH);
 }
 
 int pa_kv_append(const pa_shape* shape, void* k_cache, void* v_cache, const float* k_scale,

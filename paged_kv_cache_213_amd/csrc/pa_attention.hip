@@ -311,33 +311,41 @@ __device__ int block_exclusive_scan(int v, int* total) {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __shared__ int s_tp[kMaxTiles + 1];  // nb per tile, then its exclusive prefix
+    __shared__ int s_nsplit;
     const int cap = min(a.max_tiles, kMaxTiles);
+    const int H = a.num_kv_heads;
 
-    // 1. tiles of every sequence's query span, in sequence order
-    int tile_base = 0;
-    for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
-        const int i = c0 + (int)threadIdx.x;
-        int n = 0, L = 0, ntl = 0;
-        if (i < a.num_seqs) {
-            const int qs = a.qsl ? a.qsl[i] : i;
-            n = a.qsl ? a.qsl[i + 1] - qs : 1;
-            L = min(max(a.context_lens[i], 0), a.max_context_len);
-            if (qs < 0 || n < 0 || qs + n > a.num_tokens) n = 0;  // malformed span
-            ntl = n > 0 ? (n + a.tile_tokens - 1) / a.tile_tokens : 0;
+    // 1. tiles: spans longer than one narrow tile get wide tiles (stream 0),
+    //    everything else narrow ones (stream 1); sequence order within each
+    int tile_base = 0, nwide = 0;
+    for (int st = 0; st < NUM_STREAMS; ++st) {
+        for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
+            const int i = c0 + (int)threadIdx.x;
+            int n = 0, L = 0, ntl = 0, qs = 0, tt = 1;
+            if (i < a.num_seqs) {
+                qs = a.qsl ? a.qsl[i] : i;
+                n = a.qsl ? a.qsl[i + 1] - qs : 1;
+                L = min(max(a.context_lens[i], 0), a.max_context_len);
+                if (qs < 0 || n < 0 || qs + n > a.num_tokens) n = 0;  // malformed span
+                const bool wide = n > a.narrow_tokens;
+                tt = wide ? a.wide_tokens : a.narrow_tokens;
+                ntl = (n > 0 && wide == (st == STREAM_WIDE)) ? (n + tt - 1) / tt : 0;
+            }
+            int total;
+            const int off = tile_base + block_exclusive_scan(ntl, &total);
+            for (int k = 0; k < ntl; ++k) {
+                const int t = off + k;
+                if (t >= cap) break;
+                const int k0 = k * tt;
+                const int nt = min(tt, n - k0);
+                const int maxpos = L - n + k0 + nt - 1;  // last query position of the tile
+                const int nb = max(1, maxpos >= 0 ? (min(maxpos + 1, L) + 15) >> 4 : 0);
+                a.tiles[t] = TileDesc{i, k0, nt, nb, L, qs, n, 0};
+                s_tp[t] = nb;
+            }
+            tile_base += total;
         }
-        int total;
-        const int off = tile_base + block_exclusive_scan(ntl, &total);
-        for (int k = 0; k < ntl; ++k) {
-            const int t = off + k;
-            if (t >= cap) break;
-            const int k0 = k * a.tile_tokens;
-            const int nt = min(a.tile_tokens, n - k0);
-            const int maxpos = L - n + k0 + nt - 1;  // last query position of the tile
-            const int nb = max(1, maxpos >= 0 ? (min(maxpos + 1, L) + 15) >> 4 : 0);
-            a.tiles[t] = TileDesc{i, k0, nt, nb};
-            s_tp[t] = nb;
-        }
-        tile_base += total;
+        if (st == STREAM_WIDE) nwide = min(tile_base, cap);
     }
     const int ntiles = min(tile_base, cap);
     __syncthreads();
@@ -353,63 +361,79 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         carry += total;
         __syncthreads();
     }
-    if (threadIdx.x == 0) s_tp[ntiles] = carry;
+    if (threadIdx.x == 0) {
+        s_tp[ntiles] = carry;
+        s_nsplit = 0;
+    }
     __syncthreads();
 
-    // 3. piece size and piece starts
-    const int64_t total = (int64_t)a.num_kv_heads * carry;
-    int64_t R = a.part_blocks;
-    if (R <= 0) {
-        R = (total + a.waves - 1) / max(a.waves, 1);
-        R = max(R, (int64_t)a.min_blocks);
-    }
-    int64_t V = (total + R - 1) / R;
-    if (V > a.max_pieces) {  // never for sizes the host planned for
-        R = (total + a.max_pieces - 1) / a.max_pieces;
-        V = (total + R - 1) / R;
-    }
-    for (int64_t v = threadIdx.x; v < V; v += kPlanThreads) {
-        const int64_t b = v * R;
-        const int key = (int)(b / a.num_kv_heads);  // s_tp[t] <= key  <=>  H * s_tp[t] <= b
-        int lo = 0, hi = ntiles - 1;  // last tile whose prefix is <= key
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_tp[mid] <= key) lo = mid; else hi = mid - 1;
+    // 3. per stream: piece size, piece starts
+    int64_t Rs[NUM_STREAMS];
+    for (int st = 0; st < NUM_STREAMS; ++st) {
+        const int t_lo = st == STREAM_WIDE ? 0 : nwide;
+        const int t_hi = st == STREAM_WIDE ? nwide : ntiles;
+        const int64_t total = (int64_t)H * (s_tp[t_hi] - s_tp[t_lo]);
+        int64_t R = a.part_blocks;
+        if (R <= 0) {
+            R = (total + a.waves[st] - 1) / max(a.waves[st], 1);
+            R = max(R, (int64_t)a.min_blocks);
         }
-        const int nb = s_tp[lo + 1] - s_tp[lo];
-        const int64_t r = b - (int64_t)a.num_kv_heads * s_tp[lo];
-        a.pieces[v] = PieceStart{lo, (int)(r / nb), (int)(r % nb), 0};
+        int64_t V = (total + R - 1) / R;
+        if (a.max_pieces[st] == 0) {  // no room: the caller understated max_query_len
+            V = 0;
+        } else if (V > a.max_pieces[st]) {  // never for sizes the host planned for
+            R = (total + a.max_pieces[st] - 1) / a.max_pieces[st];
+            V = (total + R - 1) / R;
+        }
+        Rs[st] = R;
+        for (int64_t v = threadIdx.x; v < V; v += kPlanThreads) {
+            const int64_t b = (int64_t)H * s_tp[t_lo] + v * R;  // global block index
+            const int key = (int)(b / H);  // s_tp[t] <= key  <=>  H * s_tp[t] <= b
+            int lo = t_lo, hi = t_hi - 1;  // last tile whose prefix is <= key
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_tp[mid] <= key) lo = mid; else hi = mid - 1;
+            }
+            const int nb = s_tp[lo + 1] - s_tp[lo];
+            const int64_t r = b - (int64_t)H * s_tp[lo];
+            PieceStart ps{};
+            ps.tile = lo;
+            ps.kvh = (int)(r / nb);
+            ps.j = (int)(r % nb);
+            ps.td = a.tiles[lo];
+            a.pieces[st][v] = ps;
+        }
+        if (threadIdx.x == 0) {
+            a.hdr[HDR_STREAM + 4 * st + HDR_TOTAL] = (int)total;
+            a.hdr[HDR_STREAM + 4 * st + HDR_R] = (int)R;
+            a.hdr[HDR_STREAM + 4 * st + HDR_NPIECES] = (int)V;
+        }
     }
 
     // 4. segments cut by a piece boundary, for the merge pass (a segment is
     //    cut iff its first and last blocks fall in different pieces)
-    __shared__ int s_nsplit;
-    if (threadIdx.x == 0) s_nsplit = 0;
-    __syncthreads();
-    const int nseg = ntiles * a.num_kv_heads;
-    for (int sg = threadIdx.x; sg < nseg; sg += kPlanThreads) {
-        const int t = sg / a.num_kv_heads, h = sg % a.num_kv_heads;
+    const int64_t max_splits = a.max_pieces[0] + a.max_pieces[1];
+    for (int sg = threadIdx.x; sg < ntiles * H; sg += kPlanThreads) {
+        const int t = sg / H, h = sg % H;
+        const int st = t < nwide ? STREAM_WIDE : STREAM_NARROW;
+        const int t_lo = st == STREAM_WIDE ? 0 : nwide;
         const int nb = s_tp[t + 1] - s_tp[t];
-        const int64_t b0 = (int64_t)a.num_kv_heads * s_tp[t] + (int64_t)h * nb;
-        const int64_t v0 = b0 / R, v1 = (b0 + nb - 1) / R;
+        const int64_t b0 = (int64_t)H * (s_tp[t] - s_tp[t_lo]) + (int64_t)h * nb;
+        const int64_t v0 = b0 / Rs[st], v1 = (b0 + nb - 1) / Rs[st];
         if (v0 != v1) {
             const int k = atomicAdd(&s_nsplit, 1);  // list order is irrelevant
             const TileDesc td = a.tiles[t];
-            const int qs = a.qsl ? a.qsl[td.seq] : td.seq;
-            if (k < a.max_pieces)
-                a.splits[k] = SplitSeg{qs + td.qtok0, td.ntok, h, (int)v0, (int)v1, {0, 0, 0}};
+            if (k < max_splits)
+                a.splits[k] = SplitSeg{td.qs + td.qtok0, td.ntok, h, (int)v0, (int)v1, st, {0, 0}};
         }
     }
     __syncthreads();
     // records past the list are marked empty, so a merge wave needs one load
-    const int nsplit = (int)min((int64_t)s_nsplit, a.max_pieces);
-    for (int64_t k = nsplit + threadIdx.x; k < a.max_pieces; k += kPlanThreads)
-        a.splits[k] = SplitSeg{0, 0, 0, -1, -1, {0, 0, 0}};
+    const int nsplit = (int)min((int64_t)s_nsplit, max_splits);
+    for (int64_t k = nsplit + threadIdx.x; k < max_splits; k += kPlanThreads)
+        a.splits[k] = SplitSeg{0, 0, 0, -1, -1, 0, {0, 0}};
     if (threadIdx.x == 0) {
         a.hdr[HDR_NTILES] = ntiles;
-        a.hdr[HDR_TOTAL] = (int)total;
-        a.hdr[HDR_R] = (int)R;
-        a.hdr[HDR_NPIECES] = (int)V;
         a.hdr[HDR_NSPLIT] = nsplit;
     }
 }
@@ -423,57 +447,70 @@ constexpr int PF = PA_PREFETCH;  // K/V blocks in flight per wave beyond the one
 
 // Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
 // each block through the block table, S = K q^T on the matrix cores, online
-// softmax in registers, O += V^T P. Then either write the rows' output (the
-// wave saw the whole segment) or write a partial result into the piece's
-// slot for the merge pass.
-template <int kv, int D>
+// softmax in registers, O += V^T P, for NT 16-row tiles of query rows that
+// share every K/V block the wave loads. Then either write the rows' output
+// (the wave saw the whole segment) or write a partial result into the
+// piece's slot for the merge pass.
+template <int kv, int D, int NT>
 __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td, const int kvh,
                                             const int j, const int take, const int piece) {
     using T = Tile<kv, D>;
+    using QReg = typename std::conditional<kv == KV_F32, float[D / 4], uint4[D / 32]>::type;
     const int lane = threadIdx.x & 63;
-    const int n = lane & 15;  // query row owned in MFMA layouts
+    const int n = lane & 15;  // query row owned in MFMA layouts (within a row tile)
     const int g = lane >> 4;  // lane group
     const int Hkv = a.num_kv_heads, G = a.group, Hq = a.num_q_heads;
     const int seq = td.seq;
-    const int L = min(a.context_lens[seq], a.max_context_len);
-    const int qs = a.qsl ? a.qsl[seq] : seq;
-    const int nspan = a.qsl ? a.qsl[seq + 1] - qs : 1;
+    const int L = td.L, qs = td.qs, nspan = td.nspan;
     const int nrows = td.ntok * G;
 
-    // this lane's query row: token qj of the tile, head kvh*G + n % G
-    const int qj = n / G;
-    const int qrow = qs + td.qtok0 + qj;
-    const int qhead = kvh * G + (n - qj * G);
-    const bool row_ok = n < nrows;
-    const int pos = row_ok ? L - nspan + td.qtok0 + qj : -1;
-
-    // q operand (B of S = K q^T), holding row n's dims in the same order as
-    // the K tile: f32 16j + 4g + e; bf16 32m + 8g + e; fp8
-    // 64(m/2) + 16g + 8(m%2) + e for MFMA step m
-    typename std::conditional<kv == KV_F32, float[D / 4], uint4[D / 32]>::type qreg;
-    if constexpr (kv == KV_F32) {
-        const float* qp = (const float*)a.q + ((int64_t)qrow * Hq + qhead) * D + 4 * g;
+    // this lane's query row in row tile r: tile row 16 r + n = token qj,
+    // head kvh*G + (row % G)
+    QReg qreg[NT];
+    int pos[NT];
+    int64_t rowid[NT];
+    bool row_ok[NT];
 #pragma unroll
-        for (int m = 0; m < D / 16; ++m) {
-            float4 x = row_ok ? *(const float4*)(qp + 16 * m) : make_float4(0.f, 0.f, 0.f, 0.f);
-            qreg[4 * m] = x.x;
-            qreg[4 * m + 1] = x.y;
-            qreg[4 * m + 2] = x.z;
-            qreg[4 * m + 3] = x.w;
-        }
-    } else {
-        const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)qrow * Hq + qhead) * D;
+    for (int r = 0; r < NT; ++r) {
+        const int rr = 16 * r + n;
+        const int qj = rr / G;
+        row_ok[r] = rr < nrows;
+        pos[r] = row_ok[r] ? L - nspan + td.qtok0 + qj : -1;
+        rowid[r] = (int64_t)(qs + td.qtok0 + qj) * Hq + kvh * G + (rr - qj * G);
+        // q operand (B of S = K q^T), holding the row's dims in the same order
+        // as the K tile: f32 16m + 4g + e; bf16 32m + 8g + e; fp8
+        // 64(m/2) + 16g + 8(m%2) + e for MFMA step m
+        if constexpr (kv == KV_F32) {
+            const float* qp = (const float*)a.q + rowid[r] * D + 4 * g;
 #pragma unroll
-        for (int m = 0; m < D / 32; ++m) {
-            const int d0 = kv == KV_FP8 ? 64 * (m / 2) + 16 * g + 8 * (m % 2) : 32 * m + 8 * g;
-            qreg[m] = row_ok ? *(const uint4*)(qp + d0) : make_uint4(0, 0, 0, 0);
+            for (int m = 0; m < D / 16; ++m) {
+                float4 x = row_ok[r] ? *(const float4*)(qp + 16 * m)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+                qreg[r][4 * m] = x.x;
+                qreg[r][4 * m + 1] = x.y;
+                qreg[r][4 * m + 2] = x.z;
+                qreg[r][4 * m + 3] = x.w;
+            }
+        } else {
+            const uint16_t* qp = (const uint16_t*)a.q + rowid[r] * D;
+#pragma unroll
+            for (int m = 0; m < D / 32; ++m) {
+                const int d0 =
+                    kv == KV_FP8 ? 64 * (m / 2) + 16 * g + 8 * (m % 2) : 32 * m + 8 * g;
+                qreg[r][m] = row_ok[r] ? *(const uint4*)(qp + d0) : make_uint4(0, 0, 0, 0);
+            }
         }
     }
 
-    f32x4 o[D / 16];
+    f32x4 o[NT][D / 16];
+    float m_run[NT], l_run[NT];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int r = 0; r < NT; ++r) {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[r] = -INFINITY;
+        l_run[r] = 0.f;
+    }
 
     const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
     for (int c0 = 0; c0 < take; c0 += 64) {
@@ -492,9 +529,8 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         }
         // per-block work on block i of the chunk
         auto consume = [&](T& cur, int i) {
-            const int jb = j + c0 + i;      // logical block
-            const int t0 = jb * 16 + 4 * g; // my first token in it
-            const int lim = pos;
+            const int jb = j + c0 + i;       // logical block
+            const int t0 = jb * 16 + 4 * g;  // my first token in it
             float c = a.scale_log2;
             float vsc = 1.f;
             if constexpr (kv == KV_FP8) {
@@ -503,34 +539,37 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                     __builtin_bit_cast(int, my_vs), i));
             }
-            f32x4 sc = cur.qk(qreg);
-            float sv[4];
+            typename std::conditional<kv == KV_F32, float[NT][4], s16x4[NT]>::type pk;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sv[r] = (t0 + r <= lim) ? sc[r] * c : -INFINITY;
-            float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-            mx = wave_max_xor_16_32(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = fexp2(m_run - m_use);
-            float p[4];
+            for (int r = 0; r < NT; ++r) {
+                f32x4 sc = cur.qk(qreg[r]);
+                float sv[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = fexp2(sv[r] - m_use);
-            l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-            m_run = m_new;
+                for (int e = 0; e < 4; ++e) sv[e] = (t0 + e <= pos[r]) ? sc[e] * c : -INFINITY;
+                float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+                mx = wave_max_xor_16_32(mx);
+                const float m_new = fmaxf(m_run[r], mx);
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                const float alpha = fexp2(m_run[r] - m_use);
+                float p[4];
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) o[dt] *= alpha;
+                for (int e = 0; e < 4; ++e) p[e] = fexp2(sv[e] - m_use);
+                l_run[r] = l_run[r] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+                m_run[r] = m_new;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) o[r][dt] *= alpha;
+                if constexpr (kv == KV_F32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pk[r][e] = p[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pk[r][e] = (short)bf16_bits_rne(p[e] * vsc);
+                }
+            }
             // zero V slots past the context (NaN there must not reach P.V)
             cur.mask_v(L - t0);
-            if constexpr (kv == KV_F32) {
-                cur.pv(p, o);
-            } else {
-                s16x4 pb;
-                pb[0] = (short)bf16_bits_rne(p[0] * vsc);
-                pb[1] = (short)bf16_bits_rne(p[1] * vsc);
-                pb[2] = (short)bf16_bits_rne(p[2] * vsc);
-                pb[3] = (short)bf16_bits_rne(p[3] * vsc);
-                cur.pv(pb, o);
-            }
+#pragma unroll
+            for (int r = 0; r < NT; ++r) cur.pv(pk[r], o[r]);
         };
         auto fetch = [&](T& dst, int i) {
             const int ph = __builtin_amdgcn_readlane(my_phys, i);
@@ -566,69 +605,74 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         }
     }
 
-    // rows' totals: l summed over the four lane groups that share a row
-    l_run = wave_sum_xor_16_32(l_run);
     const bool whole = j == 0 && take == td.nb;
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    const int64_t rowid = (int64_t)qrow * Hq + qhead;
-    if (whole) {
-        if (row_ok) {
+    const int64_t slot = (int64_t)piece * 2 + (j > 0 ? SLOT_HEAD : SLOT_TAIL);
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+        // row totals: l summed over the four lane groups that share a row
+        const float l = wave_sum_xor_16_32(l_run[r]);
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        if (!row_ok[r]) continue;
+        if (whole) {
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
                 const int d = 16 * dt + 4 * g;
                 if constexpr (kv == KV_F32) {
-                    *(float4*)((float*)a.out + rowid * D + d) = make_float4(
-                        o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
+                    *(float4*)((float*)a.out + rowid[r] * D + d) =
+                        make_float4(o[r][dt][0] * inv, o[r][dt][1] * inv, o[r][dt][2] * inv,
+                                    o[r][dt][3] * inv);
                 } else {
                     uint2 w;
-                    w.x = bf16_bits_rne(o[dt][0] * inv) | (bf16_bits_rne(o[dt][1] * inv) << 16);
-                    w.y = bf16_bits_rne(o[dt][2] * inv) | (bf16_bits_rne(o[dt][3] * inv) << 16);
-                    *(uint2*)((uint16_t*)a.out + rowid * D + d) = w;
+                    w.x = bf16_bits_rne(o[r][dt][0] * inv) |
+                          (bf16_bits_rne(o[r][dt][1] * inv) << 16);
+                    w.y = bf16_bits_rne(o[r][dt][2] * inv) |
+                          (bf16_bits_rne(o[r][dt][3] * inv) << 16);
+                    *(uint2*)((uint16_t*)a.out + rowid[r] * D + d) = w;
                 }
             }
             if (a.lse && g == 0)
-                a.lse[rowid] = l_run > 0.f ? (m_run + __log2f(l_run)) * kLn2 : -INFINITY;
-        }
-        return;
-    }
-
-    if (!row_ok) return;  // only the tile's rows carry partials
-    // partials keep the accumulator's register layout: [slot][dt][lane] float4,
-    // so each store instruction writes one contiguous kilobyte
-    const int64_t slot = (int64_t)piece * 2 + (j > 0 ? SLOT_HEAD : SLOT_TAIL);
-    float4* po = (float4*)a.part_o + slot * (D / 16) * 64 + lane;
+                a.lse[rowid[r]] = l > 0.f ? (m_run[r] + __log2f(l)) * kLn2 : -INFINITY;
+        } else {
+            // partials keep the accumulator's register layout:
+            // [slot][r][dt][lane] float4, one contiguous kilobyte per store
+            float4* po = (float4*)a.part_o + ((slot * NT + r) * (D / 16)) * 64 + lane;
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt)
-        po[dt * 64] = make_float4(o[dt][0] * inv, o[dt][1] * inv, o[dt][2] * inv, o[dt][3] * inv);
-    if (g == 0) a.part_lse[slot * 16 + n] = l_run > 0.f ? m_run + __log2f(l_run) : -INFINITY;
-
+            for (int dt = 0; dt < D / 16; ++dt)
+                po[dt * 64] = make_float4(o[r][dt][0] * inv, o[r][dt][1] * inv,
+                                          o[r][dt][2] * inv, o[r][dt][3] * inv);
+            if (g == 0)
+                a.part_lse[slot * (16 * NT) + 16 * r + n] =
+                    l > 0.f ? m_run[r] + __log2f(l) : -INFINITY;
+        }
+    }
 }
 
-// One wave per workgroup; wave w streams pieces w, w + grid, ...
+// One wave per workgroup; wave w streams pieces w, w + grid, ... of its
+// stream (tiles of NT row tiles).
 #ifdef PA_WAVES_PER_EU
 #define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU, 8)))
 #else
 #define PA_OCCUPANCY
 #endif
-template <int kv, int D>
+template <int kv, int D, int NT>
 __global__ __launch_bounds__(64) PA_OCCUPANCY void attention_kernel(AttnArgs a) {
-    const int V = a.hdr[HDR_NPIECES], R = a.hdr[HDR_R], total = a.hdr[HDR_TOTAL];
+    const int* h = a.hdr + HDR_STREAM + 4 * a.stream;
+    const int V = h[HDR_NPIECES], R = h[HDR_R], total = h[HDR_TOTAL];
     const int Hkv = a.num_kv_heads;
     for (int v = blockIdx.x; v < V; v += gridDim.x) {
         const PieceStart ps = a.pieces[v];
         int t = ps.tile, kvh = ps.kvh, j = ps.j;
-        int64_t b = (int64_t)v * R;  // stream index of block j of segment (t, kvh)
-        int left = (int)min((int64_t)R, (int64_t)total - b);
+        TileDesc td = ps.td;
+        int left = (int)min((int64_t)R, (int64_t)total - (int64_t)v * R);
         while (left > 0) {
-            const TileDesc td = a.tiles[t];
             const int take = min(left, td.nb - j);
-            run_segment<kv, D>(a, td, kvh, j, take, v);
+            run_segment<kv, D, NT>(a, td, kvh, j, take, v);
             left -= take;
-            b += take;
             j = 0;
             if (++kvh == Hkv) {
                 kvh = 0;
                 ++t;
+                if (left > 0) td = a.tiles[t];
             }
         }
     }
@@ -649,69 +693,75 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     const int lane = threadIdx.x;
     const int n = lane & 15, g = lane >> 4;  // the attention kernel's layout
     const int G = a.group;
-    if (n >= sp.ntok * G) return;  // rows past the tile hold no partials
+    const int nt = sp.stream == STREAM_WIDE ? wide_tiles(qd) : 1;  // row tiles per slot
+    const float* part_lse = a.part_lse[sp.stream];
+    const float4* part_o = (const float4*)a.part_o[sp.stream];
     auto slot_of = [&](int v) { return (int64_t)v * 2 + (v == sp.v0 ? SLOT_TAIL : SLOT_HEAD); };
-    float M = -INFINITY, W = 0.f;
-    float4 acc[D / 16];
+    for (int r = 0; r < nt; ++r) {
+        const int rr = 16 * r + n;
+        if (rr >= sp.ntok * G) break;  // rows past the tile hold no partials
+        float M = -INFINITY, W = 0.f;
+        float4 acc[D / 16];
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int v = sp.v0; v <= sp.v1; v += 4) {
-        // all four pieces' values are requested before any is used
-        float l4[4];
-        float4 x[4][D / 16];
+        for (int dt = 0; dt < D / 16; ++dt) acc[dt] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int v = sp.v0; v <= sp.v1; v += 4) {
+            // all four pieces' values are requested before any is used
+            float l4[4];
+            float4 x[4][D / 16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bool ok = v + u <= sp.v1;
-            const int64_t sl = slot_of(ok ? v + u : sp.v1);
-            l4[u] = ok ? a.part_lse[sl * 16 + n] : -INFINITY;
-            const float4* po = (const float4*)a.part_o + sl * (D / 16) * 64 + lane;
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = v + u <= sp.v1;
+                const int64_t sl = slot_of(ok ? v + u : sp.v1);
+                l4[u] = ok ? part_lse[sl * (16 * nt) + rr] : -INFINITY;
+                const float4* po = part_o + ((sl * nt + r) * (D / 16)) * 64 + lane;
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) x[u][dt] = po[dt * 64];
-        }
-        // fold the group into the running (M, W, acc) with one rescale
-        float m4 = M;
+                for (int dt = 0; dt < D / 16; ++dt) x[u][dt] = po[dt * 64];
+            }
+            // fold the group into the running (M, W, acc) with one rescale
+            float m4 = M;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) m4 = fmaxf(m4, l4[u]);
-        const float rescale = M == -INFINITY ? 0.f : fexp2(M - m4);
-        W *= rescale;
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            acc[dt].x *= rescale;
-            acc[dt].y *= rescale;
-            acc[dt].z *= rescale;
-            acc[dt].w *= rescale;
-        }
-        M = m4;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float w = l4[u] == -INFINITY ? 0.f : fexp2(l4[u] - M);
-            W += w;
+            for (int u = 0; u < 4; ++u) m4 = fmaxf(m4, l4[u]);
+            const float rescale = M == -INFINITY ? 0.f : fexp2(M - m4);
+            W *= rescale;
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
-                acc[dt].x += w * x[u][dt].x;
-                acc[dt].y += w * x[u][dt].y;
-                acc[dt].z += w * x[u][dt].z;
-                acc[dt].w += w * x[u][dt].w;
+                acc[dt].x *= rescale;
+                acc[dt].y *= rescale;
+                acc[dt].z *= rescale;
+                acc[dt].w *= rescale;
+            }
+            M = m4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float w = l4[u] == -INFINITY ? 0.f : fexp2(l4[u] - M);
+                W += w;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) {
+                    acc[dt].x += w * x[u][dt].x;
+                    acc[dt].y += w * x[u][dt].y;
+                    acc[dt].z += w * x[u][dt].z;
+                    acc[dt].w += w * x[u][dt].w;
+                }
             }
         }
-    }
-    const float inv = W > 0.f ? 1.0f / W : 0.f;
-    const int mj = n / G;
-    const int64_t row = (int64_t)(sp.row0 + mj) * a.num_q_heads + sp.kvh * G + (n - mj * G);
+        const float inv = W > 0.f ? 1.0f / W : 0.f;
+        const int mj = rr / G;
+        const int64_t row = (int64_t)(sp.row0 + mj) * a.num_q_heads + sp.kvh * G + (rr - mj * G);
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-        const int d = 16 * dt + 4 * g;
-        if constexpr (qd == PA_F32) {
-            *(float4*)((float*)a.out + row * D + d) =
-                make_float4(acc[dt].x * inv, acc[dt].y * inv, acc[dt].z * inv, acc[dt].w * inv);
-        } else {
-            uint2 w;
-            w.x = bf16_bits_rne(acc[dt].x * inv) | (bf16_bits_rne(acc[dt].y * inv) << 16);
-            w.y = bf16_bits_rne(acc[dt].z * inv) | (bf16_bits_rne(acc[dt].w * inv) << 16);
-            *(uint2*)((uint16_t*)a.out + row * D + d) = w;
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const int d = 16 * dt + 4 * g;
+            if constexpr (qd == PA_F32) {
+                *(float4*)((float*)a.out + row * D + d) = make_float4(
+                    acc[dt].x * inv, acc[dt].y * inv, acc[dt].z * inv, acc[dt].w * inv);
+            } else {
+                uint2 w;
+                w.x = bf16_bits_rne(acc[dt].x * inv) | (bf16_bits_rne(acc[dt].y * inv) << 16);
+                w.y = bf16_bits_rne(acc[dt].z * inv) | (bf16_bits_rne(acc[dt].w * inv) << 16);
+                *(uint2*)((uint16_t*)a.out + row * D + d) = w;
+            }
         }
+        if (a.lse && g == 0) a.lse[row] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
     }
-    if (a.lse && g == 0) a.lse[row] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
 }
 
 __global__ void fp8_decode_kernel(const uint8_t* in, float* out, int n) {
@@ -724,7 +774,7 @@ __global__ void fp8_decode_kernel(const uint8_t* in, float* out, int n) {
 
 // ---- launch configuration ----------------------------------------------------
 
-template <int kv, int D>
+template <int kv, int D, int NT>
 int resident_waves_t() {
     static int cached = -1;  // device properties do not change in a process
     if (cached < 0) {
@@ -732,24 +782,44 @@ int resident_waves_t() {
         if (hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
                 hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attention_kernel<kv, D>, 64, 0) !=
-                hipSuccess)
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attention_kernel<kv, D, NT>, 64,
+                                                         0) != hipSuccess)
             return 0;
         cached = (occ > 0 ? occ : 1) * num_cu;
     }
     return cached;
 }
 
+template <int kv, int D>
+int resident_waves_d(int stream) {
+    return stream == STREAM_WIDE ? resident_waves_t<kv, D, wide_tiles(kv)>()
+                                 : resident_waves_t<kv, D, 1>();
+}
+
+template <int kv, int D>
+hipError_t launch_attention_d(const AttnArgs& a, int64_t max_pieces, hipStream_t s) {
+    int64_t grid = resident_waves_d<kv, D>(a.stream);
+    if (grid <= 0) return hipErrorInvalidDevice;
+    if (max_pieces < grid) grid = max_pieces;
+    if (grid < 1) grid = 1;
+    if (a.stream == STREAM_WIDE)
+        hipLaunchKernelGGL((attention_kernel<kv, D, wide_tiles(kv)>), dim3((unsigned)grid),
+                           dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL((attention_kernel<kv, D, 1>), dim3((unsigned)grid), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
-int resident_waves(int kv_dtype, int head_dim) {
+int resident_waves(int kv_dtype, int head_dim, int stream) {
     switch (kv_dtype * 1000 + head_dim) {
-    case PA_F32 * 1000 + 64: return resident_waves_t<KV_F32, 64>();
-    case PA_F32 * 1000 + 128: return resident_waves_t<KV_F32, 128>();
-    case PA_BF16 * 1000 + 64: return resident_waves_t<KV_BF16, 64>();
-    case PA_BF16 * 1000 + 128: return resident_waves_t<KV_BF16, 128>();
-    case PA_FP8_E4M3FN * 1000 + 64: return resident_waves_t<KV_FP8, 64>();
-    case PA_FP8_E4M3FN * 1000 + 128: return resident_waves_t<KV_FP8, 128>();
+    case PA_F32 * 1000 + 64: return resident_waves_d<KV_F32, 64>(stream);
+    case PA_F32 * 1000 + 128: return resident_waves_d<KV_F32, 128>(stream);
+    case PA_BF16 * 1000 + 64: return resident_waves_d<KV_BF16, 64>(stream);
+    case PA_BF16 * 1000 + 128: return resident_waves_d<KV_BF16, 128>(stream);
+    case PA_FP8_E4M3FN * 1000 + 64: return resident_waves_d<KV_FP8, 64>(stream);
+    case PA_FP8_E4M3FN * 1000 + 128: return resident_waves_d<KV_FP8, 128>(stream);
     default: return 0;
     }
 }
@@ -759,25 +829,15 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int kv, int D>
-hipError_t launch_attention_t(const AttnArgs& a, int64_t max_pieces, hipStream_t s) {
-    int64_t grid = resident_waves_t<kv, D>();
-    if (grid <= 0) return hipErrorInvalidDevice;
-    if (max_pieces < grid) grid = max_pieces;
-    if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((attention_kernel<kv, D>), dim3((unsigned)grid), dim3(64), 0, s, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64_t max_pieces,
                             hipStream_t s) {
     switch (kv_dtype * 1000 + head_dim) {
-    case PA_F32 * 1000 + 64: return launch_attention_t<KV_F32, 64>(a, max_pieces, s);
-    case PA_F32 * 1000 + 128: return launch_attention_t<KV_F32, 128>(a, max_pieces, s);
-    case PA_BF16 * 1000 + 64: return launch_attention_t<KV_BF16, 64>(a, max_pieces, s);
-    case PA_BF16 * 1000 + 128: return launch_attention_t<KV_BF16, 128>(a, max_pieces, s);
-    case PA_FP8_E4M3FN * 1000 + 64: return launch_attention_t<KV_FP8, 64>(a, max_pieces, s);
-    case PA_FP8_E4M3FN * 1000 + 128: return launch_attention_t<KV_FP8, 128>(a, max_pieces, s);
+    case PA_F32 * 1000 + 64: return launch_attention_d<KV_F32, 64>(a, max_pieces, s);
+    case PA_F32 * 1000 + 128: return launch_attention_d<KV_F32, 128>(a, max_pieces, s);
+    case PA_BF16 * 1000 + 64: return launch_attention_d<KV_BF16, 64>(a, max_pieces, s);
+    case PA_BF16 * 1000 + 128: return launch_attention_d<KV_BF16, 128>(a, max_pieces, s);
+    case PA_FP8_E4M3FN * 1000 + 64: return launch_attention_d<KV_FP8, 64>(a, max_pieces, s);
+    case PA_FP8_E4M3FN * 1000 + 128: return launch_attention_d<KV_FP8, 128>(a, max_pieces, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -19,34 +19,51 @@ struct TileDesc {
     int32_t qtok0;  // first query token of the tile, relative to the span
     int32_t ntok;   // query tokens in the tile
     int32_t nb;     // key blocks the tile reads (>= 1)
+    int32_t L;      // the sequence's context length (clamped)
+    int32_t qs;     // the sequence's first query token row
+    int32_t nspan;  // the sequence's query tokens
+    int32_t pad;
 };
 
-// Where a piece of the block stream begins: segment (tile, kv head), block j.
+// Where a piece of the block stream begins: segment (tile, kv head), block j,
+// with a copy of that tile's record so a wave starts with one load.
 struct PieceStart {
     int32_t tile;
     int32_t kvh;
     int32_t j;
-    int32_t pad;
+    int32_t pad[5];
+    TileDesc td;
 };
 
 // A segment cut by piece boundaries: its rows and the pieces holding its
-// partial results (v0 wrote its tail slot, v0+1 .. v1 their head slots).
+// partial results (v0 wrote its tail slot, v0+1 .. v1 their head slots);
+// piece numbers are local to the segment's stream.
 struct SplitSeg {
-    int32_t row0;  // first query token row of the tile
-    int32_t ntok;  // query tokens in the tile
+    int32_t row0;    // first query token row of the tile
+    int32_t ntok;    // query tokens in the tile
     int32_t kvh;
     int32_t v0;
     int32_t v1;
-    int32_t pad[3];
+    int32_t stream;  // STREAM_WIDE or STREAM_NARROW
+    int32_t pad[2];
 };
 
-// Header words at the start of the workspace.
+// Two block streams: tiles of multi-token spans (wide: up to 64 rows, four
+// MFMA row tiles share each K/V block) and single-token tiles (narrow: up to
+// 16 rows). Each is cut into its own pieces and run by its own launch.
+enum { STREAM_WIDE = 0, STREAM_NARROW = 1, NUM_STREAMS = 2 };
+// 16-row MFMA tiles in a wide tile (fp32 operands take twice the registers)
+constexpr int wide_tiles(int dtype) { return dtype == PA_F32 ? 2 : 4; }
+
+// Header words at the start of the workspace: per stream s, its total
+// blocks, piece size and piece count at HDR_STREAM + 4 s.
 enum {
     HDR_NTILES = 0,
-    HDR_TOTAL = 1,
-    HDR_R = 2,
-    HDR_NPIECES = 3,
-    HDR_NSPLIT = 4,
+    HDR_NSPLIT = 1,
+    HDR_STREAM = 4,
+    HDR_TOTAL = 0,
+    HDR_R = 1,
+    HDR_NPIECES = 2,
     HDR_WORDS = 64
 };
 
@@ -62,16 +79,17 @@ struct PlanArgs {
     int32_t num_seqs;
     int32_t num_tokens;
     int32_t max_context_len;  // contexts are clamped to this
-    int32_t tile_tokens;
+    int32_t narrow_tokens;    // query tokens per narrow tile (16 / G, 1 for decode)
+    int32_t wide_tokens;      // query tokens per wide tile (64 / G)
     int32_t num_kv_heads;
-    int32_t part_blocks;  // blocks per piece; 0 = balance over `waves`
-    int32_t waves;        // resident waves of the attention grid
-    int32_t min_blocks;   // smallest piece when balancing
+    int32_t part_blocks;  // blocks per piece; 0 = balance over the stream's waves
+    int32_t waves[NUM_STREAMS];  // resident waves of each stream's kernel
+    int32_t min_blocks;          // smallest piece when balancing
     int32_t max_tiles;
-    int64_t max_pieces;
+    int64_t max_pieces[NUM_STREAMS];
     TileDesc* tiles;
-    PieceStart* pieces;
-    SplitSeg* splits;  // [max_pieces] segments the merge pass completes
+    PieceStart* pieces[NUM_STREAMS];
+    SplitSeg* splits;  // [max_pieces of both streams] segments the merge completes
     int32_t* hdr;
 };
 
@@ -87,10 +105,11 @@ struct AttnArgs {
     const int32_t* context_lens;
     const int32_t* qsl;
     const TileDesc* tiles;
-    const PieceStart* pieces;
+    const PieceStart* pieces;  // this stream's pieces
     const int32_t* hdr;
-    float* part_lse;  // [pieces][2][16], log2 units
-    float* part_o;    // [pieces][2][D/16][64 lanes] float4, normalized
+    int32_t stream;
+    float* part_lse;  // [pieces][2][NT * 16], log2 units
+    float* part_o;    // [pieces][2][NT][D/16][64 lanes] float4, normalized
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t group;
@@ -105,8 +124,8 @@ struct MergeArgs {
     float* lse;
     const SplitSeg* splits;
     const int32_t* hdr;
-    const float* part_lse;
-    const float* part_o;
+    const float* part_lse[NUM_STREAMS];
+    const float* part_o[NUM_STREAMS];
     int32_t num_q_heads;
     int32_t group;
 };
@@ -128,10 +147,10 @@ struct AppendArgs {
 // Launchers (host side), defined next to their kernels.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64_t max_pieces,
-                            hipStream_t s);
-// Waves of the attention kernel that fit on the device at once (> 0), or 0
-// if the device cannot be queried.
-int resident_waves(int kv_dtype, int head_dim);
+                            hipStream_t s);  // a.stream selects the wide or narrow kernel
+// Waves of the attention kernel of a stream that fit on the device at once
+// (> 0), or 0 if the device cannot be queried.
+int resident_waves(int kv_dtype, int head_dim, int stream);
 hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t max_splits,
                         hipStream_t s);
 hipError_t launch_append(int new_dtype, int kv_dtype, const AppendArgs& a, hipStream_t s);

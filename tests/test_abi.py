@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     names = _declared_functions()
     for want in ("pa_workspace_bytes", "pa_paged_attn_decode", "pa_paged_attn_hybrid",
                  "pa_kv_append", "pa_status_string", "pa_version", "pa_fp8_e4m3fn_to_f32",
-                 "pa_probe_stream_read", "pa_probe_copy", "pa_plan", "pa_paged_attn_run"):
+                 "pa_probe_stream_read", "pa_probe_copy", "pa_plan", "pa_paged_attn_run",
+                 "pa_paged_attn_partial", "pa_paged_attn_merge"):
         assert want in names
 
 

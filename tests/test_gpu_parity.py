@@ -332,3 +332,24 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
         _ = (t2["q"].float() * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_partial_then_merge_equals_run():
+    wl = W.make_config("c3", small=True)
+    vals, pre = prepare(wl)
+    t = dev_tensors(wl, vals, pre)
+    pa.kv_append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["slots"])
+    shape = pa.make_shape(t["q"], t["k_cache"], t["bt"], 64)
+    ws = torch.zeros(pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len, 1),
+                     dtype=torch.uint8, device="cuda")
+    pa.plan(shape, t["cl"], ws, num_q_tokens=wl.num_tokens, max_query_len=1,
+            max_context_len=wl.max_context_len)
+    kw = dict(max_query_len=1, max_context_len=wl.max_context_len)
+    ref = pa.run(shape, t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], wl.scale, ws, **kw)
+    out = torch.full_like(t["q"], float("nan"))
+    pa.run(shape, t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], wl.scale, ws, out=out,
+           passes="partial", **kw)
+    pa.run(shape, t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], wl.scale, ws, out=out,
+           passes="merge", **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
