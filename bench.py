@@ -96,6 +96,65 @@ def cpu_baseline(wl, budget_s: float = 10.0):
     }
 
 
+PROFILE_FILES = {
+    "c1": "kernels_tiny_paged_decode_fp32.md",
+    "c2": "kernels_llama3_8b_decode_bf16.md",
+    "c3": "kernels_long_context_split_kv_bf16.md",
+    "c4": "kernels_hybrid_chunked_prefill_bf16.md",
+    "c5": "kernels_70b_decode_fp8_kv.md",
+}
+
+
+def attention_source_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_213_amd",
+                        "csrc")
+    for f in ("pa_attention.hip", "pa_internal.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(config: str):
+    """HBM bytes per attention launch recorded by the profiler counters for
+    this workload (profiles/), or None when none are recorded or the
+    attention source has changed since they were taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        PROFILE_FILES.get(config, ""))
+    if not os.path.isfile(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            k, sep, v = line.partition(":")
+            if sep and k in ("traffic_bytes_per_launch", "attention_source_sha256"):
+                fields[k] = v.strip()
+    if fields.get("attention_source_sha256") != attention_source_sha256():
+        return None
+    t = fields.get("traffic_bytes_per_launch")
+    return int(t) if t and t.isdigit() else None
+
+
+def stream_read_probe(pa, torch, dev, mib: int = 4096, reps: int = 10) -> float:
+    """GB/s of the library's streaming-read probe over a buffer 16x the
+    Infinity Cache: what a plain read of HBM reaches on this device."""
+    buf = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(8 * 1024, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        pa.probe_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        pa.probe_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / reps
+    del buf, sink
+    return round((mib << 20) / sec / 1e9, 1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +302,34 @@ def main():
             s.synchronize()
             att_ms.append(e0.elapsed_time(e1) / layers)
     att_ms = np.array(att_ms)
+
+    def back_to_back_us(enqueue_layer, reps=5):
+        """Mean duration of one launch, timed over every layer's launch back
+        to back (same method as the attention pass above)."""
+        per = []
+        with torch.cuda.stream(s):
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(2_000_000)
+                e0.record(s)
+                for L_ in range(layers):
+                    enqueue_layer(L_)
+                e1.record(s)
+                s.synchronize()
+                per.append(e0.elapsed_time(e1) * 1e3 / layers)
+        return round(float(np.mean(per)), 2)
+
+    append_us = back_to_back_us(lambda L_: pa.kv_append(
+        kc[L_], vc[L_], vals.k_new, vals.v_new, slots, k_scale=k_scale, v_scale=v_scale,
+        stream=s))
+    merge_us = back_to_back_us(lambda L_: pa.run(
+        shape, qs[L_], kc[L_], vc[L_], bt, cl, wl.scale, ws, query_start_loc=qsl,
+        max_query_len=mq, max_context_len=wl.max_context_len, out=outs[L_], lse=lse, stream=s,
+        passes="merge"))
+    plan_us = back_to_back_us(lambda L_: pa.plan(
+        shape, cl, ws, query_start_loc=qsl, num_q_tokens=wl.num_tokens, max_query_len=mq,
+        max_context_len=wl.max_context_len, stream=s))
+    probe_gbs = stream_read_probe(pa, torch, dev)
     ms_per_step = wall * 1e3 / args.steps
     kv_bytes = wl.kv_bytes_logical()
     value = layers * kv_bytes / (ms_per_step / 1e3) / 1e9
@@ -287,13 +374,20 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(wl.name),
+            "traffic_note": "HBM bytes per attention pass launch (calibrated FETCH_SIZE + "
+                            "WRITE_SIZE, profiles/); null if not recorded for the current "
+                            "attention source",
             "kernel": "attention_kernel (pass 1, one launch per layer); HIP events around "
                       "the back-to-back pass-1 launches of all layers, divided by the layers",
             "launch_us_mean": round(att_mean * 1e3, 2),
             "launch_us_min_max": [round(float(att_ms.min()) * 1e3, 2),
                                   round(float(att_ms.max()) * 1e3, 2)],
+            "stream_read_probe_gbs": probe_gbs,
+            "frac_of_stream_read_probe": round(achieved / probe_gbs, 4),
         },
+        "launch_us": {"plan_per_step": plan_us, "kv_append": append_us,
+                      "attention": round(att_mean * 1e3, 2), "merge": merge_us},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)

@@ -78,8 +78,12 @@ typedef enum pa_status {
  * G = Hq / Hkv <= 16; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
  * (BF16, FP8_E4M3FN)}; partition_size 0 (split each call's key blocks into
  * equal pieces, one per resident wave, at least 128 tokens each) or a
- * positive multiple of 16 (pieces of that many tokens). At most 8192 tiles
- * per call (a tile is up to 16 query rows: G heads of 16 / G tokens). */
+ * positive multiple of 16 (pieces of that many tokens). Query rows are
+ * grouped into tiles: a span of at most 16 / G tokens (every decode) is one
+ * narrow tile of G * n_i rows; a longer span is cut into wide tiles of
+ * 64 / G tokens (32 / G for F32). A call may hold at most 8192 tiles,
+ * counted as 2 * num_seqs + ceil(num_q_tokens / (64 / G)) for a hybrid call
+ * and num_seqs for a decode call; beyond that it returns PA_ENOTSUP. */
 typedef struct pa_shape {
     int32_t num_q_heads;        /* Hq */
     int32_t num_kv_heads;       /* Hkv */
@@ -140,8 +144,9 @@ int pa_plan(const pa_shape* shape, const int32_t* context_lens, const int32_t* q
             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Attention with a plan made by pa_plan (same arguments as the plan, plus
- * the tensors): one kernel launch. Pieces that cut a segment write partial
- * results to the workspace and the last of them merges by log-sum-exp. */
+ * the tensors). Enqueues the attention pass (one launch per tile class
+ * present) and then the merge pass: pieces that cut a segment write partial
+ * results to the workspace, and the merge combines them by log-sum-exp. */
 int pa_paged_attn_run(const pa_shape* shape, void* out, float* lse, const void* q,
                       const void* k_cache, const void* v_cache, const float* k_scale,
                       const float* v_scale, const int32_t* block_tables,

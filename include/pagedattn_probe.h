@@ -19,7 +19,8 @@ extern "C" {
 #endif
 
 /* Read `bytes` (a multiple of 16, 16-byte aligned) of `buf` once with
- * coalesced 16-byte loads; `sink` receives at most a few words so the loads
+ * coalesced nontemporal 16-byte loads (the load kind the attention kernels
+ * use for K/V); `sink` receives at most a few words so the loads
  * cannot be optimized away (it needs room for 8 words per compute unit). */
 int pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 

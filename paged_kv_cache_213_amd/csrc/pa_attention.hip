@@ -2,21 +2,28 @@
 //
 // Three kernels run in order on the caller's stream:
 //
-//   plan       one workgroup turns (query spans, context lengths) into a list
-//              of work items -- (sequence, query tile, key partition) -- in
-//              device memory, so the host never reads lengths back. This is
-//              the per-step "plan" of the request trace on "03 -- Engines
-//              Papers" (whiteboard test), done on the device.
-//   attention  a persistent grid; each workgroup takes (item, KV head) units
-//              from an atomic counter. Its four waves split the partition's
-//              16-token blocks, gather them through the block table
-//              ("03 -- Engines Papers", section 2), and keep an online
-//              softmax (running max and sum, Milakov & Gimelshein on the
-//              "References" page) in registers; the waves' states are then
-//              combined through LDS. A unit covering a whole context writes
-//              the output; otherwise it writes a partial (lse, o) per row.
-//   merge      combines the partials of split rows by log-sum-exp (split-K
-//              decode, playbook Theme 4; LSE merge, first page section 12).
+//   plan       one workgroup turns (query spans, context lengths) into the
+//              work of the call, in device memory, so the host never reads
+//              lengths back. This is the per-step "plan" of the request
+//              trace on "03 -- Engines Papers" (whiteboard test), done on
+//              the device. Query rows are grouped into tiles: a narrow tile
+//              holds up to 16 rows (G query heads x 16/G tokens of one
+//              span); a wide tile holds 4 x 16 rows (2 x 16 for fp32) of a
+//              chunked-prefill span. Every (tile, KV head) pair is a segment
+//              of 16-token key blocks; the segments of each tile class form
+//              one stream of blocks, cut into pieces of equal size (one per
+//              resident wave, or partition_size tokens each).
+//   attention  a persistent grid of one-wave workgroups per tile class; wave
+//              v walks pieces v, v + grid, ... Inside a piece it gathers the
+//              blocks through the block table ("03 -- Engines Papers",
+//              section 2), one block ahead in a register ring, and keeps an
+//              online softmax (running max and sum, Milakov & Gimelshein on
+//              the "References" page) in registers. A segment the piece saw
+//              whole writes its output rows; a segment cut by a piece
+//              boundary writes a partial (lse, normalized o) per row.
+//   merge      one wave per cut segment combines its partials by
+//              log-sum-exp (split-K decode, playbook Theme 4; LSE merge,
+//              first page section 12).
 //
 // Matrix cores: with K stored [block][head][16 tokens][D] and V stored
 // [block][head][D][16 tokens], both contractions read K-contiguous operands

@@ -9,20 +9,28 @@
 
 namespace {
 
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ src,
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// Nontemporal 16-byte load: the same load kind the attention kernels use for
+// the K/V bytes they read once.
+__device__ __forceinline__ u32x4_t ld_stream(const u32x4_t* p) {
+    return __builtin_nontemporal_load(p);
+}
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src,
                                                           int64_t n16, uint32_t* sink) {
     uint32_t acc = 0;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     // four independent 16-byte loads in flight per thread per iteration
     for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride],
-                    d = src[i + 3 * stride];
+        const u32x4_t a = ld_stream(src + i), b = ld_stream(src + i + stride),
+                      c = ld_stream(src + i + 2 * stride), d = ld_stream(src + i + 3 * stride);
         acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^
                d.y ^ d.z ^ d.w;
     }
     for (; i < n16; i += stride) {
-        const uint4 a = src[i];
+        const u32x4_t a = ld_stream(src + i);
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
     if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;  // keeps the loads live
@@ -50,7 +58,7 @@ extern "C" int pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* sin
     if (!buf || !sink || (bytes & 15) || ((uintptr_t)buf & 15)) return PA_EINVAL;
     const int64_t n16 = (int64_t)(bytes / 16);
     hipLaunchKernelGGL(stream_read_kernel, dim3(grid_for(n16)), dim3(256), 0,
-                       (hipStream_t)stream, (const uint4*)buf, n16, sink);
+                       (hipStream_t)stream, (const u32x4_t*)buf, n16, sink);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_EHIP;
 }
 

@@ -48,18 +48,22 @@ def test_c1_full_parity():
     assert e["max_tol_err"] <= 1e-5
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
-def test_full_config_sampled_parity(name):
-    """Full-size batches in the launch configuration the bench times;
-    the oracle checks a sample of sequences (the longest, the shortest and
-    spread ones, plus the prefill span in the hybrid batch)."""
+@pytest.mark.parametrize("name,P", [("c2", None), ("c3", None), ("c3", 0), ("c4", None),
+                                    ("c4", 0), ("c5", None)])
+def test_full_config_sampled_parity(name, P):
+    """Full-size batches, with the configuration's own partition size and
+    with the balanced split (partition_size 0, the launch configuration the
+    bench times); the oracle checks a sample of sequences (the longest, the
+    shortest and spread ones, plus the prefill span in the hybrid batch)."""
     wl = W.make_config(name)
+    if P is not None:
+        wl.partition_size = P
     L = wl.context_lens
     order = np.argsort(L)
     pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2]), 0, wl.num_seqs - 1}
     pick |= set(int(i) for i in np.linspace(0, wl.num_seqs - 1, 6).astype(int))
     e, _, _ = _check_step(wl, seq_subset=np.array(sorted(pick), np.int32))
-    print(f"{name} full sampled: {e}", flush=True)
+    print(f"{name} full sampled, partition_size {wl.partition_size}: {e}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c5"])
