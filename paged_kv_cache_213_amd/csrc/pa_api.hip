@@ -14,6 +14,7 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int cdiv(int a, int b) { return (a + b - 1) / b; }
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -74,9 +75,13 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
         const int w = pa::resident_waves(s->kv_dtype, s->head_dim, st);
         l.waves[st] = w > 0 ? w : kWaveBound;
-        const int64_t max_total = tiles_of[st] * s->num_kv_heads * blocks_per_tile;
-        int64_t mp = l.part_blocks > 0 ? (max_total + l.part_blocks - 1) / l.part_blocks
-                                       : (int64_t)l.waves[st];
+        // pieces per KV head substream: ceil(B / R) with B <= tiles * blocks
+        // per tile, and R = P / 16, or R >= Hkv * B / waves when balanced
+        const int64_t H = s->num_kv_heads;
+        const int64_t per_head = l.part_blocks > 0
+                                     ? cdiv(tiles_of[st] * blocks_per_tile, (int64_t)l.part_blocks)
+                                     : cdiv((int64_t)l.waves[st], H);
+        int64_t mp = H * per_head;
         if (tiles_of[st] == 0) mp = 0;
         l.max_pieces[st] = mp;
         splits += mp;
@@ -224,6 +229,7 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
             ma.part_o[st] = (const float*)(ws + l.off_o[st]);
         }
         ma.num_q_heads = s->num_q_heads;
+        ma.num_kv_heads = s->num_kv_heads;
         ma.group = s->num_q_heads / s->num_kv_heads;
         const int64_t records = l.max_pieces[0] + l.max_pieces[1];
         if (records > 1 && pa::launch_merge(s->q_dtype, s->head_dim, ma, records, hs) != hipSuccess)

@@ -56,23 +56,39 @@ enum KvKind { KV_F32 = PA_F32, KV_BF16 = PA_BF16, KV_FP8 = PA_FP8_E4M3FN };
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_max_xor_16_32(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16));
-    v = fmaxf(v, __shfl_xor(v, 32));
-    return v;
+// Reductions over the four lanes n, n + 16, n + 32, n + 48 that hold one
+// query row, with the gfx950 row swaps: permlane16_swap exchanges 16-lane
+// rows 1 <-> 0 and 3 <-> 2 between its two operands, permlane32_swap rows
+// 2, 3 <-> 0, 1; given the same value twice, the two results hold a lane's
+// own value and its partner's, in some order, so any symmetric op of them
+// reduces over the pair.
+__device__ __forceinline__ float pair16_max(float v) {
+    const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(w[0]), __uint_as_float(w[1]));
+}
+__device__ __forceinline__ float pair32_max(float v) {
+    const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(w[0]), __uint_as_float(w[1]));
+}
+__device__ __forceinline__ float row_max(float v) { return pair32_max(pair16_max(v)); }
+__device__ __forceinline__ float row_sum(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ float wave_sum_xor_16_32(float v) {
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    return v;
-}
-
-// Round-to-nearest-even float -> bf16 bits.
-__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;  // NaN stays NaN
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two floats -> two bf16 (round to nearest even) packed low, high: one
+// v_cvt_pk_bf16_f32.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // Two e4m3fn bytes (b0 low) -> two bf16 packed in a dword. Every e4m3 value
@@ -84,39 +100,46 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
     return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xffff0000u);
 }
 
-// K/V bytes are read once per call: stream them with nontemporal loads so
-// they do not evict the block tables, queries and partials from the caches.
+// K/V loads. A block that one wave reads once per call (a decode's context)
+// is streamed with nontemporal loads, so it does not evict the block tables,
+// queries and partials from the caches; blocks that several query tiles read
+// (a chunked-prefill span's context) use ordinary loads, so the tiles after
+// the first find them in L2.
 #ifndef PA_NT_LOADS
 #define PA_NT_LOADS 1
 #endif
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
+template <bool nt>
 __device__ __forceinline__ uint4 ld_kv(const uint4* p) {
-#if PA_NT_LOADS
-    const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
-    return make_uint4(v.x, v.y, v.z, v.w);
-#else
-    return *p;
-#endif
+    if constexpr (nt) {
+        const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *p;
+    }
 }
+template <bool nt>
 __device__ __forceinline__ uint2 ld_kv(const uint2* p) {
-#if PA_NT_LOADS
-    const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)p);
-    return make_uint2(v.x, v.y);
-#else
-    return *p;
-#endif
+    if constexpr (nt) {
+        const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)p);
+        return make_uint2(v.x, v.y);
+    } else {
+        return *p;
+    }
 }
+template <bool nt>
 __device__ __forceinline__ uint32_t ld_kv(const uint32_t* p) {
-#if PA_NT_LOADS
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
+    if constexpr (nt) {
+        return __builtin_nontemporal_load(p);
+    } else {
+        return *p;
+    }
 }
+template <bool nt>
 __device__ __forceinline__ float4 ld_kv(const float4* p) {
-    const uint4 v = ld_kv((const uint4*)p);
+    const uint4 v = ld_kv<nt>((const uint4*)p);
     return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
                        __uint_as_float(v.w));
 }
@@ -133,17 +156,18 @@ struct Tile<KV_F32, D> {
     float4 v[D / 16];  // V^T[16dt + d][4g .. 4g+3]
     using QReg = float[D / 4];
 
+    template <bool nt>
     __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t blk_head,
                                          int lane) {
         const int t = lane & 15, g = lane >> 4;
         // load j reads 64 contiguous bytes of row t across the 4 lane groups
         const float* kp = (const float*)kc + blk_head * 16 * D + t * D + 4 * g;
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j) k[j] = ld_kv((const float4*)(kp + 16 * j));
+        for (int j = 0; j < D / 16; ++j) k[j] = ld_kv<nt>((const float4*)(kp + 16 * j));
         const float* vb = (const float*)vc + blk_head * 16 * D;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-            v[dt] = ld_kv((const float4*)(vb + (16 * dt + t) * 16 + 4 * g));
+            v[dt] = ld_kv<nt>((const float4*)(vb + (16 * dt + t) * 16 + 4 * g));
     }
     __device__ __forceinline__ f32x4 qk(const float* q) const {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -183,17 +207,18 @@ struct Tile<KV_BF16, D> {
     uint4 k[D / 32];  // 8 bf16 each: K[t][32j + 8g .. +8]
     uint2 v[D / 16];  // 4 bf16 each: V^T[16dt + d][4g .. 4g+3]
 
+    template <bool nt>
     __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t blk_head,
                                          int lane) {
         const int t = lane & 15, g = lane >> 4;
         // load j reads 64 contiguous bytes of row t across the 4 lane groups
         const uint16_t* kp = (const uint16_t*)kc + blk_head * 16 * D + t * D + 8 * g;
 #pragma unroll
-        for (int j = 0; j < D / 32; ++j) k[j] = ld_kv((const uint4*)(kp + 32 * j));
+        for (int j = 0; j < D / 32; ++j) k[j] = ld_kv<nt>((const uint4*)(kp + 32 * j));
         const uint16_t* vb = (const uint16_t*)vc + blk_head * 16 * D;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-            v[dt] = ld_kv((const uint2*)(vb + (16 * dt + t) * 16 + 4 * g));
+            v[dt] = ld_kv<nt>((const uint2*)(vb + (16 * dt + t) * 16 + 4 * g));
     }
     __device__ __forceinline__ f32x4 qk(const uint4* q) const {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -226,17 +251,18 @@ struct Tile<KV_FP8, D> {
     uint4 k[D / 64];     // 16 e4m3 bytes each: K[t][64j + 16g .. +16]
     uint32_t v[D / 16];  // 4 e4m3 bytes each: V^T[16dt + d][4g .. 4g+3]
 
+    template <bool nt>
     __device__ __forceinline__ void load(const void* kc, const void* vc, int64_t blk_head,
                                          int lane) {
         const int t = lane & 15, g = lane >> 4;
         // load j reads 64 contiguous bytes of row t across the 4 lane groups
         const uint8_t* kp = (const uint8_t*)kc + blk_head * 16 * D + t * D + 16 * g;
 #pragma unroll
-        for (int j = 0; j < D / 64; ++j) k[j] = ld_kv((const uint4*)(kp + 64 * j));
+        for (int j = 0; j < D / 64; ++j) k[j] = ld_kv<nt>((const uint4*)(kp + 64 * j));
         const uint8_t* vb = (const uint8_t*)vc + blk_head * 16 * D;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
-            v[dt] = ld_kv((const uint32_t*)(vb + (16 * dt + t) * 16 + 4 * g));
+            v[dt] = ld_kv<nt>((const uint32_t*)(vb + (16 * dt + t) * 16 + 4 * g));
     }
     __device__ __forceinline__ f32x4 qk(const uint4* q) const {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -277,14 +303,22 @@ struct Tile<KV_FP8, D> {
 
 // ---- plan ------------------------------------------------------------------
 //
-// The batch's work is one stream of 16-token key blocks: segment (tile t, KV
-// head h) contributes the nb[t] blocks its rows read, segments ordered
-// t-major, h-minor. The stream is cut into pieces of R consecutive blocks;
-// each wave of the attention grid streams whole pieces. With R chosen as
-// total / resident waves, every wave gets the same number of blocks, so all
-// finish together whatever the spread of context lengths (the split-KV
-// decode of the playbook's Theme 4, balanced by block count). A segment cut
-// by a piece boundary leaves partial results that the merge pass combines.
+// The work of each tile class is a stream of 16-token key blocks: segment
+// (tile t, KV head h) contributes the nb[t] blocks its rows read. The stream
+// is laid out KV-head-major: one substream per KV head, holding that head's
+// segments in tile order. Each substream is cut into pieces of R
+// consecutive blocks, and piece k of head h gets number k * Hkv + h, so the
+// pieces of one head interleave with period Hkv. Each wave of the attention
+// grid streams whole pieces: wave w takes pieces w, w + grid, ... With a
+// grid that is a multiple of Hkv, every piece a wave takes belongs to head
+// w mod Hkv; since workgroups are dealt to the XCDs in turn, the waves of
+// one XCD then serve one KV head (or a few), and tiles that read the same
+// blocks (the query tiles of a chunked-prefill span) find them in that
+// XCD's L2. With R chosen as Hkv * substream / resident waves, every wave
+// gets the same number of blocks, so all finish together whatever the
+// spread of context lengths (the split-KV decode of the playbook's Theme 4,
+// balanced by block count). A segment cut by a piece boundary leaves
+// partial results that the merge pass combines.
 
 constexpr int kPlanThreads = 1024;
 
@@ -374,64 +408,67 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
     __syncthreads();
 
-    // 3. per stream: piece size, piece starts
-    int64_t Rs[NUM_STREAMS];
+    // 3. per stream: piece size, piece starts (all KV heads' substreams
+    //    hold the same blocks, B = the stream's tiles' nb summed)
+    int Rs[NUM_STREAMS];
     for (int st = 0; st < NUM_STREAMS; ++st) {
         const int t_lo = st == STREAM_WIDE ? 0 : nwide;
         const int t_hi = st == STREAM_WIDE ? nwide : ntiles;
-        const int64_t total = (int64_t)H * (s_tp[t_hi] - s_tp[t_lo]);
+        const int64_t B = s_tp[t_hi] - s_tp[t_lo];
         int64_t R = a.part_blocks;
         if (R <= 0) {
-            R = (total + a.waves[st] - 1) / max(a.waves[st], 1);
+            R = ((int64_t)H * B + a.waves[st] - 1) / max(a.waves[st], 1);
             R = max(R, (int64_t)a.min_blocks);
         }
-        int64_t V = (total + R - 1) / R;
-        if (a.max_pieces[st] == 0) {  // no room: the caller understated max_query_len
-            V = 0;
-        } else if (V > a.max_pieces[st]) {  // never for sizes the host planned for
-            R = (total + a.max_pieces[st] - 1) / a.max_pieces[st];
-            V = (total + R - 1) / R;
+        int64_t K = (B + R - 1) / R;  // pieces per substream
+        const int64_t kmax = a.max_pieces[st] / H;
+        if (kmax == 0) {  // no room: the caller understated max_query_len
+            K = 0;
+        } else if (K > kmax) {  // never for sizes the host planned for
+            R = (B + kmax - 1) / kmax;
+            K = (B + R - 1) / R;
         }
-        Rs[st] = R;
+        R = max(R, (int64_t)1);
+        Rs[st] = (int)R;
+        const int64_t V = K * H;
         for (int64_t v = threadIdx.x; v < V; v += kPlanThreads) {
-            const int64_t b = (int64_t)H * s_tp[t_lo] + v * R;  // global block index
-            const int key = (int)(b / H);  // s_tp[t] <= key  <=>  H * s_tp[t] <= b
+            const int h = (int)(v % H);
+            const int key = s_tp[t_lo] + (int)((v / H) * R);  // block offset in the tile prefix
             int lo = t_lo, hi = t_hi - 1;  // last tile whose prefix is <= key
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
                 if (s_tp[mid] <= key) lo = mid; else hi = mid - 1;
             }
-            const int nb = s_tp[lo + 1] - s_tp[lo];
-            const int64_t r = b - (int64_t)H * s_tp[lo];
             PieceStart ps{};
             ps.tile = lo;
-            ps.kvh = (int)(r / nb);
-            ps.j = (int)(r % nb);
+            ps.kvh = h;
+            ps.j = key - s_tp[lo];
             ps.td = a.tiles[lo];
             a.pieces[st][v] = ps;
         }
         if (threadIdx.x == 0) {
-            a.hdr[HDR_STREAM + 4 * st + HDR_TOTAL] = (int)total;
+            a.hdr[HDR_STREAM + 4 * st + HDR_TOTAL] = (int)B;
             a.hdr[HDR_STREAM + 4 * st + HDR_R] = (int)R;
             a.hdr[HDR_STREAM + 4 * st + HDR_NPIECES] = (int)V;
         }
     }
 
     // 4. segments cut by a piece boundary, for the merge pass (a segment is
-    //    cut iff its first and last blocks fall in different pieces)
+    //    cut iff its first and last blocks fall in different pieces of its
+    //    KV head's substream)
     const int64_t max_splits = a.max_pieces[0] + a.max_pieces[1];
     for (int sg = threadIdx.x; sg < ntiles * H; sg += kPlanThreads) {
         const int t = sg / H, h = sg % H;
         const int st = t < nwide ? STREAM_WIDE : STREAM_NARROW;
         const int t_lo = st == STREAM_WIDE ? 0 : nwide;
         const int nb = s_tp[t + 1] - s_tp[t];
-        const int64_t b0 = (int64_t)H * (s_tp[t] - s_tp[t_lo]) + (int64_t)h * nb;
-        const int64_t v0 = b0 / Rs[st], v1 = (b0 + nb - 1) / Rs[st];
-        if (v0 != v1) {
+        const int b0 = s_tp[t] - s_tp[t_lo];
+        const int k0 = b0 / Rs[st], k1 = (b0 + nb - 1) / Rs[st];
+        if (k0 != k1) {
             const int k = atomicAdd(&s_nsplit, 1);  // list order is irrelevant
             const TileDesc td = a.tiles[t];
             if (k < max_splits)
-                a.splits[k] = SplitSeg{td.qs + td.qtok0, td.ntok, h, (int)v0, (int)v1, st, {0, 0}};
+                a.splits[k] = SplitSeg{td.qs + td.qtok0, td.ntok, h, k0, k1, st, {0, 0}};
         }
     }
     __syncthreads();
@@ -462,6 +499,8 @@ template <int kv, int D, int NT>
 __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td, const int kvh,
                                             const int j, const int take, const int piece) {
     using T = Tile<kv, D>;
+    // single-token tiles read each block once; wide tiles share it through L2
+    constexpr bool kStreamLoads = NT == 1 && PA_NT_LOADS;
     using QReg = typename std::conditional<kv == KV_F32, float[D / 4], uint4[D / 32]>::type;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;  // query row owned in MFMA layouts (within a row tile)
@@ -509,15 +548,26 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         }
     }
 
+    // Online softmax with a lazily moved reference (log2 units): scores are
+    // taken relative to m_use, the row maximum when the reference was last
+    // moved, and p = 2^(s - m_use). The reference moves (rescaling o and l)
+    // only when some score exceeds it by more than kLazy, so p <= 2^kLazy and
+    // most blocks need neither a row reduction nor a rescale. thr is kLazy
+    // once a row has a reference and -inf before its first visible key.
+    constexpr float kLazy = 8.f;
     f32x4 o[NT][D / 16];
-    float m_run[NT], l_run[NT];
+    float m_use[NT], thr[NT], l_run[NT];
 #pragma unroll
     for (int r = 0; r < NT; ++r) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m_run[r] = -INFINITY;
+        m_use[r] = 0.f;
+        thr[r] = -INFINITY;
         l_run[r] = 0.f;
     }
+    // blocks ending at or before the tile's first query position are visible
+    // to every row and lie inside the context: no masks
+    const int pos_first = L - nspan + td.qtok0;
 
     const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
     for (int c0 = 0; c0 < take; c0 += 64) {
@@ -538,6 +588,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         auto consume = [&](T& cur, int i) {
             const int jb = j + c0 + i;       // logical block
             const int t0 = jb * 16 + 4 * g;  // my first token in it
+            const bool full = jb * 16 + 15 <= pos_first;  // wave-uniform
             float c = a.scale_log2;
             float vsc = 1.f;
             if constexpr (kv == KV_FP8) {
@@ -549,38 +600,50 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             typename std::conditional<kv == KV_F32, float[NT][4], s16x4[NT]>::type pk;
 #pragma unroll
             for (int r = 0; r < NT; ++r) {
-                f32x4 sc = cur.qk(qreg[r]);
-                float sv[4];
+                const f32x4 sc = cur.qk(qreg[r]);
+                float x[4];  // scores relative to the reference
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sv[e] = (t0 + e <= pos[r]) ? sc[e] * c : -INFINITY;
-                float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-                mx = wave_max_xor_16_32(mx);
-                const float m_new = fmaxf(m_run[r], mx);
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                const float alpha = fexp2(m_run[r] - m_use);
+                for (int e = 0; e < 4; ++e) x[e] = fmaf(sc[e], c, -m_use[r]);
+                if (!full) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] = (t0 + e <= pos[r]) ? x[e] : -INFINITY;
+                }
+                const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+                if (__builtin_amdgcn_ballot_w64(mx > thr[r]) != 0) {
+                    // move the reference of the tile's rows up to their maxima
+                    const float rm = row_max(mx);
+                    const bool had = thr[r] != -INFINITY;
+                    const float delta = had ? fmaxf(rm, 0.f) : (rm == -INFINITY ? 0.f : rm);
+                    const float alpha = had ? fexp2(-delta) : 1.f;  // o, l are 0 before
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) x[e] -= delta;
+                    m_use[r] += delta;
+                    if (rm != -INFINITY) thr[r] = kLazy;
+                    l_run[r] *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < D / 16; ++dt) o[r][dt] *= alpha;
+                }
                 float p[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = fexp2(sv[e] - m_use);
-                l_run[r] = l_run[r] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-                m_run[r] = m_new;
-#pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt) o[r][dt] *= alpha;
+                for (int e = 0; e < 4; ++e) p[e] = fexp2(x[e]);
+                l_run[r] += (p[0] + p[1]) + (p[2] + p[3]);
                 if constexpr (kv == KV_F32) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) pk[r][e] = p[e];
                 } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pk[r][e] = (short)bf16_bits_rne(p[e] * vsc);
+                    const uint32_t lo = pack_bf16x2(p[0] * vsc, p[1] * vsc);
+                    const uint32_t hi = pack_bf16x2(p[2] * vsc, p[3] * vsc);
+                    pk[r] = __builtin_bit_cast(s16x4, make_uint2(lo, hi));
                 }
             }
             // zero V slots past the context (NaN there must not reach P.V)
-            cur.mask_v(L - t0);
+            if (!full) cur.mask_v(L - t0);
 #pragma unroll
             for (int r = 0; r < NT; ++r) cur.pv(pk[r], o[r]);
         };
         auto fetch = [&](T& dst, int i) {
             const int ph = __builtin_amdgcn_readlane(my_phys, i);
-            dst.load(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
+            dst.template load<kStreamLoads>(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
         };
         // ring of PF + 1 register tiles: PF blocks stay in flight while one is
         // consumed. In the steady-state loop every refill is in range, so it
@@ -617,7 +680,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 #pragma unroll
     for (int r = 0; r < NT; ++r) {
         // row totals: l summed over the four lane groups that share a row
-        const float l = wave_sum_xor_16_32(l_run[r]);
+        const float l = row_sum(l_run[r]);
         const float inv = l > 0.f ? 1.0f / l : 0.f;
         if (!row_ok[r]) continue;
         if (whole) {
@@ -630,15 +693,13 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                                     o[r][dt][3] * inv);
                 } else {
                     uint2 w;
-                    w.x = bf16_bits_rne(o[r][dt][0] * inv) |
-                          (bf16_bits_rne(o[r][dt][1] * inv) << 16);
-                    w.y = bf16_bits_rne(o[r][dt][2] * inv) |
-                          (bf16_bits_rne(o[r][dt][3] * inv) << 16);
+                    w.x = pack_bf16x2(o[r][dt][0] * inv, o[r][dt][1] * inv);
+                    w.y = pack_bf16x2(o[r][dt][2] * inv, o[r][dt][3] * inv);
                     *(uint2*)((uint16_t*)a.out + rowid[r] * D + d) = w;
                 }
             }
             if (a.lse && g == 0)
-                a.lse[rowid[r]] = l > 0.f ? (m_run[r] + __log2f(l)) * kLn2 : -INFINITY;
+                a.lse[rowid[r]] = l > 0.f ? (m_use[r] + __log2f(l)) * kLn2 : -INFINITY;
         } else {
             // partials keep the accumulator's register layout:
             // [slot][r][dt][lane] float4, one contiguous kilobyte per store
@@ -649,7 +710,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                                           o[r][dt][2] * inv, o[r][dt][3] * inv);
             if (g == 0)
                 a.part_lse[slot * (16 * NT) + 16 * r + n] =
-                    l > 0.f ? m_run[r] + __log2f(l) : -INFINITY;
+                    l > 0.f ? m_use[r] + __log2f(l) : -INFINITY;
         }
     }
 }
@@ -664,23 +725,22 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 template <int kv, int D, int NT>
 __global__ __launch_bounds__(64) PA_OCCUPANCY void attention_kernel(AttnArgs a) {
     const int* h = a.hdr + HDR_STREAM + 4 * a.stream;
-    const int V = h[HDR_NPIECES], R = h[HDR_R], total = h[HDR_TOTAL];
+    const int V = h[HDR_NPIECES], R = h[HDR_R], B = h[HDR_TOTAL];
     const int Hkv = a.num_kv_heads;
     for (int v = blockIdx.x; v < V; v += gridDim.x) {
         const PieceStart ps = a.pieces[v];
-        int t = ps.tile, kvh = ps.kvh, j = ps.j;
+        int t = ps.tile, j = ps.j;
+        const int kvh = ps.kvh;
         TileDesc td = ps.td;
-        int left = (int)min((int64_t)R, (int64_t)total - (int64_t)v * R);
+        // the piece's blocks, within its KV head's substream
+        int left = (int)min((int64_t)R, (int64_t)B - (int64_t)(v / Hkv) * R);
         while (left > 0) {
             const int take = min(left, td.nb - j);
             run_segment<kv, D, NT>(a, td, kvh, j, take, v);
             left -= take;
             j = 0;
-            if (++kvh == Hkv) {
-                kvh = 0;
-                ++t;
-                if (left > 0) td = a.tiles[t];
-            }
+            ++t;
+            if (left > 0) td = a.tiles[t];
         }
     }
 }
@@ -696,14 +756,18 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void attention_kernel(AttnArgs a) 
 template <int qd, int D>
 __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     const SplitSeg sp = a.splits[blockIdx.x];
-    if (sp.v0 < 0) return;  // past the list of cut segments
+    if (sp.k0 < 0) return;  // past the list of cut segments
     const int lane = threadIdx.x;
     const int n = lane & 15, g = lane >> 4;  // the attention kernel's layout
     const int G = a.group;
     const int nt = sp.stream == STREAM_WIDE ? wide_tiles(qd) : 1;  // row tiles per slot
     const float* part_lse = a.part_lse[sp.stream];
     const float4* part_o = (const float4*)a.part_o[sp.stream];
-    auto slot_of = [&](int v) { return (int64_t)v * 2 + (v == sp.v0 ? SLOT_TAIL : SLOT_HEAD); };
+    const int Hkv = a.num_kv_heads;
+    // slot of the segment's k-th piece (k0: the tail it left unfinished)
+    auto slot_of = [&](int k) {
+        return ((int64_t)k * Hkv + sp.kvh) * 2 + (k == sp.k0 ? SLOT_TAIL : SLOT_HEAD);
+    };
     for (int r = 0; r < nt; ++r) {
         const int rr = 16 * r + n;
         if (rr >= sp.ntok * G) break;  // rows past the tile hold no partials
@@ -711,14 +775,14 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
         float4 acc[D / 16];
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) acc[dt] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int v = sp.v0; v <= sp.v1; v += 4) {
+        for (int k = sp.k0; k <= sp.k1; k += 4) {
             // all four pieces' values are requested before any is used
             float l4[4];
             float4 x[4][D / 16];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const bool ok = v + u <= sp.v1;
-                const int64_t sl = slot_of(ok ? v + u : sp.v1);
+                const bool ok = k + u <= sp.k1;
+                const int64_t sl = slot_of(ok ? k + u : sp.k1);
                 l4[u] = ok ? part_lse[sl * (16 * nt) + rr] : -INFINITY;
                 const float4* po = part_o + ((sl * nt + r) * (D / 16)) * 64 + lane;
 #pragma unroll
@@ -762,8 +826,8 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
                     acc[dt].x * inv, acc[dt].y * inv, acc[dt].z * inv, acc[dt].w * inv);
             } else {
                 uint2 w;
-                w.x = bf16_bits_rne(acc[dt].x * inv) | (bf16_bits_rne(acc[dt].y * inv) << 16);
-                w.y = bf16_bits_rne(acc[dt].z * inv) | (bf16_bits_rne(acc[dt].w * inv) << 16);
+                w.x = pack_bf16x2(acc[dt].x * inv, acc[dt].y * inv);
+                w.y = pack_bf16x2(acc[dt].z * inv, acc[dt].w * inv);
                 *(uint2*)((uint16_t*)a.out + row * D + d) = w;
             }
         }

@@ -36,14 +36,15 @@ struct PieceStart {
 };
 
 // A segment cut by piece boundaries: its rows and the pieces holding its
-// partial results (v0 wrote its tail slot, v0+1 .. v1 their head slots);
-// piece numbers are local to the segment's stream.
+// partial results. Pieces are numbered within the substream of the
+// segment's KV head: k0 wrote its tail slot, k0+1 .. k1 their head slots;
+// piece k of KV head h is piece k * Hkv + h of the stream.
 struct SplitSeg {
     int32_t row0;    // first query token row of the tile
     int32_t ntok;    // query tokens in the tile
     int32_t kvh;
-    int32_t v0;
-    int32_t v1;
+    int32_t k0;
+    int32_t k1;
     int32_t stream;  // STREAM_WIDE or STREAM_NARROW
     int32_t pad[2];
 };
@@ -55,8 +56,9 @@ enum { STREAM_WIDE = 0, STREAM_NARROW = 1, NUM_STREAMS = 2 };
 // 16-row MFMA tiles in a wide tile (fp32 operands take twice the registers)
 constexpr int wide_tiles(int dtype) { return dtype == PA_F32 ? 2 : 4; }
 
-// Header words at the start of the workspace: per stream s, its total
-// blocks, piece size and piece count at HDR_STREAM + 4 s.
+// Header words at the start of the workspace: per stream s, the blocks of
+// each KV head's substream, the piece size and the piece count at
+// HDR_STREAM + 4 s.
 enum {
     HDR_NTILES = 0,
     HDR_NSPLIT = 1,
@@ -127,6 +129,7 @@ struct MergeArgs {
     const float* part_lse[NUM_STREAMS];
     const float* part_o[NUM_STREAMS];
     int32_t num_q_heads;
+    int32_t num_kv_heads;
     int32_t group;
 };
 
