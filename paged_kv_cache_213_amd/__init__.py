@@ -52,6 +52,9 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise PagedAttentionError(
             f"{path} is missing: build it with `python -m paged_kv_cache_213_amd.build`")
+    # torch first: the library then binds to the HIP runtime torch already
+    # loaded, instead of bringing a second one into the process
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     S = ctypes.POINTER(PaShape)

@@ -6,6 +6,10 @@
 
 #include "pa_internal.h"
 
+#ifndef PA_WIDE_SPANS
+#define PA_WIDE_SPANS 1
+#endif
+
 namespace {
 
 
@@ -62,10 +66,14 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     l.narrow_tokens = decode ? 1 : (16 / G > 1 ? 16 / G : 1);
     l.wide_tokens = (16 * wt) / G > 1 ? (16 * wt) / G : 1;
     l.part_blocks = s->partition_size / PA_BLOCK_SIZE;
-    const bool spans = !decode && max_query_len > l.narrow_tokens;
+    // wide tiles for spans longer than a narrow tile (0: every span in narrow tiles)
+    const bool spans = PA_WIDE_SPANS && !decode && max_query_len > l.narrow_tokens;
+    if (!spans) l.wide_tokens = 0;
     const int64_t tiles_of[pa::NUM_STREAMS] = {
         spans ? (int64_t)num_seqs + cdiv(num_tokens, l.wide_tokens) : 0,  // wide: spans
-        (int64_t)num_seqs};                                                // narrow: one each
+        // narrow: one per sequence, or every span cut into narrow tiles
+        spans || decode ? (int64_t)num_seqs
+                        : (int64_t)num_seqs + cdiv(num_tokens, l.narrow_tokens)};
     l.max_tiles = tiles_of[0] + tiles_of[1];
     const int64_t blocks_per_tile = cdiv(max_context_len > 0 ? max_context_len : 1, PA_BLOCK_SIZE);
     size_t off = align_up(sizeof(int32_t) * pa::HDR_WORDS);

@@ -91,13 +91,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-// Two e4m3fn bytes (b0 low) -> two bf16 packed in a dword. Every e4m3 value
-// is exact in fp32 and in bf16, so the fp32 -> bf16 step drops zero bits.
+// Two e4m3fn bytes (the low or the high half of a dword, b0 low) -> two
+// bf16 packed in a dword, with one gfx950 conversion (scale 1). Every e4m3
+// value is exact in bf16, so the conversion rounds nothing.
 template <bool hi>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(word, hi);
-    return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xffff0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, hi));
 }
 
 // K/V loads. A block that one wave reads once per call (a decode's context)
@@ -368,7 +367,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                 n = a.qsl ? a.qsl[i + 1] - qs : 1;
                 L = min(max(a.context_lens[i], 0), a.max_context_len);
                 if (qs < 0 || n < 0 || qs + n > a.num_tokens) n = 0;  // malformed span
-                const bool wide = n > a.narrow_tokens;
+                const bool wide = a.wide_tokens > 0 && n > a.narrow_tokens;
                 tt = wide ? a.wide_tokens : a.narrow_tokens;
                 ntl = (n > 0 && wide == (st == STREAM_WIDE)) ? (n + tt - 1) / tt : 0;
             }
@@ -717,13 +716,8 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 
 // One wave per workgroup; wave w streams pieces w, w + grid, ... of its
 // stream (tiles of NT row tiles).
-#ifdef PA_WAVES_PER_EU
-#define PA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU, 8)))
-#else
-#define PA_OCCUPANCY
-#endif
 template <int kv, int D, int NT>
-__global__ __launch_bounds__(64) PA_OCCUPANCY void attention_kernel(AttnArgs a) {
+__device__ __forceinline__ void attention_body(const AttnArgs& a) {
     const int* h = a.hdr + HDR_STREAM + 4 * a.stream;
     const int V = h[HDR_NPIECES], R = h[HDR_R], B = h[HDR_TOTAL];
     const int Hkv = a.num_kv_heads;
@@ -743,6 +737,28 @@ __global__ __launch_bounds__(64) PA_OCCUPANCY void attention_kernel(AttnArgs a) 
             if (left > 0) td = a.tiles[t];
         }
     }
+}
+
+// Single-token tiles: bound by HBM. The compiler's own register budget
+// gives two waves per SIMD; PA_NARROW_MIN_WAVES > 0 would demand more (and
+// keep the accumulators out of the AGPRs), which measured no faster.
+#ifndef PA_NARROW_MIN_WAVES
+#define PA_NARROW_MIN_WAVES 0
+#endif
+#if PA_NARROW_MIN_WAVES > 0
+#define PA_NARROW_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_NARROW_MIN_WAVES, 8)))
+#else
+#define PA_NARROW_OCCUPANCY
+#endif
+template <int kv, int D>
+__global__ __launch_bounds__(64) PA_NARROW_OCCUPANCY void attention_narrow(AttnArgs a) {
+    attention_body<kv, D, 1>(a);
+}
+
+// Wide tiles of chunked-prefill spans: matrix-core bound, one wave per SIMD.
+template <int kv, int D>
+__global__ __launch_bounds__(64) void attention_wide(AttnArgs a) {
+    attention_body<kv, D, wide_tiles(kv)>(a);
 }
 
 // ---- merge -------------------------------------------------------------------
@@ -835,36 +851,43 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     }
 }
 
+// The attention kernels' e4m3 conversion, one byte per thread, widened to
+// float32 (exact: bf16 is a prefix of float32).
 __global__ void fp8_decode_kernel(const uint8_t* in, float* out, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((uint32_t)in[i], false);
-    out[i] = f.x;
+    out[i] = __uint_as_float(fp8x2_to_bf16x2<false>((uint32_t)in[i]) << 16);
 }
 
 // ---- launch configuration ----------------------------------------------------
 
-template <int kv, int D, int NT>
-int resident_waves_t() {
-    static int cached = -1;  // device properties do not change in a process
-    if (cached < 0) {
-        int dev = 0, num_cu = 0, occ = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) !=
-                hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attention_kernel<kv, D, NT>, 64,
-                                                         0) != hipSuccess)
-            return 0;
-        cached = (occ > 0 ? occ : 1) * num_cu;
-    }
-    return cached;
+// Experiments may cap the narrow kernel's waves per SIMD (0: no cap).
+#ifndef PA_NARROW_MAX_WAVES
+#define PA_NARROW_MAX_WAVES 0
+#endif
+
+template <typename K>
+int resident_waves_of(K kernel, int cap_per_simd) {
+    int dev = 0, num_cu = 0, occ = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, 64, 0) != hipSuccess)
+        return 0;
+    if (cap_per_simd > 0 && occ > 4 * cap_per_simd) occ = 4 * cap_per_simd;
+    return (occ > 0 ? occ : 1) * num_cu;
 }
 
 template <int kv, int D>
 int resident_waves_d(int stream) {
-    return stream == STREAM_WIDE ? resident_waves_t<kv, D, wide_tiles(kv)>()
-                                 : resident_waves_t<kv, D, 1>();
+    static int cached[NUM_STREAMS] = {-1, -1};  // device properties do not change
+    if (cached[stream] < 0) {
+        const int w = stream == STREAM_WIDE
+                          ? resident_waves_of(attention_wide<kv, D>, 0)
+                          : resident_waves_of(attention_narrow<kv, D>, PA_NARROW_MAX_WAVES);
+        if (w <= 0) return 0;
+        cached[stream] = w;
+    }
+    return cached[stream];
 }
 
 template <int kv, int D>
@@ -874,10 +897,9 @@ hipError_t launch_attention_d(const AttnArgs& a, int64_t max_pieces, hipStream_t
     if (max_pieces < grid) grid = max_pieces;
     if (grid < 1) grid = 1;
     if (a.stream == STREAM_WIDE)
-        hipLaunchKernelGGL((attention_kernel<kv, D, wide_tiles(kv)>), dim3((unsigned)grid),
-                           dim3(64), 0, s, a);
+        hipLaunchKernelGGL((attention_wide<kv, D>), dim3((unsigned)grid), dim3(64), 0, s, a);
     else
-        hipLaunchKernelGGL((attention_kernel<kv, D, 1>), dim3((unsigned)grid), dim3(64), 0, s, a);
+        hipLaunchKernelGGL((attention_narrow<kv, D>), dim3((unsigned)grid), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
