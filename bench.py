@@ -378,8 +378,9 @@ def main():
             "traffic_note": "HBM bytes per attention pass launch (calibrated FETCH_SIZE + "
                             "WRITE_SIZE, profiles/); null if not recorded for the current "
                             "attention source",
-            "kernel": "attention_kernel (pass 1, one launch per layer); HIP events around "
-                      "the back-to-back pass-1 launches of all layers, divided by the layers",
+            "kernel": "attention pass (attention_wide for chunked-prefill spans, then "
+                      "attention_narrow, one launch each per layer); HIP events around the "
+                      "back-to-back pass-1 launches of all layers, divided by the layers",
             "launch_us_mean": round(att_mean * 1e3, 2),
             "launch_us_min_max": [round(float(att_ms.min()) * 1e3, 2),
                                   round(float(att_ms.max()) * 1e3, 2)],

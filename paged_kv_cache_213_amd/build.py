@@ -26,6 +26,9 @@ FLAGS = [
     "-Wall",
     # no packed fp32 arithmetic in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in VGPRs: the softmax rescale of the output
+    # accumulators then needs no AGPR <-> VGPR copies in the block loop
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

@@ -483,6 +483,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
 // ---- attention ---------------------------------------------------------------
 
+#ifndef PA_WIDE_SCHED_BARRIER
+#define PA_WIDE_SCHED_BARRIER 1
+#endif
 #ifndef PA_PREFETCH
 #define PA_PREFETCH 1
 #endif
@@ -661,7 +664,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 consume(ring[r], i0 + r);
                 // keep the steps in order: the scheduler would otherwise hoist
                 // later steps' products above their loads' waits
-                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (NT == 1 || PA_WIDE_SCHED_BARRIER) __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -739,9 +742,8 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
     }
 }
 
-// Single-token tiles: bound by HBM. The compiler's own register budget
-// gives two waves per SIMD; PA_NARROW_MIN_WAVES > 0 would demand more (and
-// keep the accumulators out of the AGPRs), which measured no faster.
+// Single-token tiles: bound by HBM. PA_NARROW_MIN_WAVES > 0 would make the
+// compiler budget registers for that many waves per SIMD.
 #ifndef PA_NARROW_MIN_WAVES
 #define PA_NARROW_MIN_WAVES 0
 #endif
@@ -861,9 +863,11 @@ __global__ void fp8_decode_kernel(const uint8_t* in, float* out, int n) {
 
 // ---- launch configuration ----------------------------------------------------
 
-// Experiments may cap the narrow kernel's waves per SIMD (0: no cap).
+// Waves per SIMD of the persistent narrow grid (0: as many as fit). Its
+// registers would allow three; two keep more of each wave's loads in flight
+// per byte of cache and measured faster.
 #ifndef PA_NARROW_MAX_WAVES
-#define PA_NARROW_MAX_WAVES 0
+#define PA_NARROW_MAX_WAVES 2
 #endif
 
 template <typename K>

@@ -54,7 +54,10 @@ struct SplitSeg {
 // 16 rows). Each is cut into its own pieces and run by its own launch.
 enum { STREAM_WIDE = 0, STREAM_NARROW = 1, NUM_STREAMS = 2 };
 // 16-row MFMA tiles in a wide tile (fp32 operands take twice the registers)
-constexpr int wide_tiles(int dtype) { return dtype == PA_F32 ? 2 : 4; }
+#ifndef PA_WIDE_TILES
+#define PA_WIDE_TILES 4
+#endif
+constexpr int wide_tiles(int dtype) { return dtype == PA_F32 ? 2 : PA_WIDE_TILES; }
 
 // Header words at the start of the workspace: per stream s, the blocks of
 // each KV head's substream, the piece size and the piece count at
