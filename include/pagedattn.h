@@ -94,6 +94,8 @@ typedef struct pa_shape {
     int32_t q_dtype;            /* pa_dtype of q, out, and new K/V rows */
     int32_t kv_dtype;           /* pa_dtype of the caches */
     int32_t partition_size;     /* split-KV piece in tokens, 0 = balanced */
+    int32_t cascade;            /* 1: plans may hold shared-prefix groups
+                                   (pa_plan_cascade); reserves their room */
 } pa_shape;
 
 /* Bytes of device workspace the attention calls need for this batch (work
@@ -142,6 +144,33 @@ int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const voi
 int pa_plan(const pa_shape* shape, const int32_t* context_lens, const int32_t* query_start_loc,
             int num_seqs, int num_q_tokens, int max_query_len, int max_context_len,
             void* workspace, size_t workspace_bytes, void* stream);
+
+/* pa_plan for a batch in which groups of single-token sequences share the
+ * physical blocks of a common prefix -- a parallel-sampling group, requests
+ * that hit the same cached prompt -- through copy-on-write ("03 -- Engines
+ * Papers", section 2). Cascade attention (same page, section 12): each
+ * group's prefix is read once for all of its members, in tiles of up to
+ * 16 * 4 / G members (16 * 2 / G for F32), and each member reads only the
+ * blocks after the prefix; the run's merge pass combines the two parts of
+ * every member by log-sum-exp. The outputs are the same attention as
+ * without groups, up to rounding.
+ *
+ * Group g's members are group_members[group_offsets[g] ..
+ * group_offsets[g + 1]) (sequence indices; device arrays, group_offsets
+ * [num_groups + 1] with group_offsets[0] = 0 and group_offsets[num_groups]
+ * = num_members); they share their first group_prefix_blocks[g] block-table
+ * entries (device [num_groups]). The prefix is read through the first
+ * member's block table. A member that has more than one query token, or no
+ * key past the prefix, reads its whole context itself instead. Contract
+ * (not checked by the kernels): the members' tables do hold the same
+ * physical blocks there, and a sequence is in at most one group.
+ * shape->cascade must be 1; num_groups, num_members <= num_seqs. */
+int pa_plan_cascade(const pa_shape* shape, const int32_t* context_lens,
+                    const int32_t* query_start_loc, int num_seqs, int num_q_tokens,
+                    int max_query_len, int max_context_len, int num_groups, int num_members,
+                    const int32_t* group_offsets, const int32_t* group_members,
+                    const int32_t* group_prefix_blocks, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /* Attention with a plan made by pa_plan (same arguments as the plan, plus
  * the tensors). Enqueues the attention pass (one launch per tile class
@@ -192,7 +221,8 @@ int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream);
 /* Static text for a status code. */
 const char* pa_status_string(int status);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor): 200 added pa_shape.cascade
+ * and pa_plan_cascade. */
 int pa_version(void);
 
 #ifdef __cplusplus

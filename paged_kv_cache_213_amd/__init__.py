@@ -37,6 +37,7 @@ class PaShape(ctypes.Structure):
         ("q_dtype", ctypes.c_int32),
         ("kv_dtype", ctypes.c_int32),
         ("partition_size", ctypes.c_int32),
+        ("cascade", ctypes.c_int32),
     ]
 
 
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH):
     lib.pa_paged_attn_hybrid.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
     lib.pa_plan.restype = I
     lib.pa_plan.argtypes = [S, P, P, I, I, I, I, P, Z, P]
+    lib.pa_plan_cascade.restype = I
+    lib.pa_plan_cascade.argtypes = [S, P, P, I, I, I, I, I, I, P, P, P, P, Z, P]
     lib.pa_paged_attn_run.restype = I
     lib.pa_paged_attn_run.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
     lib.pa_paged_attn_partial.restype = I
@@ -121,13 +124,14 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
-def make_shape(q, k_cache, block_tables, partition_size: int = 0) -> PaShape:
+def make_shape(q, k_cache, block_tables, partition_size: int = 0,
+               cascade: bool = False) -> PaShape:
     T, Hq, D = q.shape
     NB, Hkv, B, D2 = k_cache.shape
     if B != 16 or D2 != D:
         raise PagedAttentionError(f"k_cache shape {tuple(k_cache.shape)} does not match q")
     return PaShape(Hq, Hkv, D, 16, NB, block_tables.shape[1], _dtype_code(q),
-                   _dtype_code(k_cache), int(partition_size))
+                   _dtype_code(k_cache), int(partition_size), int(bool(cascade)))
 
 
 def workspace_bytes(shape: PaShape, num_seqs: int, num_q_tokens: int, max_context_len: int,
@@ -193,6 +197,30 @@ def hybrid(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, sca
     return out
 
 
+def cascade(q, k_cache, v_cache, block_tables, context_lens, scale: float, groups, *,
+            max_context_len: int, query_start_loc=None, max_query_len: int = 1, k_scale=None,
+            v_scale=None, partition_size: int = 0, out=None, lse=None, workspace=None,
+            stream=None):
+    """Paged attention with shared-prefix groups (``PrefixGroups``): plan
+    with the groups, then the attention and merge passes. Same result as
+    decode()/hybrid(); each group's prefix is read once for its members."""
+    import torch
+    shape = make_shape(q, k_cache, block_tables, partition_size, cascade=True)
+    T = q.shape[0]
+    S = context_lens.shape[0]
+    mq = max_query_len if query_start_loc is not None else 1
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = workspace_bytes(shape, S, T, max_context_len, mq)
+    ws = _workspace(nbytes, q.device, workspace)
+    plan_cascade(shape, context_lens, ws, groups, query_start_loc=query_start_loc,
+                 num_q_tokens=T, max_query_len=mq, max_context_len=max_context_len, stream=stream)
+    return run(shape, q, k_cache, v_cache, block_tables, context_lens, scale, ws,
+               query_start_loc=query_start_loc, max_query_len=mq,
+               max_context_len=max_context_len, k_scale=k_scale, v_scale=v_scale, out=out,
+               lse=lse, stream=stream)
+
+
 def plan(shape: PaShape, context_lens, workspace, *, query_start_loc=None, num_q_tokens: int,
          max_query_len: int, max_context_len: int, stream=None):
     """Enqueue the work plan of a batch into ``workspace`` (reusable by every
@@ -203,6 +231,40 @@ def plan(shape: PaShape, context_lens, workspace, *, query_start_loc=None, num_q
                      int(num_q_tokens), int(max_query_len), int(max_context_len), _ptr(workspace),
                      workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "pa_plan")
+
+
+class PrefixGroups:
+    """Shared-prefix groups of a batch for cascade attention, as device
+    int32 tensors: CSR offsets [G + 1], member sequence indices, and the
+    shared leading blocks of each group."""
+
+    def __init__(self, groups, prefix_blocks, device):
+        import torch
+        offs, mem = [0], []
+        for g in groups:
+            mem.extend(int(i) for i in g)
+            offs.append(len(mem))
+        self.num_groups = len(groups)
+        self.num_members = len(mem)
+        self.offsets = torch.tensor(offs, dtype=torch.int32, device=device)
+        self.members = torch.tensor(mem if mem else [0], dtype=torch.int32, device=device)
+        self.prefix_blocks = torch.tensor([int(b) for b in prefix_blocks] or [0],
+                                          dtype=torch.int32, device=device)
+
+
+def plan_cascade(shape: PaShape, context_lens, workspace, groups: PrefixGroups, *,
+                 query_start_loc=None, num_q_tokens: int, max_query_len: int,
+                 max_context_len: int, stream=None):
+    """plan() with shared-prefix groups: each group's prefix is read once
+    for all its single-token members (shape.cascade must be 1)."""
+    lib = load_library()
+    S = context_lens.shape[0]
+    rc = lib.pa_plan_cascade(ctypes.byref(shape), _ptr(context_lens), _ptr(query_start_loc), S,
+                             int(num_q_tokens), int(max_query_len), int(max_context_len),
+                             groups.num_groups, groups.num_members, _ptr(groups.offsets),
+                             _ptr(groups.members), _ptr(groups.prefix_blocks), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "pa_plan_cascade")
 
 
 def run(shape: PaShape, q, k_cache, v_cache, block_tables, context_lens, scale: float, workspace,

@@ -32,6 +32,13 @@ struct Layout {
     size_t off_pieces[pa::NUM_STREAMS] = {0, 0};
     size_t off_lse[pa::NUM_STREAMS] = {0, 0};
     size_t off_o[pa::NUM_STREAMS] = {0, 0};
+    // cascade (shared-prefix groups), when the shape allows them
+    bool cascade = false;
+    int members_per_tile = 0;
+    int64_t max_cas_recs = 0;
+    size_t off_cas_seq = 0;  // 5 int arrays of num_seqs
+    size_t off_cas_recs = 0;
+    size_t off_cas_lse[2] = {0, 0}, off_cas_o[2] = {0, 0};
 };
 
 int check_shape(const pa_shape* s) {
@@ -47,6 +54,7 @@ int check_shape(const pa_shape* s) {
                     (s->q_dtype == PA_BF16 && s->kv_dtype == PA_FP8_E4M3FN);
     if (!ok) return PA_EINVAL;
     if (s->partition_size < 0 || s->partition_size % PA_BLOCK_SIZE) return PA_EINVAL;
+    if (s->cascade != 0 && s->cascade != 1) return PA_EINVAL;
     return PA_OK;
 }
 
@@ -69,8 +77,14 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     // wide tiles for spans longer than a narrow tile (0: every span in narrow tiles)
     const bool spans = PA_WIDE_SPANS && !decode && max_query_len > l.narrow_tokens;
     if (!spans) l.wide_tokens = 0;
+    l.cascade = s->cascade != 0;
+    l.members_per_tile = (16 * wt) / G > 1 ? (16 * wt) / G : 1;
+    // wide: spans' tiles, then shared-prefix groups' tiles (at most one per
+    // group plus one per members_per_tile members, each sequence in at most
+    // one group)
     const int64_t tiles_of[pa::NUM_STREAMS] = {
-        spans ? (int64_t)num_seqs + cdiv(num_tokens, l.wide_tokens) : 0,  // wide: spans
+        (spans ? (int64_t)num_seqs + cdiv(num_tokens, l.wide_tokens) : 0) +
+            (l.cascade ? 2 * (int64_t)num_seqs : 0),
         // narrow: one per sequence, or every span cut into narrow tiles
         spans || decode ? (int64_t)num_seqs
                         : (int64_t)num_seqs + cdiv(num_tokens, l.narrow_tokens)};
@@ -96,6 +110,20 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     }
     l.off_splits = off;  // every cut segment holds a piece boundary of its stream
     off = align_up(off + sizeof(pa::SplitSeg) * (size_t)(splits > 0 ? splits : 1));
+    if (l.cascade) {
+        const size_t rows = (size_t)num_tokens * s->num_q_heads;
+        l.max_cas_recs = (int64_t)num_seqs * s->num_kv_heads;
+        l.off_cas_seq = off;
+        off = align_up(off + sizeof(int32_t) * 5 * (size_t)num_seqs);
+        l.off_cas_recs = off;
+        off = align_up(off + sizeof(pa::CascadeRec) * (size_t)l.max_cas_recs);
+        for (int k = 0; k < 2; ++k) {
+            l.off_cas_lse[k] = off;
+            off = align_up(off + sizeof(float) * rows);
+            l.off_cas_o[k] = off;
+            off = align_up(off + sizeof(float) * rows * s->head_dim);
+        }
+    }
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
         const int nt = st == pa::STREAM_WIDE ? wt : 1;
         const size_t slots = (size_t)l.max_pieces[st] * 2;
@@ -140,13 +168,27 @@ int check_io(const pa_shape* s, const void* out, const void* q, const void* k_ca
     return PA_OK;
 }
 
+// Shared-prefix groups handed to a plan (device arrays, host counts).
+struct Groups {
+    int num_groups = 0, num_members = 0;
+    const int32_t* offsets = nullptr;
+    const int32_t* members = nullptr;
+    const int32_t* prefix_blocks = nullptr;
+};
+
 int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl, int num_seqs,
-              int num_tokens, int max_query_len, int max_context_len, void* workspace,
-              size_t workspace_bytes, void* stream) {
+              int num_tokens, int max_query_len, int max_context_len, const Groups& grp,
+              void* workspace, size_t workspace_bytes, void* stream) {
     Layout l;
     int rc = check_batch(s, context_lens, qsl, num_seqs, num_tokens, max_query_len,
                          max_context_len, workspace, workspace_bytes, &l);
     if (rc != PA_OK) return rc;
+    if (grp.num_groups < 0 || grp.num_members < 0) return PA_EINVAL;
+    if (grp.num_groups > 0) {
+        if (!l.cascade) return PA_EINVAL;  // the shape reserved no room for groups
+        if (grp.num_groups > num_seqs || grp.num_members > num_seqs) return PA_EINVAL;
+        if (!grp.offsets || !grp.members || !grp.prefix_blocks) return PA_EINVAL;
+    }
     if (num_seqs == 0 || num_tokens == 0) return PA_OK;
     char* ws = (char*)workspace;
     pa::PlanArgs pl{};
@@ -169,6 +211,21 @@ int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl
     }
     pl.splits = (pa::SplitSeg*)(ws + l.off_splits);
     pl.hdr = (int32_t*)ws;
+    if (l.cascade) {
+        pl.num_groups = grp.num_groups;
+        pl.members_per_tile = l.members_per_tile;
+        pl.group_offsets = grp.offsets;
+        pl.group_members = grp.members;
+        pl.group_prefix_blocks = grp.prefix_blocks;
+        int32_t* cs = (int32_t*)(ws + l.off_cas_seq);
+        pl.cas_prefix = cs;
+        pl.cas_tile = cs + num_seqs;
+        pl.cas_gtile = cs + 2 * (size_t)num_seqs;
+        pl.cas_pos = cs + 3 * (size_t)num_seqs;
+        pl.cas_members = cs + 4 * (size_t)num_seqs;
+        pl.cas_recs = (pa::CascadeRec*)(ws + l.off_cas_recs);
+        pl.max_cas_recs = (int32_t)l.max_cas_recs;
+    }
     return pa::launch_plan(pl, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_EHIP;
 }
 
@@ -214,6 +271,15 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
         aa.max_blocks_per_seq = s->max_blocks_per_seq;
         aa.max_context_len = max_context_len;
         aa.scale_log2 = scale * 1.44269504088896340736f;
+        aa.num_seqs = num_seqs;
+        if (l.cascade) {
+            aa.cas_prefix = (const int32_t*)(ws + l.off_cas_seq);
+            aa.group_members = (const int32_t*)(ws + l.off_cas_seq) + 4 * (size_t)num_seqs;
+            for (int k = 0; k < 2; ++k) {
+                aa.cas_lse[k] = (float*)(ws + l.off_cas_lse[k]);
+                aa.cas_o[k] = (float*)(ws + l.off_cas_o[k]);
+            }
+        }
         // spans first (matrix-core heavy), then the single-token tiles
         for (int st = 0; st < pa::NUM_STREAMS; ++st) {
             if (l.max_pieces[st] == 0) continue;
@@ -239,8 +305,19 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
         ma.num_q_heads = s->num_q_heads;
         ma.num_kv_heads = s->num_kv_heads;
         ma.group = s->num_q_heads / s->num_kv_heads;
-        const int64_t records = l.max_pieces[0] + l.max_pieces[1];
-        if (records > 1 && pa::launch_merge(s->q_dtype, s->head_dim, ma, records, hs) != hipSuccess)
+        const int64_t splits = l.max_pieces[0] + l.max_pieces[1];
+        ma.max_splits = (int32_t)splits;
+        int64_t records = splits > 1 ? splits : 0;  // one piece cuts nothing
+        if (l.cascade) {
+            ma.max_splits = (int32_t)records;
+            ma.cas_recs = (const pa::CascadeRec*)(ws + l.off_cas_recs);
+            for (int k = 0; k < 2; ++k) {
+                ma.cas_lse[k] = (const float*)(ws + l.off_cas_lse[k]);
+                ma.cas_o[k] = (const float*)(ws + l.off_cas_o[k]);
+            }
+            records += l.max_cas_recs;
+        }
+        if (records > 0 && pa::launch_merge(s->q_dtype, s->head_dim, ma, records, hs) != hipSuccess)
             return PA_EHIP;
     }
     return PA_OK;
@@ -265,7 +342,23 @@ int pa_plan(const pa_shape* shape, const int32_t* context_lens, const int32_t* q
             int num_seqs, int num_q_tokens, int max_query_len, int max_context_len,
             void* workspace, size_t workspace_bytes, void* stream) {
     return plan_impl(shape, context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
-                     max_context_len, workspace, workspace_bytes, stream);
+                     max_context_len, Groups{}, workspace, workspace_bytes, stream);
+}
+
+int pa_plan_cascade(const pa_shape* shape, const int32_t* context_lens,
+                    const int32_t* query_start_loc, int num_seqs, int num_q_tokens,
+                    int max_query_len, int max_context_len, int num_groups, int num_members,
+                    const int32_t* group_offsets, const int32_t* group_members,
+                    const int32_t* group_prefix_blocks, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    Groups grp;
+    grp.num_groups = num_groups;
+    grp.num_members = num_members;
+    grp.offsets = group_offsets;
+    grp.members = group_members;
+    grp.prefix_blocks = group_prefix_blocks;
+    return plan_impl(shape, context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                     max_context_len, grp, workspace, workspace_bytes, stream);
 }
 
 int pa_paged_attn_run(const pa_shape* shape, void* out, float* lse, const void* q,
@@ -311,7 +404,7 @@ int pa_paged_attn_decode(const pa_shape* shape, void* out, float* lse, const voi
         if (rc0 != PA_OK) return rc0;
     }
     int rc = plan_impl(shape, context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len,
-                       workspace, workspace_bytes, stream);
+                       Groups{}, workspace, workspace_bytes, stream);
     if (rc != PA_OK) return rc;
     return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                     context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len, scale,
@@ -332,7 +425,7 @@ int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const voi
         if (rc0 != PA_OK) return rc0;
     }
     int rc = plan_impl(shape, context_lens, query_start_loc, num_seqs, num_q_tokens,
-                       max_query_len, max_context_len, workspace, workspace_bytes, stream);
+                       max_query_len, max_context_len, Groups{}, workspace, workspace_bytes, stream);
     if (rc != PA_OK) return rc;
     return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                     context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
@@ -374,6 +467,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 100; }
+int pa_version(void) { return 200; }
 
 }  // extern "C"

@@ -354,36 +354,112 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __shared__ int s_nsplit;
     const int cap = min(a.max_tiles, kMaxTiles);
     const int H = a.num_kv_heads;
+    const int S = a.num_seqs;
+    auto span_of = [&](int i, int& qs, int& n, int& L) {
+        qs = a.qsl ? a.qsl[i] : i;
+        n = a.qsl ? a.qsl[i + 1] - qs : 1;
+        L = min(max(a.context_lens[i], 0), a.max_context_len);
+        if (qs < 0 || n < 0 || qs + n > a.num_tokens) n = 0;  // malformed span
+    };
+
+    // 0. shared-prefix groups: a single-token member whose context extends
+    //    past the group's prefix reads the prefix through its group's tiles
+    //    and only the rest itself (cascade attention)
+    if (a.num_groups > 0) {
+        for (int i = threadIdx.x; i < S; i += kPlanThreads) {
+            a.cas_prefix[i] = 0;
+            a.cas_tile[i] = -1;
+            a.cas_gtile[i] = -1;
+            a.cas_pos[i] = 0;
+            // the attention pass reads the members from the workspace (the
+            // host guarantees at most num_seqs of them)
+            a.cas_members[i] = i < a.group_offsets[a.num_groups] ? a.group_members[i] : -1;
+        }
+        __syncthreads();
+        for (int g = threadIdx.x; g < a.num_groups; g += kPlanThreads) {
+            const int pb = a.group_prefix_blocks[g];
+            const int e0 = a.group_offsets[g], e1 = a.group_offsets[g + 1];
+            const int lead = e1 > e0 ? a.group_members[e0] : -1;  // its table is read
+            if (pb < 1 || lead < 0 || lead >= S) continue;
+            for (int e = e0; e < e1; ++e) {
+                const int i = a.group_members[e];
+                if (i < 0 || i >= S) continue;
+                int qs, n, L;
+                span_of(i, qs, n, L);
+                if (n == 1 && L > 16 * pb) a.cas_prefix[i] = pb;
+            }
+        }
+        __syncthreads();
+    }
 
     // 1. tiles: spans longer than one narrow tile get wide tiles (stream 0),
-    //    everything else narrow ones (stream 1); sequence order within each
+    //    followed by the groups' tiles; everything else narrow ones (stream
+    //    1); sequence order within each
     int tile_base = 0, nwide = 0;
     for (int st = 0; st < NUM_STREAMS; ++st) {
-        for (int c0 = 0; c0 < a.num_seqs; c0 += kPlanThreads) {
+        for (int c0 = 0; c0 < S; c0 += kPlanThreads) {
             const int i = c0 + (int)threadIdx.x;
             int n = 0, L = 0, ntl = 0, qs = 0, tt = 1;
-            if (i < a.num_seqs) {
-                qs = a.qsl ? a.qsl[i] : i;
-                n = a.qsl ? a.qsl[i + 1] - qs : 1;
-                L = min(max(a.context_lens[i], 0), a.max_context_len);
-                if (qs < 0 || n < 0 || qs + n > a.num_tokens) n = 0;  // malformed span
+            if (i < S) {
+                span_of(i, qs, n, L);
                 const bool wide = a.wide_tokens > 0 && n > a.narrow_tokens;
                 tt = wide ? a.wide_tokens : a.narrow_tokens;
                 ntl = (n > 0 && wide == (st == STREAM_WIDE)) ? (n + tt - 1) / tt : 0;
             }
             int total;
             const int off = tile_base + block_exclusive_scan(ntl, &total);
+            const int pre = (st == STREAM_NARROW && a.num_groups > 0 && i < S) ? a.cas_prefix[i]
+                                                                               : 0;
             for (int k = 0; k < ntl; ++k) {
                 const int t = off + k;
                 if (t >= cap) break;
                 const int k0 = k * tt;
                 const int nt = min(tt, n - k0);
                 const int maxpos = L - n + k0 + nt - 1;  // last query position of the tile
-                const int nb = max(1, maxpos >= 0 ? (min(maxpos + 1, L) + 15) >> 4 : 0);
-                a.tiles[t] = TileDesc{i, k0, nt, nb, L, qs, n, 0};
-                s_tp[t] = nb;
+                int nb = max(1, maxpos >= 0 ? (min(maxpos + 1, L) + 15) >> 4 : 0);
+                TileDesc td{i, k0, nt, nb, L, qs, n, 0, 0, {0, 0, 0}};
+                if (pre > 0) {  // a cascade member's suffix: blocks pre .. of its context
+                    td.flags = TILE_SUFFIX;
+                    td.b0 = pre;
+                    td.nb = nb - pre;
+                    a.cas_tile[i] = t;
+                }
+                a.tiles[t] = td;
+                s_tp[t] = td.nb;
             }
             tile_base += total;
+        }
+        if (st == STREAM_WIDE && a.num_groups > 0) {
+            const int mpt = a.members_per_tile;
+            for (int c0 = 0; c0 < a.num_groups; c0 += kPlanThreads) {
+                const int g = c0 + (int)threadIdx.x;
+                int ntl = 0, e0 = 0, cnt = 0, pb = 0, lead = -1;
+                if (g < a.num_groups) {
+                    pb = a.group_prefix_blocks[g];
+                    e0 = a.group_offsets[g];
+                    cnt = a.group_offsets[g + 1] - e0;
+                    lead = cnt > 0 ? a.group_members[e0] : -1;
+                    if (pb >= 1 && cnt > 0 && lead >= 0 && lead < S) ntl = (cnt + mpt - 1) / mpt;
+                }
+                int total;
+                const int off = tile_base + block_exclusive_scan(ntl, &total);
+                for (int k = 0; k < ntl; ++k) {
+                    const int t = off + k;
+                    if (t >= cap) break;
+                    const int m0 = k * mpt, mn = min(mpt, cnt - m0);
+                    a.tiles[t] = TileDesc{lead, e0 + m0, mn, pb, 16 * pb, 0, 1, TILE_GROUP, 0,
+                                          {0, 0, 0}};
+                    s_tp[t] = pb;
+                    for (int m = 0; m < mn; ++m) {
+                        const int i = a.group_members[e0 + m0 + m];
+                        if (i >= 0 && i < S && a.cas_prefix[i] == pb) {
+                            a.cas_gtile[i] = t;
+                            a.cas_pos[i] = m;
+                        }
+                    }
+                }
+                tile_base += total;
+            }
         }
         if (st == STREAM_WIDE) nwide = min(tile_base, cap);
     }
@@ -451,23 +527,30 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             a.hdr[HDR_STREAM + 4 * st + HDR_NPIECES] = (int)V;
         }
     }
+    // pieces of substream h holding a segment's first and last blocks
+    auto cut = [&](int t, int& k0, int& k1) {
+        const int st = t < nwide ? STREAM_WIDE : STREAM_NARROW;
+        const int t_lo = st == STREAM_WIDE ? 0 : nwide;
+        const int b0 = s_tp[t] - s_tp[t_lo];
+        k0 = b0 / Rs[st];
+        k1 = (b0 + s_tp[t + 1] - s_tp[t] - 1) / Rs[st];
+    };
 
     // 4. segments cut by a piece boundary, for the merge pass (a segment is
     //    cut iff its first and last blocks fall in different pieces of its
-    //    KV head's substream)
+    //    KV head's substream); cascade parts are combined per member (5.)
     const int64_t max_splits = a.max_pieces[0] + a.max_pieces[1];
     for (int sg = threadIdx.x; sg < ntiles * H; sg += kPlanThreads) {
         const int t = sg / H, h = sg % H;
-        const int st = t < nwide ? STREAM_WIDE : STREAM_NARROW;
-        const int t_lo = st == STREAM_WIDE ? 0 : nwide;
-        const int nb = s_tp[t + 1] - s_tp[t];
-        const int b0 = s_tp[t] - s_tp[t_lo];
-        const int k0 = b0 / Rs[st], k1 = (b0 + nb - 1) / Rs[st];
+        const TileDesc td = a.tiles[t];
+        if (td.flags != 0) continue;
+        int k0, k1;
+        cut(t, k0, k1);
         if (k0 != k1) {
             const int k = atomicAdd(&s_nsplit, 1);  // list order is irrelevant
-            const TileDesc td = a.tiles[t];
             if (k < max_splits)
-                a.splits[k] = SplitSeg{td.qs + td.qtok0, td.ntok, h, k0, k1, st, {0, 0}};
+                a.splits[k] = SplitSeg{td.qs + td.qtok0, td.ntok, h, k0, k1,
+                                       t < nwide ? STREAM_WIDE : STREAM_NARROW, {0, 0}};
         }
     }
     __syncthreads();
@@ -475,9 +558,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int nsplit = (int)min((int64_t)s_nsplit, max_splits);
     for (int64_t k = nsplit + threadIdx.x; k < max_splits; k += kPlanThreads)
         a.splits[k] = SplitSeg{0, 0, 0, -1, -1, 0, {0, 0}};
+
+    // 5. one record per (cascade member, KV head): its prefix and suffix
+    int ncas = 0;
+    if (a.num_groups > 0) {
+        for (int c0 = 0; c0 < S; c0 += kPlanThreads) {
+            const int i = c0 + (int)threadIdx.x;
+            const bool mem = i < S && a.cas_prefix[i] > 0 && a.cas_tile[i] >= 0 &&
+                             a.cas_gtile[i] >= 0 && a.cas_tile[i] < ntiles &&
+                             a.cas_gtile[i] < ntiles;
+            int total;
+            const int rank = ncas + block_exclusive_scan(mem ? 1 : 0, &total);
+            if (mem && (int64_t)(rank + 1) * H <= a.max_cas_recs) {
+                const TileDesc td = a.tiles[a.cas_tile[i]];
+                int sk0, sk1, pk0, pk1;
+                cut(a.cas_tile[i], sk0, sk1);
+                cut(a.cas_gtile[i], pk0, pk1);
+                for (int h = 0; h < H; ++h)
+                    a.cas_recs[(int64_t)rank * H + h] =
+                        CascadeRec{td.qs, h, sk0, sk1, pk0, pk1, a.cas_pos[i], 0};
+            }
+            ncas += total;
+        }
+        ncas = (int)min((int64_t)ncas * H, (int64_t)a.max_cas_recs);
+    }
     if (threadIdx.x == 0) {
         a.hdr[HDR_NTILES] = ntiles;
         a.hdr[HDR_NSPLIT] = nsplit;
+        a.hdr[HDR_NCAS] = ncas;
     }
 }
 
@@ -521,10 +629,21 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 #pragma unroll
     for (int r = 0; r < NT; ++r) {
         const int rr = 16 * r + n;
-        const int qj = rr / G;
+        const int qj = rr / G;  // token of the span (group tile: member)
         row_ok[r] = rr < nrows;
-        pos[r] = row_ok[r] ? L - nspan + td.qtok0 + qj : -1;
-        rowid[r] = (int64_t)(qs + td.qtok0 + qj) * Hq + kvh * G + (rr - qj * G);
+        if (td.flags == TILE_GROUP) {
+            // the single query token of member qj sees every prefix key; a
+            // member that reads its whole context itself has no row here
+            int i = -1;
+            if (row_ok[r]) i = a.group_members[td.qtok0 + qj];
+            row_ok[r] = i >= 0 && i < a.num_seqs && a.cas_prefix[i] == td.nb;
+            const int qrow = row_ok[r] ? (a.qsl ? a.qsl[i] : i) : 0;
+            pos[r] = row_ok[r] ? L - 1 : -1;
+            rowid[r] = (int64_t)qrow * Hq + kvh * G + (rr - qj * G);
+        } else {
+            pos[r] = row_ok[r] ? L - nspan + td.qtok0 + qj : -1;
+            rowid[r] = (int64_t)(qs + td.qtok0 + qj) * Hq + kvh * G + (rr - qj * G);
+        }
         // q operand (B of S = K q^T), holding the row's dims in the same order
         // as the K tile: f32 16m + 4g + e; bf16 32m + 8g + e; fp8
         // 64(m/2) + 16g + 8(m%2) + e for MFMA step m
@@ -569,7 +688,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     }
     // blocks ending at or before the tile's first query position are visible
     // to every row and lie inside the context: no masks
-    const int pos_first = L - nspan + td.qtok0;
+    const int pos_first = td.flags == TILE_GROUP ? L - 1 : L - nspan + td.qtok0;
 
     const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
     for (int c0 = 0; c0 < take; c0 += 64) {
@@ -580,7 +699,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         int my_phys = 0;
         float my_ks = 1.f, my_vs = 1.f;
         if (lane < cnt) {
-            my_phys = min(max(bt_row[j + c0 + lane], 0), a.num_blocks - 1);
+            my_phys = min(max(bt_row[td.b0 + j + c0 + lane], 0), a.num_blocks - 1);
             if constexpr (kv == KV_FP8) {
                 my_ks = a.k_scale[(int64_t)my_phys * Hkv + kvh];
                 my_vs = a.v_scale[(int64_t)my_phys * Hkv + kvh];
@@ -588,7 +707,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         }
         // per-block work on block i of the chunk
         auto consume = [&](T& cur, int i) {
-            const int jb = j + c0 + i;       // logical block
+            const int jb = td.b0 + j + c0 + i;  // logical block
             const int t0 = jb * 16 + 4 * g;  // my first token in it
             const bool full = jb * 16 + 15 <= pos_first;  // wave-uniform
             float c = a.scale_log2;
@@ -685,7 +804,17 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         const float l = row_sum(l_run[r]);
         const float inv = l > 0.f ? 1.0f / l : 0.f;
         if (!row_ok[r]) continue;
-        if (whole) {
+        if (whole && td.flags != 0) {
+            // a whole cascade part: normalized output and lse per row
+            const int kind = td.flags == TILE_GROUP ? CAS_PRE : CAS_SUF;
+            float* bo = a.cas_o[kind] + rowid[r] * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt)
+                *(float4*)(bo + 16 * dt + 4 * g) =
+                    make_float4(o[r][dt][0] * inv, o[r][dt][1] * inv, o[r][dt][2] * inv,
+                                o[r][dt][3] * inv);
+            if (g == 0) a.cas_lse[kind][rowid[r]] = l > 0.f ? m_use[r] + __log2f(l) : -INFINITY;
+        } else if (whole) {
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt) {
                 const int d = 16 * dt + 4 * g;
@@ -771,8 +900,98 @@ __global__ __launch_bounds__(64) void attention_wide(AttnArgs a) {
 // taken four pieces at a time with a running rescale so that one round trip
 // of loads covers the usual two to four pieces. Lanes keep the attention
 // kernel's accumulator layout (row lane % 16, dims 16dt + 4(lane / 16) + i).
+// Log-sum-exp combination of partial results for one query row, fed one
+// part at a time: (lse in log2 units, normalized output dims of this lane).
+template <int D>
+struct LseAcc {
+    float M = -INFINITY, W = 0.f;
+    float4 acc[D / 16];
+    __device__ LseAcc() {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) acc[dt] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __device__ __forceinline__ void add(float l, const float4* x) {
+        if (l == -INFINITY) return;
+        const float m = fmaxf(M, l);
+        const float r = M == -INFINITY ? 0.f : fexp2(M - m);
+        const float w = fexp2(l - m);
+        W = W * r + w;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            acc[dt].x = acc[dt].x * r + w * x[dt].x;
+            acc[dt].y = acc[dt].y * r + w * x[dt].y;
+            acc[dt].z = acc[dt].z * r + w * x[dt].z;
+            acc[dt].w = acc[dt].w * r + w * x[dt].w;
+        }
+        M = m;
+    }
+};
+
+// Writes a merged row: out (the q dtype) and lse (natural log).
+template <int qd, int D>
+__device__ __forceinline__ void write_row(const MergeArgs& a, int64_t row, int g, float M,
+                                          float W, const float4* acc) {
+    const float inv = W > 0.f ? 1.0f / W : 0.f;
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+        const int d = 16 * dt + 4 * g;
+        if constexpr (qd == PA_F32) {
+            *(float4*)((float*)a.out + row * D + d) =
+                make_float4(acc[dt].x * inv, acc[dt].y * inv, acc[dt].z * inv, acc[dt].w * inv);
+        } else {
+            uint2 w;
+            w.x = pack_bf16x2(acc[dt].x * inv, acc[dt].y * inv);
+            w.y = pack_bf16x2(acc[dt].z * inv, acc[dt].w * inv);
+            *(uint2*)((uint16_t*)a.out + row * D + d) = w;
+        }
+    }
+    if (a.lse && g == 0) a.lse[row] = W > 0.f ? (M + __log2f(W)) * kLn2 : -INFINITY;
+}
+
+// A cascade member's rows (G, one per query head of its KV head): the
+// prefix part and the suffix part, each either one whole part in the
+// per-row buffers or the slots of the pieces that cut it.
+template <int qd, int D>
+__device__ __forceinline__ void merge_cascade(const MergeArgs& a, const CascadeRec rc) {
+    const int lane = threadIdx.x;
+    const int n = lane & 15, g = lane >> 4;
+    const int G = a.group, Hkv = a.num_kv_heads;
+    if (n >= G) return;
+    const int64_t row = (int64_t)rc.row * a.num_q_heads + rc.kvh * G + n;
+    LseAcc<D> acc;
+    float4 x[D / 16];
+    for (int kind = CAS_PRE; kind <= CAS_SUF; ++kind) {
+        const int k0 = kind == CAS_PRE ? rc.pre_k0 : rc.suf_k0;
+        const int k1 = kind == CAS_PRE ? rc.pre_k1 : rc.suf_k1;
+        if (k0 == k1) {  // read whole by one piece
+            const float* bo = a.cas_o[kind] + row * D;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) x[dt] = *(const float4*)(bo + 16 * dt + 4 * g);
+            acc.add(a.cas_lse[kind][row], x);
+            continue;
+        }
+        const int st = kind == CAS_PRE ? STREAM_WIDE : STREAM_NARROW;
+        const int nt = st == STREAM_WIDE ? wide_tiles(qd) : 1;
+        const int rr = (kind == CAS_PRE ? rc.pre_pos * G : 0) + n;  // row in the slot
+        const float4* po = (const float4*)a.part_o[st];
+        for (int k = k0; k <= k1; ++k) {
+            const int64_t sl = ((int64_t)k * Hkv + rc.kvh) * 2 + (k == k0 ? SLOT_TAIL : SLOT_HEAD);
+            const float4* p = po + ((sl * nt + rr / 16) * (D / 16)) * 64 + (rr % 16) + 16 * g;
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) x[dt] = p[dt * 64];
+            acc.add(a.part_lse[st][sl * (16 * nt) + rr], x);
+        }
+    }
+    write_row<qd, D>(a, row, g, acc.M, acc.W, acc.acc);
+}
+
 template <int qd, int D>
 __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
+    if ((int)blockIdx.x >= a.max_splits) {
+        const int c = (int)blockIdx.x - a.max_splits;
+        if (c < a.hdr[HDR_NCAS]) merge_cascade<qd, D>(a, a.cas_recs[c]);
+        return;
+    }
     const SplitSeg sp = a.splits[blockIdx.x];
     if (sp.k0 < 0) return;  // past the list of cut segments
     const int lane = threadIdx.x;
@@ -939,10 +1158,10 @@ hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64
     }
 }
 
-hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t max_splits,
+hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t records,
                         hipStream_t s) {
-    if (max_splits <= 0) return hipSuccess;
-    const dim3 grid((unsigned)max_splits), block(64);
+    if (records <= 0) return hipSuccess;
+    const dim3 grid((unsigned)records), block(64);
     if (q_dtype == PA_F32 && head_dim == 64)
         hipLaunchKernelGGL((merge_kernel<PA_F32, 64>), grid, block, 0, s, a);
     else if (q_dtype == PA_F32 && head_dim == 128)

@@ -9,29 +9,41 @@
 
 namespace pa {
 
-// A tile: up to 16 query rows of one sequence (the G heads of `ntok`
-// consecutive query tokens of its span), and the number of 16-token key
-// blocks those rows need (causal: up to the tile's last query position;
-// at least one, so a tile with no keys still gets a wave that writes its
-// zero rows).
+// A tile: query rows and the 16-token key blocks they read.
+//  - span tile (flags 0): the G heads of `ntok` consecutive query tokens of
+//    one sequence's span; blocks 0 .. nb-1 (causal: up to the tile's last
+//    query position; at least one, so a tile with no keys still gets a wave
+//    that writes its zero rows).
+//  - suffix tile (TILE_SUFFIX): a single-token sequence in a shared-prefix
+//    group; blocks b0 .. b0+nb-1, the keys after the shared prefix.
+//  - group tile (TILE_GROUP): the single query tokens of up to `ntok`
+//    members of a shared-prefix group (group_members[qtok0 ..]), G rows
+//    each; blocks 0 .. nb-1 of the prefix, read once for all of them
+//    (cascade attention, "03 -- Engines Papers", section 12).
+enum { TILE_SUFFIX = 1, TILE_GROUP = 2 };
 struct TileDesc {
-    int32_t seq;
-    int32_t qtok0;  // first query token of the tile, relative to the span
-    int32_t ntok;   // query tokens in the tile
+    int32_t seq;    // the sequence whose block table the tile reads
+    int32_t qtok0;  // first query token of the tile, relative to the span;
+                    // group tile: first entry in group_members
+    int32_t ntok;   // query tokens in the tile (group tile: members)
     int32_t nb;     // key blocks the tile reads (>= 1)
-    int32_t L;      // the sequence's context length (clamped)
+    int32_t L;      // the sequence's context length (clamped); group tile:
+                    // 16 * nb, the prefix
     int32_t qs;     // the sequence's first query token row
     int32_t nspan;  // the sequence's query tokens
-    int32_t pad;
+    int32_t flags;  // TILE_SUFFIX, TILE_GROUP or 0
+    int32_t b0;     // first logical block
+    int32_t pad[3];
 };
 
-// Where a piece of the block stream begins: segment (tile, kv head), block j,
-// with a copy of that tile's record so a wave starts with one load.
+// Where a piece of the block stream begins: segment (tile, kv head), block j
+// (counted from the tile's b0), with a copy of that tile's record so a wave
+// starts with one load.
 struct PieceStart {
     int32_t tile;
     int32_t kvh;
     int32_t j;
-    int32_t pad[5];
+    int32_t pad;
     TileDesc td;
 };
 
@@ -65,6 +77,7 @@ constexpr int wide_tiles(int dtype) { return dtype == PA_F32 ? 2 : PA_WIDE_TILES
 enum {
     HDR_NTILES = 0,
     HDR_NSPLIT = 1,
+    HDR_NCAS = 2,  // cascade records
     HDR_STREAM = 4,
     HDR_TOTAL = 0,
     HDR_R = 1,
@@ -77,6 +90,25 @@ enum {
 enum { SLOT_HEAD = 0, SLOT_TAIL = 1 };
 
 constexpr int kMaxTiles = 8192;  // tiles per call (the plan keeps them in LDS)
+
+// A single-token sequence in a shared-prefix group, for one KV head: its G
+// rows combine two parts by log-sum-exp, the prefix (rows row_off .. of
+// group tile gtile) and the suffix (rows 0 .. of its suffix tile). A part
+// read whole by one piece was written to the dense per-row buffer of its
+// kind; a cut part lies in the slots of pieces k0 .. k1 of its stream's KV
+// head substream.
+struct CascadeRec {
+    int32_t row;     // the sequence's query token row
+    int32_t kvh;
+    int32_t suf_k0, suf_k1;
+    int32_t pre_k0, pre_k1;
+    int32_t pre_pos;  // the member's place in the group tile (rows pre_pos * G ..)
+    int32_t pad;
+};
+
+// Per-row buffers of whole cascade parts: [T * Hq] lse (log2 units) and
+// [T * Hq][D] normalized outputs, one pair for prefixes, one for suffixes.
+enum { CAS_PRE = 0, CAS_SUF = 1 };
 
 struct PlanArgs {
     const int32_t* context_lens;
@@ -96,6 +128,19 @@ struct PlanArgs {
     PieceStart* pieces[NUM_STREAMS];
     SplitSeg* splits;  // [max_pieces of both streams] segments the merge completes
     int32_t* hdr;
+    // shared-prefix groups (num_groups 0: none)
+    int32_t num_groups;
+    int32_t members_per_tile;  // single-token members per group tile
+    const int32_t* group_offsets;        // [num_groups + 1]
+    const int32_t* group_members;        // sequence ids
+    const int32_t* group_prefix_blocks;  // [num_groups]
+    int32_t* cas_prefix;  // [num_seqs] shared blocks of a cascade member, else 0
+    int32_t* cas_tile;    // [num_seqs] a member's suffix tile
+    int32_t* cas_gtile;   // [num_seqs] a member's group tile
+    int32_t* cas_pos;     // [num_seqs] a member's place in its group tile
+    int32_t* cas_members;  // [num_seqs] copy of group_members for the attention pass
+    CascadeRec* cas_recs;  // [num_seqs * Hkv]
+    int32_t max_cas_recs;
 };
 
 struct AttnArgs {
@@ -115,6 +160,11 @@ struct AttnArgs {
     int32_t stream;
     float* part_lse;  // [pieces][2][NT * 16], log2 units
     float* part_o;    // [pieces][2][NT][D/16][64 lanes] float4, normalized
+    const int32_t* group_members;  // group tiles' members (sequence ids, workspace copy)
+    const int32_t* cas_prefix;     // [num_seqs] shared blocks of a cascade member
+    float* cas_lse[2];             // CAS_PRE, CAS_SUF per-row buffers
+    float* cas_o[2];
+    int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t group;
@@ -134,6 +184,10 @@ struct MergeArgs {
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t group;
+    int32_t max_splits;  // workgroups [0, max_splits) complete cut segments
+    const CascadeRec* cas_recs;  // the rest combine cascade parts
+    const float* cas_lse[2];
+    const float* cas_o[2];
 };
 
 struct AppendArgs {
@@ -157,7 +211,8 @@ hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64
 // Waves of the attention kernel of a stream that fit on the device at once
 // (> 0), or 0 if the device cannot be queried.
 int resident_waves(int kv_dtype, int head_dim, int stream);
-hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t max_splits,
+// records: cut-segment workgroups (a.max_splits) plus cascade records
+hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t records,
                         hipStream_t s);
 hipError_t launch_append(int new_dtype, int kv_dtype, const AppendArgs& a, hipStream_t s);
 hipError_t launch_fp8_decode(const uint8_t* in, float* out, int n, hipStream_t s);

@@ -57,6 +57,7 @@ class Workload:
     partition_size: int  # split-KV partition in tokens (0 = library default)
     seed: int
     shared_groups: list = field(default_factory=list)  # lists of seqs sharing blocks
+    shared_prefix_blocks: list = field(default_factory=list)  # per group: shared leading blocks
     # explicit list of slots this step appends (defaults: every query token's slot)
     _slot_mapping: Optional[np.ndarray] = None
 
@@ -266,7 +267,7 @@ def _c4(seed: int, small: bool) -> Workload:
             cur += nb
     groups = [list(range(1, 1 + nshare))]
     return Workload("c4", 32, 8, 128, "bf16", "bf16", lens, qlens, bt, nblk, 512, seed,
-                    shared_groups=groups)
+                    shared_groups=groups, shared_prefix_blocks=[pb])
 
 
 def _c5(seed: int, small: bool) -> Workload:
@@ -296,7 +297,8 @@ def _c5(seed: int, small: bool) -> Workload:
         groups.append(members)
     lens = np.asarray(lens, dtype=np.int32)
     return Workload("c5", 64, 8, 128, "bf16", "fp8", lens, np.ones(len(lens), np.int32), bt,
-                    nblk, 0, seed, shared_groups=groups)
+                    nblk, 0, seed, shared_groups=groups,
+                    shared_prefix_blocks=[_blocks_for(int(L)) - 1 for L in glens])
 
 
 _BUILDERS = {"c1": _c1, "c2": _c2, "c3": _c3, "c4": _c4, "c5": _c5}

@@ -35,8 +35,11 @@ def dev_tensors(wl, vals, pre):
     return t
 
 
-def gpu_step(wl, t, *, partition_size=None, hybrid=None, with_lse=True, append=True):
-    """kv_append (in place on t's caches) then attention; returns (out, lse)."""
+def gpu_step(wl, t, *, partition_size=None, hybrid=None, with_lse=True, append=True,
+             groups=None):
+    """kv_append (in place on t's caches) then attention; returns (out, lse).
+    groups: (lists of sequences, shared prefix blocks per list) for cascade
+    attention."""
     if append:
         pa.kv_append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["slots"],
                      k_scale=t["k_scale"], v_scale=t["v_scale"])
@@ -44,7 +47,14 @@ def gpu_step(wl, t, *, partition_size=None, hybrid=None, with_lse=True, append=T
     lse = torch.empty(wl.num_tokens, wl.num_q_heads, dtype=torch.float32,
                       device="cuda") if with_lse else None
     use_hybrid = (not wl.is_decode) if hybrid is None else hybrid
-    if use_hybrid:
+    if groups is not None:
+        pg = pa.PrefixGroups(groups[0], groups[1], "cuda")
+        out = pa.cascade(t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], wl.scale, pg,
+                         max_context_len=wl.max_context_len,
+                         query_start_loc=t["qsl"] if use_hybrid else None,
+                         max_query_len=wl.max_query_len, k_scale=t["k_scale"],
+                         v_scale=t["v_scale"], partition_size=P, lse=lse)
+    elif use_hybrid:
         out = pa.hybrid(t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], t["qsl"], wl.scale,
                         max_context_len=wl.max_context_len, max_query_len=wl.max_query_len,
                         k_scale=t["k_scale"], v_scale=t["v_scale"], partition_size=P, lse=lse)
@@ -64,3 +74,27 @@ def prepare(wl, device="cuda"):
     vals = W.materialize(wl, device)
     pre = H.host_pre_append(wl, vals)
     return vals, pre
+
+
+def check_step(wl, partition_size=None, hybrid=None, seq_subset=None, groups=None):
+    """One step on the GPU against the oracle on the same inputs: the
+    per-element tolerance, the relative-RMS guard and the lse bound.
+    Returns (errors, device tensors, post-append host state)."""
+    import oracle
+    vals, pre = prepare(wl)
+    post = H.oracle_append(wl, pre)
+    t = dev_tensors(wl, vals, pre)
+    out, lse = gpu_step(wl, t, partition_size=partition_size, hybrid=hybrid, groups=groups)
+    ref, ref_lse = oracle.run_workload(wl, post, seq_subset=seq_subset)
+    got = out_f64(out)
+    got_lse = lse.cpu().numpy().astype(np.float64)
+    key = H.tolerance_key(wl)
+    if seq_subset is not None:
+        rows = np.concatenate([np.arange(wl.query_start_loc[i], wl.query_start_loc[i + 1])
+                               for i in seq_subset])
+        got, ref, got_lse, ref_lse = got[rows], ref[rows], got_lse[rows], ref_lse[rows]
+    e = H.assert_parity(got, ref, key, wl.name)
+    # lse in natural-log units, same tolerance form
+    le = np.max(np.abs(got_lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse)))
+    assert le <= H.TOL[key], f"lse error {le}"
+    return e, t, post

@@ -1,0 +1,122 @@
+"""Cascade attention on the GPU against the CPU oracle. Groups of
+single-token sequences that share the physical blocks of a prefix read it
+once, in group tiles, and each member reads only its own suffix; the two
+parts meet in the log-sum-exp merge ("03 -- Engines Papers", sections 2 and
+12). The result is the same attention, so the oracle and the tolerances
+are those of every other parity test."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_213_amd as pa
+from paged_kv_cache_213_amd import workloads as W
+from tests.gpu_common import check_step, dev_tensors, gpu_step, out_f64, prepare
+
+pytestmark = pytest.mark.gpu
+
+
+def _groups(wl):
+    return (wl.shared_groups, wl.shared_prefix_blocks)
+
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+@pytest.mark.parametrize("P", [None, 16, 0])
+def test_small_configs_with_groups(name, P):
+    """The sharing layouts of the hybrid batch (one 8-member group with an
+    8-block prefix) and of the parallel-sampling batch (4-member groups
+    sharing all but the last block); explicit tiny pieces cut every part."""
+    wl = W.make_config(name, small=True)
+    e, _, _ = check_step(wl, partition_size=P, groups=_groups(wl))
+    print(f"{name} small cascade P={P}: {e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_full_configs_with_groups_sampled(name):
+    """Full-size batches with their groups, balanced split (the bench's
+    launch configuration); the oracle checks sharers and non-sharers."""
+    wl = W.make_config(name)
+    grp = wl.shared_groups
+    pick = {0, wl.num_seqs - 1, grp[0][0], grp[0][-1], grp[-1][0], grp[-1][-1]}
+    pick |= set(int(i) for i in np.linspace(0, wl.num_seqs - 1, 5).astype(int))
+    e, _, _ = check_step(wl, partition_size=0, groups=_groups(wl),
+                         seq_subset=np.array(sorted(pick), np.int32))
+    print(f"{name} full cascade sampled: {e}", flush=True)
+
+
+def _group_batch(G, kv, q, seed, lens, prefix_len):
+    """Sequences 0..len-1 share the first prefix_len // 16 blocks."""
+    nb_pre = prefix_len // 16
+    wl = W.custom_workload(lens, num_q_heads=2 * G if G <= 8 else G, num_kv_heads=2 if G <= 8 else 1,
+                           head_dim=64, q_dtype=q, kv_dtype=kv, seed=seed)
+    shared = wl.block_tables[0, :nb_pre].copy()
+    for i in range(len(lens)):
+        wl.block_tables[i, :nb_pre] = shared
+    return wl, nb_pre
+
+
+@pytest.mark.parametrize("G,kv,q", [(4, "bf16", "bf16"), (8, "fp8", "bf16"), (16, "bf16", "bf16"),
+                                    (2, "f32", "f32")])
+def test_edge_groups(G, kv, q):
+    """Members whose context ends right after the prefix (a one-token
+    suffix), one member with no key past the prefix (it must read its
+    whole context itself), a one-member group, a group larger than one
+    group tile, and sequences in no group."""
+    lens = [16 * 6 + 1, 16 * 6 + 40, 16 * 6, 200, 16 * 6 + 16, 300, 121, 16 * 6 + 3]
+    wl, nb = _group_batch(G, kv, q, 11, lens, 96)
+    members = [0, 1, 2, 4, 7]  # 2 has no key past the prefix
+    groups = ([members, [5]], [nb, 3])
+    # sequence 5 shares nothing with others: give it a private 3-block prefix group of one
+    e, _, _ = check_step(wl, partition_size=0, groups=groups)
+    print(f"G={G} {kv}: {e}", flush=True)
+
+
+def test_hybrid_span_member_reads_whole_context():
+    """A chunked-prefill span listed in a group is not a cascade member: it
+    keeps its own tiles over its whole context, and the result is exact."""
+    lens = [160, 170, 180]
+    wl = W.custom_workload(lens, query_lens=[1, 20, 1], num_q_heads=8, num_kv_heads=2,
+                           head_dim=128, q_dtype="bf16", kv_dtype="bf16", seed=5)
+    shared = wl.block_tables[0, :8].copy()
+    for i in range(3):
+        wl.block_tables[i, :8] = shared
+    e, _, _ = check_step(wl, partition_size=0, groups=([[0, 1, 2]], [8]))
+    print(f"span member: {e}", flush=True)
+
+
+def test_cascade_agrees_with_plain_attention():
+    """The same batch with and without groups: both within tolerance of the
+    oracle, and of each other (they differ only in rounding order)."""
+    wl = W.make_config("c5", small=True)
+    vals, pre = prepare(wl)
+    t = dev_tensors(wl, vals, pre)
+    a, _ = gpu_step(wl, t, partition_size=0, groups=_groups(wl))
+    b, _ = gpu_step(wl, t, partition_size=0, append=False)
+    d = np.abs(out_f64(a) - out_f64(b)) / np.maximum(1.0, np.abs(out_f64(b)))
+    assert d.max() <= 3e-2, d.max()
+
+
+def test_plan_with_groups_is_reused_across_layers():
+    """One cascade plan serves two runs (two layers' caches) bitwise the
+    same as planning each time."""
+    wl = W.make_config("c5", small=True)
+    vals, pre = prepare(wl)
+    t = dev_tensors(wl, vals, pre)
+    pa.kv_append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["slots"],
+                 k_scale=t["k_scale"], v_scale=t["v_scale"])
+    pg = pa.PrefixGroups(wl.shared_groups, wl.shared_prefix_blocks, "cuda")
+    shape = pa.make_shape(t["q"], t["k_cache"], t["bt"], 0, cascade=True)
+    nbytes = pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len, 1)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    pa.plan_cascade(shape, t["cl"], ws, pg, num_q_tokens=wl.num_tokens, max_query_len=1,
+                    max_context_len=wl.max_context_len)
+    outs = []
+    for _ in range(2):
+        outs.append(pa.run(shape, t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], wl.scale,
+                           ws, max_query_len=1, max_context_len=wl.max_context_len,
+                           k_scale=t["k_scale"], v_scale=t["v_scale"]))
+    ref = pa.cascade(t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], wl.scale, pg,
+                     max_context_len=wl.max_context_len, k_scale=t["k_scale"],
+                     v_scale=t["v_scale"])
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), ref.view(torch.int16))

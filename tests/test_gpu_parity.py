@@ -10,29 +10,13 @@ import oracle
 import paged_kv_cache_213_amd as pa
 from paged_kv_cache_213_amd import workloads as W
 from tests import helpers as H
-from tests.gpu_common import dev_tensors, gpu_step, out_f64, prepare
+from tests.gpu_common import check_step, dev_tensors, gpu_step, out_f64, prepare
 
 pytestmark = pytest.mark.gpu
 
 
 def _check_step(wl, partition_size=None, hybrid=None, seq_subset=None):
-    vals, pre = prepare(wl)
-    post = H.oracle_append(wl, pre)
-    t = dev_tensors(wl, vals, pre)
-    out, lse = gpu_step(wl, t, partition_size=partition_size, hybrid=hybrid)
-    ref, ref_lse = oracle.run_workload(wl, post, seq_subset=seq_subset)
-    got = out_f64(out)
-    got_lse = lse.cpu().numpy().astype(np.float64)
-    key = H.tolerance_key(wl)
-    if seq_subset is not None:
-        rows = np.concatenate([np.arange(wl.query_start_loc[i], wl.query_start_loc[i + 1])
-                               for i in seq_subset])
-        got, ref, got_lse, ref_lse = got[rows], ref[rows], got_lse[rows], ref_lse[rows]
-    e = H.assert_parity(got, ref, key, wl.name)
-    # lse in natural-log units, same tolerance form
-    le = np.max(np.abs(got_lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse)))
-    assert le <= H.TOL[key], f"lse error {le}"
-    return e, t, post
+    return check_step(wl, partition_size=partition_size, hybrid=hybrid, seq_subset=seq_subset)
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
