@@ -116,10 +116,10 @@ def attention_source_sha256() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(config: str):
+def recorded_traffic(config: str, cascade: bool):
     """HBM bytes per attention launch recorded by the profiler counters for
-    this workload (profiles/), or None when none are recorded or the
-    attention source has changed since they were taken."""
+    this workload and method (profiles/), or None when none are recorded or
+    the attention source has changed since they were taken."""
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                         PROFILE_FILES.get(config, ""))
     if not os.path.isfile(path):
@@ -128,12 +128,37 @@ def recorded_traffic(config: str):
     with open(path) as fh:
         for line in fh:
             k, sep, v = line.partition(":")
-            if sep and k in ("traffic_bytes_per_launch", "attention_source_sha256"):
+            if sep and k in ("traffic_bytes_per_launch", "attention_source_sha256", "cascade"):
                 fields[k] = v.strip()
     if fields.get("attention_source_sha256") != attention_source_sha256():
         return None
+    if fields.get("cascade", "off") != ("on" if cascade else "off"):
+        return None
     t = fields.get("traffic_bytes_per_launch")
     return int(t) if t and t.isdigit() else None
+
+
+def cascade_read_bytes(wl, members_per_tile: int) -> int:
+    """K/V bytes cascade attention reads: each group tile reads its group's
+    prefix once, each member with keys past the prefix reads only those,
+    everything else its whole context (same per-token bytes as the logical
+    count, whole prefix blocks)."""
+    per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.kv_elem_bytes
+    L = wl.context_lens.astype(np.int64)
+    toks = int(L.sum())
+    blocks = int(((L + 15) // 16).sum())
+    for grp, pb in zip(wl.shared_groups, wl.shared_prefix_blocks):
+        tiles = -(-len(grp) // members_per_tile)
+        toks += tiles * 16 * pb
+        blocks += tiles * pb
+        for i in grp:
+            if int(wl.query_lens[i]) == 1 and int(L[i]) > 16 * pb:
+                toks -= 16 * pb
+                blocks -= pb
+    b = toks * per_tok
+    if wl.kv_dtype == "fp8":
+        b += blocks * wl.num_kv_heads * 2 * 4
+    return b
 
 
 def stream_read_probe(pa, torch, dev, mib: int = 4096, reps: int = 10) -> float:
@@ -171,6 +196,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
+    ap.add_argument("--cascade", choices=("auto", "on", "off"), default="auto",
+                    help="read shared prefixes once per group (auto: when the workload's "
+                         "sequences share prefix blocks)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run the library's plain copy kernel over this many MiB, a "
                          "kernel of known traffic for calibrating profiler byte counters")
@@ -227,14 +255,22 @@ def main():
     qsl = None if wl.is_decode else torch.from_numpy(wl.query_start_loc).to(dev)
     slots = torch.from_numpy(wl.slot_mapping).to(dev)
     lse = torch.empty(wl.num_tokens, wl.num_q_heads, dtype=torch.float32, device=dev)
-    shape = pa.make_shape(vals.q, vals.k_cache, bt, P)
+    use_cascade = args.cascade == "on" or (args.cascade == "auto" and bool(wl.shared_groups))
+    shape = pa.make_shape(vals.q, vals.k_cache, bt, P, cascade=use_cascade)
+    groups = pa.PrefixGroups(wl.shared_groups, wl.shared_prefix_blocks, dev) if use_cascade \
+        else None
     nbytes = pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len,
                                 wl.max_query_len)
     ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
     mq = 1 if wl.is_decode else wl.max_query_len
     def model_step(stream):
-        pa.plan(shape, cl, ws, query_start_loc=qsl, num_q_tokens=wl.num_tokens,
-                max_query_len=mq, max_context_len=wl.max_context_len, stream=stream)
+        if groups is not None:
+            pa.plan_cascade(shape, cl, ws, groups, query_start_loc=qsl,
+                            num_q_tokens=wl.num_tokens, max_query_len=mq,
+                            max_context_len=wl.max_context_len, stream=stream)
+        else:
+            pa.plan(shape, cl, ws, query_start_loc=qsl, num_q_tokens=wl.num_tokens,
+                    max_query_len=mq, max_context_len=wl.max_context_len, stream=stream)
         for L_ in range(layers):
             pa.kv_append(kc[L_], vc[L_], vals.k_new, vals.v_new, slots, k_scale=k_scale,
                          v_scale=v_scale, stream=stream)
@@ -244,6 +280,15 @@ def main():
             pa.run(shape, qs[L_], kc[L_], vc[L_], bt, cl, wl.scale, ws, query_start_loc=qsl,
                    max_query_len=mq, max_context_len=wl.max_context_len, out=outs[L_],
                    lse=lse, stream=stream, passes="merge")
+
+    def model_step_plan(stream):
+        if groups is not None:
+            pa.plan_cascade(shape, cl, ws, groups, query_start_loc=qsl,
+                            num_q_tokens=wl.num_tokens, max_query_len=mq,
+                            max_context_len=wl.max_context_len, stream=stream)
+        else:
+            pa.plan(shape, cl, ws, query_start_loc=qsl, num_q_tokens=wl.num_tokens,
+                    max_query_len=mq, max_context_len=wl.max_context_len, stream=stream)
 
     if args.calibrate_copy_mib > 0:
         nb = args.calibrate_copy_mib << 20
@@ -326,15 +371,18 @@ def main():
         shape, qs[L_], kc[L_], vc[L_], bt, cl, wl.scale, ws, query_start_loc=qsl,
         max_query_len=mq, max_context_len=wl.max_context_len, out=outs[L_], lse=lse, stream=s,
         passes="merge"))
-    plan_us = back_to_back_us(lambda L_: pa.plan(
-        shape, cl, ws, query_start_loc=qsl, num_q_tokens=wl.num_tokens, max_query_len=mq,
-        max_context_len=wl.max_context_len, stream=s))
+    plan_us = back_to_back_us(lambda L_: model_step_plan(s))
     probe_gbs = stream_read_probe(pa, torch, dev)
     ms_per_step = wall * 1e3 / args.steps
     kv_bytes = wl.kv_bytes_logical()
     value = layers * kv_bytes / (ms_per_step / 1e3) / 1e9
     att_mean = float(att_ms.mean())
-    achieved = kv_bytes / (att_mean / 1e3) / 1e9
+    # the roofline counts what the method must read: the logical bytes, or
+    # with cascade the group prefixes once per group tile
+    G = wl.num_q_heads // wl.num_kv_heads
+    mpt = max(1, (16 * (2 if wl.kv_dtype == "f32" else 4)) // G)
+    read_bytes = cascade_read_bytes(wl, mpt) if use_cascade else kv_bytes
+    achieved = read_bytes / (att_mean / 1e3) / 1e9
     layer_ms = ms_per_step / layers
     res = {
         "metric": METRIC,
@@ -366,6 +414,9 @@ def main():
             "layers_per_step": layers,
             "partition_size": P,
             "graph": graph is not None,
+            "cascade": use_cascade,
+            "kv_bytes_read_per_layer": read_bytes,
+            "kv_bytes_unique_per_layer": wl.kv_bytes_unique() if wl.shared_groups else kv_bytes,
             "seed": wl.seed,
         },
         "roofline": {
@@ -374,7 +425,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": recorded_traffic(wl.name),
+            "traffic": recorded_traffic(wl.name, use_cascade),
             "traffic_note": "HBM bytes per attention pass launch (calibrated FETCH_SIZE + "
                             "WRITE_SIZE, profiles/); null if not recorded for the current "
                             "attention source",

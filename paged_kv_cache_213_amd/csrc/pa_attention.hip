@@ -282,6 +282,30 @@ struct Tile<KV_FP8, D> {
         }
         return acc;
     }
+    // The bf16 image of the block (exact), for tiles whose K and V serve
+    // several row tiles: converted once, not once per row tile. K step m of
+    // the image holds dims 64(m/2) + 16g + 8(m%2) + e, the order of qk()
+    // below and of the fp8 q operand.
+    __device__ __forceinline__ Tile<KV_BF16, D> to_bf16() const {
+        Tile<KV_BF16, D> b;
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) {
+            const uint32_t w[4] = {k[j].x, k[j].y, k[j].z, k[j].w};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                b.k[2 * j + h].x = fp8x2_to_bf16x2<false>(w[2 * h]);
+                b.k[2 * j + h].y = fp8x2_to_bf16x2<true>(w[2 * h]);
+                b.k[2 * j + h].z = fp8x2_to_bf16x2<false>(w[2 * h + 1]);
+                b.k[2 * j + h].w = fp8x2_to_bf16x2<true>(w[2 * h + 1]);
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            b.v[dt].x = fp8x2_to_bf16x2<false>(v[dt]);
+            b.v[dt].y = fp8x2_to_bf16x2<true>(v[dt]);
+        }
+        return b;
+    }
     __device__ __forceinline__ void mask_v(int nvalid) {
         const uint32_t m =
             nvalid >= 4 ? 0xffffffffu : (nvalid <= 0 ? 0u : ((1u << (8 * nvalid)) - 1u));
@@ -597,7 +621,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 #ifndef PA_PREFETCH
 #define PA_PREFETCH 1
 #endif
-constexpr int PF = PA_PREFETCH;  // K/V blocks in flight per wave beyond the one in use
+// K/V blocks in flight per wave beyond the one in use: the narrow kernel
+// hides latency with two waves per SIMD; the wide kernel runs one wave per
+// SIMD with registers to spare, and its group tiles stream long prefixes.
+#ifndef PA_WIDE_PREFETCH
+#define PA_WIDE_PREFETCH 1
+#endif
 
 // Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
 // each block through the block table, S = K q^T on the matrix cores, online
@@ -619,6 +648,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     const int seq = td.seq;
     const int L = td.L, qs = td.qs, nspan = td.nspan;
     const int nrows = td.ntok * G;
+    const int nrt = (nrows + 15) >> 4;  // row tiles holding rows
 
     // this lane's query row in row tile r: tile row 16 r + n = token qj,
     // head kvh*G + (row % G)
@@ -706,7 +736,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             }
         }
         // per-block work on block i of the chunk
-        auto consume = [&](T& cur, int i) {
+        auto consume_tile = [&](auto& cur, int i) {
             const int jb = td.b0 + j + c0 + i;  // logical block
             const int t0 = jb * 16 + 4 * g;  // my first token in it
             const bool full = jb * 16 + 15 <= pos_first;  // wave-uniform
@@ -721,6 +751,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             typename std::conditional<kv == KV_F32, float[NT][4], s16x4[NT]>::type pk;
 #pragma unroll
             for (int r = 0; r < NT; ++r) {
+                if (r >= nrt) break;  // row tiles without rows (wave-uniform)
                 const f32x4 sc = cur.qk(qreg[r]);
                 float x[4];  // scores relative to the reference
 #pragma unroll
@@ -760,12 +791,22 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             // zero V slots past the context (NaN there must not reach P.V)
             if (!full) cur.mask_v(L - t0);
 #pragma unroll
-            for (int r = 0; r < NT; ++r) cur.pv(pk[r], o[r]);
+            for (int r = 0; r < NT; ++r)
+                if (r < nrt) cur.pv(pk[r], o[r]);
+        };
+        auto consume = [&](T& cur, int i) {
+            if constexpr (kv == KV_FP8 && NT > 1) {
+                auto cb = cur.to_bf16();
+                consume_tile(cb, i);
+            } else {
+                consume_tile(cur, i);
+            }
         };
         auto fetch = [&](T& dst, int i) {
             const int ph = __builtin_amdgcn_readlane(my_phys, i);
             dst.template load<kStreamLoads>(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
         };
+        constexpr int PF = NT == 1 ? PA_PREFETCH : PA_WIDE_PREFETCH;
         // ring of PF + 1 register tiles: PF blocks stay in flight while one is
         // consumed. In the steady-state loop every refill is in range, so it
         // is straight-line code in which each wait covers exactly one block;
@@ -974,12 +1015,22 @@ __device__ __forceinline__ void merge_cascade(const MergeArgs& a, const CascadeR
         const int nt = st == STREAM_WIDE ? wide_tiles(qd) : 1;
         const int rr = (kind == CAS_PRE ? rc.pre_pos * G : 0) + n;  // row in the slot
         const float4* po = (const float4*)a.part_o[st];
-        for (int k = k0; k <= k1; ++k) {
-            const int64_t sl = ((int64_t)k * Hkv + rc.kvh) * 2 + (k == k0 ? SLOT_TAIL : SLOT_HEAD);
-            const float4* p = po + ((sl * nt + rr / 16) * (D / 16)) * 64 + (rr % 16) + 16 * g;
+        // four pieces per round trip: all their loads are issued first
+        for (int kb = k0; kb <= k1; kb += 4) {
+            float l4[4];
+            float4 x4[4][D / 16];
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) x[dt] = p[dt * 64];
-            acc.add(a.part_lse[st][sl * (16 * nt) + rr], x);
+            for (int u = 0; u < 4; ++u) {
+                const int k = min(kb + u, k1);
+                const int64_t sl =
+                    ((int64_t)k * Hkv + rc.kvh) * 2 + (k == k0 ? SLOT_TAIL : SLOT_HEAD);
+                const float4* p = po + ((sl * nt + rr / 16) * (D / 16)) * 64 + (rr % 16) + 16 * g;
+#pragma unroll
+                for (int dt = 0; dt < D / 16; ++dt) x4[u][dt] = p[dt * 64];
+                l4[u] = kb + u <= k1 ? a.part_lse[st][sl * (16 * nt) + rr] : -INFINITY;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc.add(l4[u], x4[u]);
         }
     }
     write_row<qd, D>(a, row, g, acc.M, acc.W, acc.acc);

@@ -218,7 +218,12 @@ hipError_t launch_append(int new_dtype, int kv_dtype, const AppendArgs& a, hipSt
 hipError_t launch_fp8_decode(const uint8_t* in, float* out, int n, hipStream_t s);
 
 // Smallest piece (in 16-token blocks) when pieces are balanced over the
-// resident waves: tiny batches are not shredded into one-block pieces.
-constexpr int kMinPieceBlocks = 8;
+// resident waves. One block: a wave that walked several short segments one
+// after another (one-block suffixes of cascade members, say) would pay a
+// chain of dependent loads for each, while other waves idle.
+#ifndef PA_MIN_PIECE_BLOCKS
+#define PA_MIN_PIECE_BLOCKS 1
+#endif
+constexpr int kMinPieceBlocks = PA_MIN_PIECE_BLOCKS;
 
 }  // namespace pa
