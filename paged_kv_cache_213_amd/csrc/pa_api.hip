@@ -36,7 +36,7 @@ struct Layout {
     bool cascade = false;
     int members_per_tile = 0;
     int64_t max_cas_recs = 0;
-    size_t off_cas_seq = 0;  // 5 int arrays of num_seqs
+    size_t off_cas_seq = 0;  // 6 int arrays of num_seqs
     size_t off_cas_recs = 0;
     size_t off_cas_lse[2] = {0, 0}, off_cas_o[2] = {0, 0};
 };
@@ -114,7 +114,7 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
         const size_t rows = (size_t)num_tokens * s->num_q_heads;
         l.max_cas_recs = (int64_t)num_seqs * s->num_kv_heads;
         l.off_cas_seq = off;
-        off = align_up(off + sizeof(int32_t) * 5 * (size_t)num_seqs);
+        off = align_up(off + sizeof(int32_t) * 6 * (size_t)num_seqs);
         l.off_cas_recs = off;
         off = align_up(off + sizeof(pa::CascadeRec) * (size_t)l.max_cas_recs);
         for (int k = 0; k < 2; ++k) {
@@ -223,6 +223,7 @@ int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl
         pl.cas_gtile = cs + 2 * (size_t)num_seqs;
         pl.cas_pos = cs + 3 * (size_t)num_seqs;
         pl.cas_members = cs + 4 * (size_t)num_seqs;
+        pl.cas_gbase = cs + 5 * (size_t)num_seqs;
         pl.cas_recs = (pa::CascadeRec*)(ws + l.off_cas_recs);
         pl.max_cas_recs = (int32_t)l.max_cas_recs;
     }

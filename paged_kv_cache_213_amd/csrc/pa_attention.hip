@@ -389,6 +389,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     // 0. shared-prefix groups: a single-token member whose context extends
     //    past the group's prefix reads the prefix through its group's tiles
     //    and only the rest itself (cascade attention)
+    // member entries and the group of an entry (the last group whose first
+    // entry is at or before it)
+    const int num_entries =
+        a.num_groups > 0 ? min(max(a.group_offsets[a.num_groups], 0), S) : 0;
+    auto group_of = [&](int e) {
+        int lo = 0, hi = a.num_groups - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (a.group_offsets[mid] <= e) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+    };
     if (a.num_groups > 0) {
         for (int i = threadIdx.x; i < S; i += kPlanThreads) {
             a.cas_prefix[i] = 0;
@@ -400,18 +412,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             a.cas_members[i] = i < a.group_offsets[a.num_groups] ? a.group_members[i] : -1;
         }
         __syncthreads();
-        for (int g = threadIdx.x; g < a.num_groups; g += kPlanThreads) {
+        // one thread per member entry (the groups of a batch can be large)
+        for (int e = threadIdx.x; e < num_entries; e += kPlanThreads) {
+            const int g = group_of(e);
             const int pb = a.group_prefix_blocks[g];
-            const int e0 = a.group_offsets[g], e1 = a.group_offsets[g + 1];
-            const int lead = e1 > e0 ? a.group_members[e0] : -1;  // its table is read
-            if (pb < 1 || lead < 0 || lead >= S) continue;
-            for (int e = e0; e < e1; ++e) {
-                const int i = a.group_members[e];
-                if (i < 0 || i >= S) continue;
-                int qs, n, L;
-                span_of(i, qs, n, L);
-                if (n == 1 && L > 16 * pb) a.cas_prefix[i] = pb;
-            }
+            const int lead = a.group_members[a.group_offsets[g]];  // its table is read
+            const int i = a.group_members[e];
+            if (pb < 1 || lead < 0 || lead >= S || i < 0 || i >= S) continue;
+            int qs, n, L;
+            span_of(i, qs, n, L);
+            if (n == 1 && L > 16 * pb) a.cas_prefix[i] = pb;
         }
         __syncthreads();
     }
@@ -467,6 +477,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                 }
                 int total;
                 const int off = tile_base + block_exclusive_scan(ntl, &total);
+                if (g < a.num_groups) a.cas_gbase[g] = ntl > 0 ? off : -1;
                 for (int k = 0; k < ntl; ++k) {
                     const int t = off + k;
                     if (t >= cap) break;
@@ -474,15 +485,24 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                     a.tiles[t] = TileDesc{lead, e0 + m0, mn, pb, 16 * pb, 0, 1, TILE_GROUP, 0,
                                           {0, 0, 0}};
                     s_tp[t] = pb;
-                    for (int m = 0; m < mn; ++m) {
-                        const int i = a.group_members[e0 + m0 + m];
-                        if (i >= 0 && i < S && a.cas_prefix[i] == pb) {
-                            a.cas_gtile[i] = t;
-                            a.cas_pos[i] = m;
-                        }
-                    }
                 }
                 tile_base += total;
+            }
+            __syncthreads();
+            // each qualifying member's group tile and place in it
+            for (int e = threadIdx.x; e < num_entries; e += kPlanThreads) {
+                const int g = group_of(e);
+                const int base = a.cas_gbase[g];
+                const int i = a.group_members[e];
+                if (base < 0 || i < 0 || i >= S ||
+                    a.cas_prefix[i] != a.group_prefix_blocks[g])
+                    continue;
+                const int m = e - a.group_offsets[g];
+                const int t = base + m / mpt;
+                if (t < cap) {
+                    a.cas_gtile[i] = t;
+                    a.cas_pos[i] = m % mpt;
+                }
             }
         }
         if (st == STREAM_WIDE) nwide = min(tile_base, cap);

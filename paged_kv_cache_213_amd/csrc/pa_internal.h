@@ -139,6 +139,7 @@ struct PlanArgs {
     int32_t* cas_gtile;   // [num_seqs] a member's group tile
     int32_t* cas_pos;     // [num_seqs] a member's place in its group tile
     int32_t* cas_members;  // [num_seqs] copy of group_members for the attention pass
+    int32_t* cas_gbase;    // [num_seqs] a group's first tile (-1: none)
     CascadeRec* cas_recs;  // [num_seqs * Hkv]
     int32_t max_cas_recs;
 };
