@@ -77,13 +77,14 @@ typedef enum pa_status {
  * head_dim in {64, 128}; block_size == 16; Hq % Hkv == 0 with
  * G = Hq / Hkv <= 16; (q_dtype, kv_dtype) in {(F32, F32), (BF16, BF16),
  * (BF16, FP8_E4M3FN)}; partition_size 0 (split each call's key blocks into
- * equal pieces, one per resident wave, at least 128 tokens each) or a
+ * equal pieces, one per resident wave) or a
  * positive multiple of 16 (pieces of that many tokens). Query rows are
  * grouped into tiles: a span of at most 16 / G tokens (every decode) is one
  * narrow tile of G * n_i rows; a longer span is cut into wide tiles of
  * 64 / G tokens (32 / G for F32). A call may hold at most 8192 tiles,
  * counted as 2 * num_seqs + ceil(num_q_tokens / (64 / G)) for a hybrid call
- * and num_seqs for a decode call; beyond that it returns PA_ENOTSUP. */
+ * and num_seqs for a decode call, plus 2 * num_seqs when cascade is 1;
+ * beyond that it returns PA_ENOTSUP. */
 typedef struct pa_shape {
     int32_t num_q_heads;        /* Hq */
     int32_t num_kv_heads;       /* Hkv */
