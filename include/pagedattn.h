@@ -70,7 +70,8 @@ typedef enum pa_status {
     PA_EINVAL = -1,     /* bad pointer, shape, dtype combination or size */
     PA_EWORKSPACE = -2, /* workspace NULL or smaller than pa_workspace_bytes */
     PA_EHIP = -3,       /* a HIP runtime call or kernel launch failed */
-    PA_ENOTSUP = -4     /* valid request this build does not implement */
+    PA_ENOTSUP = -4,    /* valid request this build does not implement */
+    PA_ENOMEM = -5      /* no free physical block (block manager) */
 } pa_status;
 
 /* Problem shape shared by all calls on one cache. Supported today:

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "pa_internal.h"
+#include "pagedattn_blocks.h"
 
 #ifndef PA_WIDE_SPANS
 #define PA_WIDE_SPANS 1
@@ -457,6 +458,30 @@ int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream) {
                                                                                 : PA_EHIP;
 }
 
+int pa_copy_blocks(const pa_shape* shape, void* k_cache, void* v_cache, float* k_scale,
+                   float* v_scale, const int32_t* pairs, int num_pairs, void* stream) {
+    int rc = check_shape(shape);
+    if (rc != PA_OK) return rc;
+    if (num_pairs < 0) return PA_EINVAL;
+    if (num_pairs == 0) return PA_OK;
+    if (!k_cache || !v_cache || !pairs || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_EINVAL;
+    const bool fp8 = shape->kv_dtype == PA_FP8_E4M3FN;
+    if (fp8 && (!k_scale || !v_scale)) return PA_EINVAL;
+    const int eb = shape->kv_dtype == PA_F32 ? 4 : shape->kv_dtype == PA_BF16 ? 2 : 1;
+    pa::CopyArgs ca{};
+    ca.k_cache = k_cache;
+    ca.v_cache = v_cache;
+    ca.k_scale = fp8 ? k_scale : nullptr;
+    ca.v_scale = fp8 ? v_scale : nullptr;
+    ca.pairs = pairs;
+    ca.block_bytes = (int64_t)shape->num_kv_heads * PA_BLOCK_SIZE * shape->head_dim * eb;
+    ca.num_blocks = shape->num_blocks;
+    ca.num_kv_heads = shape->num_kv_heads;
+    return pa::launch_copy_blocks(ca, num_pairs, (hipStream_t)stream) == hipSuccess ? PA_OK
+                                                                                  : PA_EHIP;
+}
+
 const char* pa_status_string(int status) {
     switch (status) {
     case PA_OK: return "ok";
@@ -464,6 +489,7 @@ const char* pa_status_string(int status) {
     case PA_EWORKSPACE: return "workspace missing or too small";
     case PA_EHIP: return "HIP runtime or launch error";
     case PA_ENOTSUP: return "not supported";
+    case PA_ENOMEM: return "no free block";
     default: return "unknown status";
     }
 }

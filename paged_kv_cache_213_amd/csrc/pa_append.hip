@@ -67,7 +67,35 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     }
 }
 
+// Copy-on-write copies: one workgroup per (source, destination) pair moves
+// the whole block, K and V of every KV head (16-byte words), and its scales.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
+    const int32_t src = a.pairs[2 * blockIdx.x], dst = a.pairs[2 * blockIdx.x + 1];
+    if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+    const int64_t words = a.block_bytes / 16;  // per cache
+    const uint4* ks = (const uint4*)a.k_cache + src * words;
+    const uint4* vs = (const uint4*)a.v_cache + src * words;
+    uint4* kd = (uint4*)a.k_cache + dst * words;
+    uint4* vd = (uint4*)a.v_cache + dst * words;
+    for (int64_t i = threadIdx.x; i < words; i += blockDim.x) {
+        kd[i] = ks[i];
+        vd[i] = vs[i];
+    }
+    if (a.k_scale && (int)threadIdx.x < a.num_kv_heads) {
+        a.k_scale[(int64_t)dst * a.num_kv_heads + threadIdx.x] =
+            a.k_scale[(int64_t)src * a.num_kv_heads + threadIdx.x];
+        a.v_scale[(int64_t)dst * a.num_kv_heads + threadIdx.x] =
+            a.v_scale[(int64_t)src * a.num_kv_heads + threadIdx.x];
+    }
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s) {
+    if (num_pairs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_append(int new_dtype, int kv_dtype, const AppendArgs& a, hipStream_t s) {
     const int64_t total = (int64_t)a.num_tokens * a.num_kv_heads * a.head_dim;

@@ -205,6 +205,17 @@ struct AppendArgs {
     int32_t num_blocks;
 };
 
+struct CopyArgs {
+    void* k_cache;
+    void* v_cache;
+    float* k_scale;  // nullptr unless fp8
+    float* v_scale;
+    const int32_t* pairs;  // [num_pairs][2] source, destination
+    int64_t block_bytes;   // bytes of one block in one cache (all KV heads)
+    int32_t num_blocks;
+    int32_t num_kv_heads;
+};
+
 // Launchers (host side), defined next to their kernels.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64_t max_pieces,
@@ -216,6 +227,7 @@ int resident_waves(int kv_dtype, int head_dim, int stream);
 hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t records,
                         hipStream_t s);
 hipError_t launch_append(int new_dtype, int kv_dtype, const AppendArgs& a, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);
 hipError_t launch_fp8_decode(const uint8_t* in, float* out, int n, hipStream_t s);
 
 // Smallest piece (in 16-token blocks) when pieces are balanced over the
