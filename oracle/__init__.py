@@ -73,7 +73,7 @@ def _load():
         lib.or_kv_append.restype = I
         lib.or_kv_append.argtypes = [I, I, I, I, P, P, P, P, P, P, P, I]
         lib.or_paged_attention.restype = I
-        lib.or_paged_attention.argtypes = [I, I, I, I, P, I, P, P, I, P, P, P, I, P, P, F, P, I,
+        lib.or_paged_attention.argtypes = [I, I, I, I, P, I, P, P, I, P, P, P, I, P, P, F, P, P, I,
                                            P, P, I]
         lib.or_paged_attention_split.restype = I
         lib.or_paged_attention_split.argtypes = [I, I, I, I, P, I, P, P, I, P, P, P, I, P, P, F,
@@ -139,9 +139,10 @@ def kv_append(k_cache, v_cache, k_new, v_new, slot_mapping, *, kv_dtype, new_dty
 
 def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale, *, q_dtype,
                     kv_dtype, num_q_heads, num_kv_heads, head_dim, query_start_loc=None,
-                    k_scale=None, v_scale=None, seq_subset=None, threads=0):
+                    k_scale=None, v_scale=None, seq_subset=None, threads=0, tree_mask=None):
     """Return (out [T][Hq][D], lse [T][Hq]) in float64. Rows of sequences
-    outside ``seq_subset`` are NaN."""
+    outside ``seq_subset`` are NaN. tree_mask [T] uint64 (or None): tree
+    verification masks of spans of at most 64 tokens."""
     qa = _c(q, _NP[q_dtype])
     kc = _c(k_cache, _NP[kv_dtype])
     vc = _c(v_cache, _NP[kv_dtype])
@@ -150,6 +151,7 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale, *, q
     qsl = _c(query_start_loc, np.int32)
     ks, vs = _c(k_scale, np.float32), _c(v_scale, np.float32)
     sub = _c(seq_subset, np.int32)
+    tm = _c(tree_mask, np.uint64)
     S = cl.shape[0]
     T = int(qsl[-1]) if qsl is not None else S
     out = np.full((T, num_q_heads, head_dim), np.nan, dtype=np.float64)
@@ -157,7 +159,8 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale, *, q
     rc = _load().or_paged_attention(S, num_q_heads, num_kv_heads, head_dim, _ptr(qa),
                                     _DT[q_dtype], _ptr(kc), _ptr(vc), _DT[kv_dtype], _ptr(ks),
                                     _ptr(vs), _ptr(bt), bt.shape[1], _ptr(cl), _ptr(qsl),
-                                    float(scale), _ptr(sub), 0 if sub is None else sub.size,
+                                    float(scale), _ptr(tm), _ptr(sub),
+                                    0 if sub is None else sub.size,
                                     _ptr(out), _ptr(lse), int(threads))
     if rc != 0:
         raise ValueError(f"or_paged_attention failed ({rc})")
@@ -191,7 +194,7 @@ def paged_attention_split(q, k_cache, v_cache, block_tables, context_lens, scale
 
 # ---- convenience: run the oracle on a workload's host arrays --------------
 
-def run_workload(wl, host, seq_subset=None, threads=0):
+def run_workload(wl, host, seq_subset=None, threads=0, tree_mask=None):
     """``host``: dict of numpy arrays q, k_cache, v_cache (post-append) and,
     for fp8, k_scale, v_scale, as produced by the test helpers."""
     qsl = None if wl.is_decode else wl.query_start_loc
@@ -200,4 +203,4 @@ def run_workload(wl, host, seq_subset=None, threads=0):
                            num_q_heads=wl.num_q_heads, num_kv_heads=wl.num_kv_heads,
                            head_dim=wl.head_dim, query_start_loc=qsl,
                            k_scale=host.get("k_scale"), v_scale=host.get("v_scale"),
-                           seq_subset=seq_subset, threads=threads)
+                           seq_subset=seq_subset, threads=threads, tree_mask=tree_mask)

@@ -23,6 +23,12 @@
  *   - The online softmax normalizer (Milakov & Gimelshein, "References")
  *     reaches exactly this softmax; the oracle does not use it: it takes
  *     the max, the exponentials and their sum in separate passes.
+ *   - Tree verification of speculative candidates ("03 -- Engines Papers",
+ *     sections 5 to 7: the draft tokens of a span are nodes of a candidate
+ *     tree verified in one pass under a tree attention mask): with a tree
+ *     mask, span token j of a span of at most 64 tokens sees every key
+ *     before the span and span token k <= j only where bit k of its mask
+ *     word is set. Spans of more than 64 tokens stay causal.
  *   - FP8 E4M3 KV with a scale ("The LLM inference engine playbook",
  *     Themes 3 and 6): a stored byte means e4m3fn(byte) * scale, with one
  *     fp32 scale per (block, KV head).
@@ -193,6 +199,7 @@ typedef struct {
     const int32_t* context_lens;
     const int32_t* query_start_loc;
     float scale;
+    const uint64_t* tree_mask; /* [T] or NULL: causal spans */
 } or_args;
 
 static double or_q_at(const or_args* a, long idx) {
@@ -226,18 +233,23 @@ static void or_gather(const or_args* a, int i, int g, int L, double* K, double* 
     }
 }
 
-/* Softmax attention of one query row over keys 0..nk-1 of gathered K/V. */
+/* Softmax attention of one query row over the keys 0..nk-1 of gathered
+ * K/V for which vis[t] is nonzero (vis NULL: all of them). */
 static void or_attend_row(const or_args* a, long qrow, int h, const double* K, const double* V,
-                          int nk, double* s, double* out, double* lse) {
+                          int nk, const unsigned char* vis, double* s, double* out,
+                          double* lse) {
     const int D = a->head_dim;
     const double scale = (double)a->scale;
-    if (nk <= 0) {
+    int any = 0;
+    for (int t = 0; t < nk; ++t) any |= vis ? vis[t] : 1;
+    if (!any) {
         for (int d = 0; d < D; ++d) out[d] = 0.0;
         *lse = -INFINITY;
         return;
     }
     double M = -INFINITY;
     for (int t = 0; t < nk; ++t) {
+        if (vis && !vis[t]) continue;
         double acc = 0.0;
         for (int d = 0; d < D; ++d)
             acc += or_q_at(a, (qrow * a->num_q_heads + h) * D + d) * K[(long)t * D + d];
@@ -246,7 +258,7 @@ static void or_attend_row(const or_args* a, long qrow, int h, const double* K, c
     }
     double Z = 0.0;
     for (int t = 0; t < nk; ++t) {
-        s[t] = exp(s[t] - M);
+        s[t] = (vis && !vis[t]) ? 0.0 : exp(s[t] - M);
         Z += s[t];
     }
     for (int d = 0; d < D; ++d) {
@@ -272,20 +284,31 @@ static void or_seq_group(const or_args* a, int i, int g, double* out, double* ls
     double* K = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * D);
     double* V = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * D);
     double* s = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    unsigned char* vis = (unsigned char*)malloc((size_t)(L > 0 ? L : 1));
     if (L > 0) or_gather(a, i, g, L, K, V);
+    const int tree = a->tree_mask != NULL && n <= 64;
     for (long j = 0; j < n; ++j) {
         long pos = (long)L - n + j; /* the span is the last n positions */
         int nk = (int)(pos + 1);    /* causal: keys 0..pos inclusive */
         if (nk > L) nk = L;
+        if (tree) { /* keys before the span, and the marked span tokens k <= j */
+            const uint64_t bits = a->tree_mask[q0 + j];
+            for (int t = 0; t < nk; ++t) {
+                const long k = t - ((long)L - n);
+                vis[t] = k < 0 || ((bits >> k) & 1u);
+            }
+        }
         for (int hh = 0; hh < G; ++hh) {
             int h = g * G + hh;
             long r = q0 + j;
-            or_attend_row(a, r, h, K, V, nk, s, out + (r * Hq + h) * D, lse + r * Hq + h);
+            or_attend_row(a, r, h, K, V, nk, tree ? vis : NULL, s, out + (r * Hq + h) * D,
+                          lse + r * Hq + h);
         }
     }
     free(K);
     free(V);
     free(s);
+    free(vis);
 }
 
 /* Compute out [T][Hq][D] and lse [T][Hq] (natural log) in float64.
@@ -296,13 +319,13 @@ int or_paged_attention(int num_seqs, int num_q_heads, int num_kv_heads, int head
                        int kv_dtype, const float* k_scale, const float* v_scale,
                        const int32_t* block_tables, int max_blocks_per_seq,
                        const int32_t* context_lens, const int32_t* query_start_loc, float scale,
-                       const int32_t* seq_subset, int n_subset, double* out, double* lse,
-                       int num_threads) {
+                       const uint64_t* tree_mask, const int32_t* seq_subset, int n_subset,
+                       double* out, double* lse, int num_threads) {
     if (num_kv_heads <= 0 || num_q_heads % num_kv_heads) return -1;
     if (fegetround() != FE_TONEAREST) return -2;
     or_args a = {num_seqs, num_q_heads, num_kv_heads, head_dim, q, q_dtype, k_cache, v_cache,
                  kv_dtype, k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
-                 query_start_loc, scale};
+                 query_start_loc, scale, tree_mask};
     const int H = num_kv_heads;
     const long nseq = seq_subset ? n_subset : num_seqs;
     const long ntask = nseq * H;

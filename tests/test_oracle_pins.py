@@ -317,3 +317,98 @@ def test_small_configs_match_sdpa(name):
             Lr = int(pos[r]) + 1
             ref = _sdpa(q[r][:, None, :], K[:, :Lr], V[:, :Lr], wl.scale)[:, 0, :]
             np.testing.assert_allclose(out[r], ref, rtol=0, atol=1e-10)
+
+
+# ---- tree verification masks ("03 -- Engines Papers", sections 5-7) -------
+
+def _tree_masks(parents):
+    """Ancestor-or-self bit masks of a tree given by parent indices
+    (parent[j] < j, -1 for a root): bit k of mask j set iff node k lies on
+    the path from a root to node j."""
+    masks = []
+    for j, p in enumerate(parents):
+        m = 1 << j
+        while p >= 0:
+            m |= 1 << p
+            p = parents[p]
+        masks.append(m)
+    return masks
+
+
+def _random_parents(rng, n):
+    return [-1] + [int(rng.integers(-1, j)) for j in range(1, n)]
+
+
+def test_chain_tree_mask_equals_causal_span():
+    """A chain (each node's parent is the previous one) is the causal mask:
+    the masked path must give bitwise the causal result. Catches an
+    inverted bit test, an off-by-one in the span offset."""
+    rng = np.random.default_rng(21)
+    hq, hkv, d = 4, 2, 16
+    lens, ns = [40, 19, 70], [8, 19, 64]
+    Kd = [rng.standard_normal((hkv, L, d)).astype(np.float32) for L in lens]
+    Vd = [rng.standard_normal((hkv, L, d)).astype(np.float32) for L in lens]
+    kc, vc, bt, _ = _scatter_dense(Kd, Vd, lens)
+    qsl = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    q = rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32)
+    masks = np.array(sum((_tree_masks([j - 1 for j in range(n)]) for n in ns), []), np.uint64)
+    a, la = _run(q, kc, vc, bt, lens, 0.25, hq, hkv, d, qsl=qsl)
+    b, lb = _run(q, kc, vc, bt, lens, 0.25, hq, hkv, d, qsl=qsl, tree_mask=masks)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tree_masks_match_sdpa_with_explicit_masks(seed):
+    """Random candidate trees against torch's attention with the same
+    boolean mask (every key before the span, plus the node's ancestors and
+    itself), in float64 on the dense layout. Catches: wrong context part,
+    wrong bit order, a mask applied to the wrong query row."""
+    rng = np.random.default_rng(100 + seed)
+    hq, hkv, d = 6, 3, 32
+    ctx, ns = [30, 0, 50], [12, 9, 64]  # committed context before each span
+    lens = [c + n for c, n in zip(ctx, ns)]
+    Kd = [rng.standard_normal((hkv, L, d)).astype(np.float32) for L in lens]
+    Vd = [rng.standard_normal((hkv, L, d)).astype(np.float32) for L in lens]
+    kc, vc, bt, _ = _scatter_dense(Kd, Vd, lens, perm_seed=seed)
+    qsl = np.concatenate([[0], np.cumsum(ns)]).astype(np.int32)
+    q = rng.standard_normal((int(qsl[-1]), hq, d)).astype(np.float32)
+    parents = [_random_parents(rng, n) for n in ns]
+    masks = np.array(sum((_tree_masks(p) for p in parents), []), np.uint64)
+    out, lse = _run(q, kc, vc, bt, lens, 0.2, hq, hkv, d, qsl=qsl, tree_mask=masks)
+    for i, (c, n) in enumerate(zip(ctx, ns)):
+        allowed = np.zeros((n, c + n), bool)
+        allowed[:, :c] = True
+        for j in range(n):
+            for k in range(n):
+                allowed[j, c + k] = bool((int(masks[qsl[i] + j]) >> k) & 1)
+        qt = torch.from_numpy(q[qsl[i]:qsl[i + 1]].astype(np.float64)).permute(1, 0, 2)[None]
+        kt = torch.from_numpy(Kd[i].astype(np.float64))[None]
+        vt = torch.from_numpy(Vd[i].astype(np.float64))[None]
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(allowed),
+                                             scale=float(np.float32(0.2)), enable_gqa=True)
+        ref = ref[0].permute(1, 0, 2).numpy()
+        np.testing.assert_allclose(out[qsl[i]:qsl[i + 1]], ref, rtol=0, atol=1e-12)
+
+
+def test_tree_mask_bits_past_the_node_and_long_spans_are_ignored():
+    """Bits for span tokens after the querying node never widen its view
+    (the node cannot see later draft tokens), and spans of more than 64
+    tokens stay causal whatever the mask says."""
+    rng = np.random.default_rng(5)
+    hq, hkv, d = 2, 1, 8
+    lens, ns = [20, 100], [6, 70]
+    Kd = [rng.standard_normal((hkv, L, d)).astype(np.float32) for L in lens]
+    Vd = [rng.standard_normal((hkv, L, d)).astype(np.float32) for L in lens]
+    kc, vc, bt, _ = _scatter_dense(Kd, Vd, lens)
+    qsl = np.array([0, 6, 76], np.int32)
+    q = rng.standard_normal((76, hq, d)).astype(np.float32)
+    causal, _ = _run(q, kc, vc, bt, lens, 0.3, hq, hkv, d, qsl=qsl)
+    all_bits = np.full(76, np.uint64(2**64 - 1), np.uint64)
+    got, _ = _run(q, kc, vc, bt, lens, 0.3, hq, hkv, d, qsl=qsl, tree_mask=all_bits)
+    assert np.array_equal(got, causal)
+    none = np.zeros(76, np.uint64)
+    sees_context, lse = _run(q, kc, vc, bt, lens, 0.3, hq, hkv, d, qsl=qsl, tree_mask=none)
+    assert np.array_equal(sees_context[6:], causal[6:])  # the 70-token span ignores the mask
+    # a node with no bits sees only the 14 committed keys: a decode over them
+    dec, _ = _run(q[0:1], kc, vc, bt[:1], [14], 0.3, hq, hkv, d)
+    np.testing.assert_array_equal(sees_context[0], dec[0])
