@@ -174,6 +174,20 @@ int pa_plan_cascade(const pa_shape* shape, const int32_t* context_lens,
                     const int32_t* group_prefix_blocks, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* pa_plan for a hybrid batch whose spans are speculative candidates
+ * verified in one pass ("03 -- Engines Papers", sections 5 to 7: the draft
+ * tokens form a candidate tree checked under a tree attention mask).
+ * tree_mask: device [num_q_tokens] uint64, one word per query token; in a
+ * span of at most 64 tokens, token j sees every key before the span and
+ * span token k <= j only where bit k of its word is set (bits above j are
+ * ignored; a chain j -> j-1 -> ... is the causal mask). Spans of more than
+ * 64 tokens, and decodes of one token with bit 0 set, attend as in
+ * pa_plan. The plan copies the masks into the workspace. */
+int pa_plan_tree(const pa_shape* shape, const int32_t* context_lens,
+                 const int32_t* query_start_loc, int num_seqs, int num_q_tokens, int max_query_len,
+                 int max_context_len, const uint64_t* tree_mask, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* Attention with a plan made by pa_plan (same arguments as the plan, plus
  * the tensors). Enqueues the attention pass (one launch per tile class
  * present) and then the merge pass: pieces that cut a segment write partial
@@ -224,7 +238,7 @@ int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream);
 const char* pa_status_string(int status);
 
 /* Library ABI version (major * 100 + minor): 200 added pa_shape.cascade
- * and pa_plan_cascade. */
+ * and pa_plan_cascade; 201 added pa_plan_tree. */
 int pa_version(void);
 
 #ifdef __cplusplus

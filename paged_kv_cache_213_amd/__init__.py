@@ -69,6 +69,8 @@ def load_library(path: str = LIB_PATH):
     lib.pa_plan.argtypes = [S, P, P, I, I, I, I, P, Z, P]
     lib.pa_plan_cascade.restype = I
     lib.pa_plan_cascade.argtypes = [S, P, P, I, I, I, I, I, I, P, P, P, P, Z, P]
+    lib.pa_plan_tree.restype = I
+    lib.pa_plan_tree.argtypes = [S, P, P, I, I, I, I, P, P, Z, P]
     lib.pa_paged_attn_run.restype = I
     lib.pa_paged_attn_run.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
     lib.pa_paged_attn_partial.restype = I
@@ -219,6 +221,44 @@ def cascade(q, k_cache, v_cache, block_tables, context_lens, scale: float, group
                query_start_loc=query_start_loc, max_query_len=mq,
                max_context_len=max_context_len, k_scale=k_scale, v_scale=v_scale, out=out,
                lse=lse, stream=stream)
+
+
+def tree(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float,
+         tree_mask, *, max_context_len: int, max_query_len: int, k_scale=None, v_scale=None,
+         partition_size: int = 0, out=None, lse=None, workspace=None, stream=None):
+    """hybrid() whose spans are speculative candidate trees: ``tree_mask``
+    [T] int64 (the bits of uint64 words), span token j sees span token
+    k <= j where bit k of word j is set (spans of at most 64 tokens)."""
+    import torch
+    shape = make_shape(q, k_cache, block_tables, partition_size)
+    T = q.shape[0]
+    S = context_lens.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    nbytes = workspace_bytes(shape, S, T, max_context_len, max_query_len)
+    ws = _workspace(nbytes, q.device, workspace)
+    plan_tree(shape, context_lens, ws, tree_mask, query_start_loc=query_start_loc,
+              num_q_tokens=T, max_query_len=max_query_len, max_context_len=max_context_len,
+              stream=stream)
+    return run(shape, q, k_cache, v_cache, block_tables, context_lens, scale, ws,
+               query_start_loc=query_start_loc, max_query_len=max_query_len,
+               max_context_len=max_context_len, k_scale=k_scale, v_scale=v_scale, out=out,
+               lse=lse, stream=stream)
+
+
+def plan_tree(shape: PaShape, context_lens, workspace, tree_mask, *, query_start_loc,
+              num_q_tokens: int, max_query_len: int, max_context_len: int, stream=None):
+    """plan() for spans under tree verification masks (``tree_mask`` [T]
+    64-bit words on the device, copied into the plan)."""
+    lib = load_library()
+    if tree_mask.element_size() != 8 or tree_mask.numel() < num_q_tokens:
+        raise ValueError("tree_mask needs one 64-bit word per query token")
+    S = context_lens.shape[0]
+    rc = lib.pa_plan_tree(ctypes.byref(shape), _ptr(context_lens), _ptr(query_start_loc), S,
+                          int(num_q_tokens), int(max_query_len), int(max_context_len),
+                          _ptr(tree_mask), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "pa_plan_tree")
 
 
 def plan(shape: PaShape, context_lens, workspace, *, query_start_loc=None, num_q_tokens: int,

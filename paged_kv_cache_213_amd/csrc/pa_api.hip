@@ -40,6 +40,7 @@ struct Layout {
     size_t off_cas_seq = 0;  // 6 int arrays of num_seqs
     size_t off_cas_recs = 0;
     size_t off_cas_lse[2] = {0, 0}, off_cas_o[2] = {0, 0};
+    size_t off_tree = 0;  // [num_tokens] uint64 tree masks
 };
 
 int check_shape(const pa_shape* s) {
@@ -111,6 +112,8 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     }
     l.off_splits = off;  // every cut segment holds a piece boundary of its stream
     off = align_up(off + sizeof(pa::SplitSeg) * (size_t)(splits > 0 ? splits : 1));
+    l.off_tree = off;
+    off = align_up(off + sizeof(uint64_t) * (size_t)(num_tokens > 0 ? num_tokens : 1));
     if (l.cascade) {
         const size_t rows = (size_t)num_tokens * s->num_q_heads;
         l.max_cas_recs = (int64_t)num_seqs * s->num_kv_heads;
@@ -175,6 +178,7 @@ struct Groups {
     const int32_t* offsets = nullptr;
     const int32_t* members = nullptr;
     const int32_t* prefix_blocks = nullptr;
+    const uint64_t* tree_mask = nullptr;  // tree verification masks
 };
 
 int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl, int num_seqs,
@@ -212,6 +216,8 @@ int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl
     }
     pl.splits = (pa::SplitSeg*)(ws + l.off_splits);
     pl.hdr = (int32_t*)ws;
+    pl.tree_mask = grp.tree_mask;
+    pl.tree_ws = (uint64_t*)(ws + l.off_tree);
     if (l.cascade) {
         pl.num_groups = grp.num_groups;
         pl.members_per_tile = l.members_per_tile;
@@ -274,6 +280,7 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
         aa.max_context_len = max_context_len;
         aa.scale_log2 = scale * 1.44269504088896340736f;
         aa.num_seqs = num_seqs;
+        aa.tree = (const uint64_t*)(ws + l.off_tree);
         if (l.cascade) {
             aa.cas_prefix = (const int32_t*)(ws + l.off_cas_seq);
             aa.group_members = (const int32_t*)(ws + l.off_cas_seq) + 4 * (size_t)num_seqs;
@@ -359,6 +366,17 @@ int pa_plan_cascade(const pa_shape* shape, const int32_t* context_lens,
     grp.offsets = group_offsets;
     grp.members = group_members;
     grp.prefix_blocks = group_prefix_blocks;
+    return plan_impl(shape, context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                     max_context_len, grp, workspace, workspace_bytes, stream);
+}
+
+int pa_plan_tree(const pa_shape* shape, const int32_t* context_lens,
+                 const int32_t* query_start_loc, int num_seqs, int num_q_tokens, int max_query_len,
+                 int max_context_len, const uint64_t* tree_mask, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    if (!query_start_loc || !tree_mask) return PA_EINVAL;
+    Groups grp;
+    grp.tree_mask = tree_mask;
     return plan_impl(shape, context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
                      max_context_len, grp, workspace, workspace_bytes, stream);
 }
@@ -494,6 +512,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 200; }
+int pa_version(void) { return 201; }
 
 }  // extern "C"

@@ -626,10 +626,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
         ncas = (int)min((int64_t)ncas * H, (int64_t)a.max_cas_recs);
     }
+    // 6. tree verification masks travel with the plan
+    if (a.tree_mask)
+        for (int r = threadIdx.x; r < a.num_tokens; r += kPlanThreads) a.tree_ws[r] = a.tree_mask[r];
     if (threadIdx.x == 0) {
         a.hdr[HDR_NTILES] = ntiles;
         a.hdr[HDR_NSPLIT] = nsplit;
         a.hdr[HDR_NCAS] = ncas;
+        a.hdr[HDR_TREE] = a.tree_mask ? 1 : 0;
     }
 }
 
@@ -676,6 +680,11 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     int pos[NT];
     int64_t rowid[NT];
     bool row_ok[NT];
+    // tree verification masks: span token k is visible to a row only where
+    // bit k of its token's mask is set (spans of at most 64 tokens)
+    const int span_start = L - nspan;
+    const bool tree = td.flags == 0 && nspan <= 64 && a.hdr[HDR_TREE] != 0;
+    uint64_t tbits[NT];
 #pragma unroll
     for (int r = 0; r < NT; ++r) {
         const int rr = 16 * r + n;
@@ -694,6 +703,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             pos[r] = row_ok[r] ? L - nspan + td.qtok0 + qj : -1;
             rowid[r] = (int64_t)(qs + td.qtok0 + qj) * Hq + kvh * G + (rr - qj * G);
         }
+        tbits[r] = (tree && row_ok[r]) ? a.tree[qs + td.qtok0 + qj] : ~0ull;
         // q operand (B of S = K q^T), holding the row's dims in the same order
         // as the K tile: f32 16m + 4g + e; bf16 32m + 8g + e; fp8
         // 64(m/2) + 16g + 8(m%2) + e for MFMA step m
@@ -738,7 +748,9 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     }
     // blocks ending at or before the tile's first query position are visible
     // to every row and lie inside the context: no masks
-    const int pos_first = td.flags == TILE_GROUP ? L - 1 : L - nspan + td.qtok0;
+    const int pos_first = td.flags == TILE_GROUP ? L - 1
+                          : tree                 ? span_start - 1
+                                                 : L - nspan + td.qtok0;
 
     const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
     for (int c0 = 0; c0 < take; c0 += 64) {
@@ -778,7 +790,11 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 for (int e = 0; e < 4; ++e) x[e] = fmaf(sc[e], c, -m_use[r]);
                 if (!full) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] = (t0 + e <= pos[r]) ? x[e] : -INFINITY;
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = t0 + e, k = t - span_start;
+                        const bool vis = t <= pos[r] && (k < 0 || ((tbits[r] >> (k & 63)) & 1u));
+                        x[e] = vis ? x[e] : -INFINITY;
+                    }
                 }
                 const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
                 if (__builtin_amdgcn_ballot_w64(mx > thr[r]) != 0) {

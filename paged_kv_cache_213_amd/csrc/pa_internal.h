@@ -78,6 +78,7 @@ enum {
     HDR_NTILES = 0,
     HDR_NSPLIT = 1,
     HDR_NCAS = 2,  // cascade records
+    HDR_TREE = 3,  // 1: the plan holds tree verification masks
     HDR_STREAM = 4,
     HDR_TOTAL = 0,
     HDR_R = 1,
@@ -142,6 +143,10 @@ struct PlanArgs {
     int32_t* cas_gbase;    // [num_seqs] a group's first tile (-1: none)
     CascadeRec* cas_recs;  // [num_seqs * Hkv]
     int32_t max_cas_recs;
+    // tree verification masks ([num_tokens], nullptr: causal spans), copied
+    // into the workspace so that the runs need no extra argument
+    const uint64_t* tree_mask;
+    uint64_t* tree_ws;
 };
 
 struct AttnArgs {
@@ -165,6 +170,7 @@ struct AttnArgs {
     const int32_t* cas_prefix;     // [num_seqs] shared blocks of a cascade member
     float* cas_lse[2];             // CAS_PRE, CAS_SUF per-row buffers
     float* cas_o[2];
+    const uint64_t* tree;          // [num_tokens] masks (used when hdr[HDR_TREE])
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;

@@ -333,6 +333,41 @@ def custom_workload(context_lens, query_lens=None, *, num_q_heads=4, num_kv_head
                     bt, nblk, partition_size, seed)
 
 
+def random_tree_parents(rng, n: int) -> list:
+    """A random candidate tree of n draft tokens in topological order:
+    parent[j] < j, -1 for a node hanging off the committed context."""
+    return [-1] + [int(rng.integers(-1, j)) for j in range(1, n)]
+
+
+def tree_masks(parents) -> list:
+    """Ancestor-or-self bit masks of a tree given by parent indices: bit k
+    of word j is set when node k lies on the path from the context to node
+    j (the visibility of a candidate tree, "03 -- Engines Papers",
+    sections 5 to 7). A chain (parent j - 1) gives the causal masks."""
+    masks = []
+    for j, p in enumerate(parents):
+        m = 1 << j
+        while p >= 0:
+            m |= 1 << p
+            p = parents[p]
+        masks.append(m)
+    return masks
+
+
+def batch_tree_masks(query_lens, seed: int, chain: bool = False) -> np.ndarray:
+    """uint64 [sum(query_lens)]: one random tree (or chain) per span of at
+    most 64 tokens; longer spans get all-ones words (they stay causal)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for n in (int(x) for x in query_lens):
+        if n > 64:
+            out += [(1 << 64) - 1] * n
+            continue
+        par = [j - 1 for j in range(n)] if chain else random_tree_parents(rng, n)
+        out += tree_masks(par)
+    return np.array(out, dtype=np.uint64)
+
+
 # --------------------------------------------------------------------------
 # values
 # --------------------------------------------------------------------------

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for want in ("pa_workspace_bytes", "pa_paged_attn_decode", "pa_paged_attn_hybrid",
                  "pa_kv_append", "pa_status_string", "pa_version", "pa_fp8_e4m3fn_to_f32",
                  "pa_probe_stream_read", "pa_probe_copy", "pa_plan", "pa_paged_attn_run",
-                 "pa_paged_attn_partial", "pa_paged_attn_merge"):
+                 "pa_paged_attn_partial", "pa_paged_attn_merge", "pa_plan_cascade", "pa_plan_tree",
+                 "pa_copy_blocks", "pa_validate_batch", "pa_bm_create"):
         assert want in names
 
 
@@ -49,7 +50,7 @@ def test_status_strings_and_version():
     assert b"invalid" in lib.pa_status_string(-1)
     assert b"workspace" in lib.pa_status_string(-2)
     assert lib.pa_status_string(-99) == b"unknown status"
-    assert lib.pa_version() >= 100
+    assert lib.pa_version() >= 201
 
 
 def _shape(**kw):

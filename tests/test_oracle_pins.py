@@ -321,22 +321,11 @@ def test_small_configs_match_sdpa(name):
 
 # ---- tree verification masks ("03 -- Engines Papers", sections 5-7) -------
 
-def _tree_masks(parents):
-    """Ancestor-or-self bit masks of a tree given by parent indices
-    (parent[j] < j, -1 for a root): bit k of mask j set iff node k lies on
-    the path from a root to node j."""
-    masks = []
-    for j, p in enumerate(parents):
-        m = 1 << j
-        while p >= 0:
-            m |= 1 << p
-            p = parents[p]
-        masks.append(m)
-    return masks
+_tree_masks = W.tree_masks
 
 
 def _random_parents(rng, n):
-    return [-1] + [int(rng.integers(-1, j)) for j in range(1, n)]
+    return W.random_tree_parents(rng, n)
 
 
 def test_chain_tree_mask_equals_causal_span():
