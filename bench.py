@@ -116,7 +116,7 @@ def attention_source_sha256() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(config: str, cascade: bool):
+def recorded_traffic(config: str, cascade: bool, fp8_qk: bool = False):
     """HBM bytes per attention launch recorded by the profiler counters for
     this workload and method (profiles/), or None when none are recorded or
     the attention source has changed since they were taken."""
@@ -128,11 +128,14 @@ def recorded_traffic(config: str, cascade: bool):
     with open(path) as fh:
         for line in fh:
             k, sep, v = line.partition(":")
-            if sep and k in ("traffic_bytes_per_launch", "attention_source_sha256", "cascade"):
+            if sep and k in ("traffic_bytes_per_launch", "attention_source_sha256", "cascade",
+                             "fp8_qk"):
                 fields[k] = v.strip()
     if fields.get("attention_source_sha256") != attention_source_sha256():
         return None
     if fields.get("cascade", "off") != ("on" if cascade else "off"):
+        return None
+    if fields.get("fp8_qk", "off") != ("on" if fp8_qk else "off"):
         return None
     t = fields.get("traffic_bytes_per_launch")
     return int(t) if t and t.isdigit() else None
@@ -199,6 +202,8 @@ def main():
     ap.add_argument("--cascade", choices=("auto", "on", "off"), default="auto",
                     help="read shared prefixes once per group (auto: when the workload's "
                          "sequences share prefix blocks)")
+    ap.add_argument("--fp8-qk", action="store_true",
+                    help="fp8 cache: S = K q^T on the fp8 matrix cores (two-term fp8 q)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run the library's plain copy kernel over this many MiB, a "
                          "kernel of known traffic for calibrating profiler byte counters")
@@ -256,7 +261,10 @@ def main():
     slots = torch.from_numpy(wl.slot_mapping).to(dev)
     lse = torch.empty(wl.num_tokens, wl.num_q_heads, dtype=torch.float32, device=dev)
     use_cascade = args.cascade == "on" or (args.cascade == "auto" and bool(wl.shared_groups))
-    shape = pa.make_shape(vals.q, vals.k_cache, bt, P, cascade=use_cascade)
+    if args.fp8_qk and wl.kv_dtype != "fp8":
+        print(json.dumps({"error": "--fp8-qk needs a workload with an fp8 cache"}))
+        sys.exit(2)
+    shape = pa.make_shape(vals.q, vals.k_cache, bt, P, cascade=use_cascade, fp8_qk=args.fp8_qk)
     groups = pa.PrefixGroups(wl.shared_groups, wl.shared_prefix_blocks, dev) if use_cascade \
         else None
     nbytes = pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len,
@@ -415,6 +423,7 @@ def main():
             "partition_size": P,
             "graph": graph is not None,
             "cascade": use_cascade,
+            "fp8_qk": bool(args.fp8_qk),
             "kv_bytes_read_per_layer": read_bytes,
             "kv_bytes_unique_per_layer": wl.kv_bytes_unique() if wl.shared_groups else kv_bytes,
             "seed": wl.seed,
@@ -425,7 +434,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": recorded_traffic(wl.name, use_cascade),
+            "traffic": recorded_traffic(wl.name, use_cascade, args.fp8_qk),
             "traffic_note": "HBM bytes per attention pass launch (calibrated FETCH_SIZE + "
                             "WRITE_SIZE, profiles/); null if not recorded for the current "
                             "attention source",

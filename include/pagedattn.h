@@ -98,6 +98,13 @@ typedef struct pa_shape {
     int32_t partition_size;     /* split-KV piece in tokens, 0 = balanced */
     int32_t cascade;            /* 1: plans may hold shared-prefix groups
                                    (pa_plan_cascade); reserves their room */
+    int32_t fp8_qk;             /* 1 (fp8 cache only): S = K q^T on the fp8
+                                   matrix cores, q quantized per (token, head)
+                                   into two e4m3 terms, value and residual
+                                   ("Inference engines", recent developments:
+                                   the QK matmul itself in FP8); results
+                                   within the fp8 tolerance, not bitwise
+                                   those of 0 */
 } pa_shape;
 
 /* Bytes of device workspace the attention calls need for this batch (work
@@ -238,7 +245,7 @@ int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream);
 const char* pa_status_string(int status);
 
 /* Library ABI version (major * 100 + minor): 200 added pa_shape.cascade
- * and pa_plan_cascade; 201 added pa_plan_tree. */
+ * and pa_plan_cascade; 201 added pa_plan_tree; 202 added pa_shape.fp8_qk. */
 int pa_version(void);
 
 #ifdef __cplusplus

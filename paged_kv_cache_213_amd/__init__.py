@@ -38,6 +38,7 @@ class PaShape(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("partition_size", ctypes.c_int32),
         ("cascade", ctypes.c_int32),
+        ("fp8_qk", ctypes.c_int32),
     ]
 
 
@@ -127,13 +128,14 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_shape(q, k_cache, block_tables, partition_size: int = 0,
-               cascade: bool = False) -> PaShape:
+               cascade: bool = False, fp8_qk: bool = False) -> PaShape:
     T, Hq, D = q.shape
     NB, Hkv, B, D2 = k_cache.shape
     if B != 16 or D2 != D:
         raise PagedAttentionError(f"k_cache shape {tuple(k_cache.shape)} does not match q")
     return PaShape(Hq, Hkv, D, 16, NB, block_tables.shape[1], _dtype_code(q),
-                   _dtype_code(k_cache), int(partition_size), int(bool(cascade)))
+                   _dtype_code(k_cache), int(partition_size), int(bool(cascade)),
+                   int(bool(fp8_qk)))
 
 
 def workspace_bytes(shape: PaShape, num_seqs: int, num_q_tokens: int, max_context_len: int,
@@ -153,7 +155,7 @@ def _workspace(nbytes: int, device, workspace):
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, *,
            max_context_len: int, k_scale=None, v_scale=None, partition_size: int = 0,
-           out=None, lse=None, workspace=None, stream=None):
+           out=None, lse=None, workspace=None, stream=None, fp8_qk: bool = False):
     """Paged attention for one query token per sequence.
 
     q [S][Hq][D]; block_tables [S][max_blocks] int32; context_lens [S] int32
@@ -161,7 +163,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, *,
     fills ``lse`` [S][Hq] float32 when given)."""
     import torch
     lib = load_library()
-    shape = make_shape(q, k_cache, block_tables, partition_size)
+    shape = make_shape(q, k_cache, block_tables, partition_size, fp8_qk=fp8_qk)
     S = q.shape[0]
     if out is None:
         out = torch.empty_like(q)
@@ -178,12 +180,13 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, *,
 
 def hybrid(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float, *,
            max_context_len: int, max_query_len: int, k_scale=None, v_scale=None,
-           partition_size: int = 0, out=None, lse=None, workspace=None, stream=None):
+           partition_size: int = 0, out=None, lse=None, workspace=None, stream=None,
+           fp8_qk: bool = False):
     """Paged attention for a mixed batch of chunked-prefill spans and
     decodes. q [T][Hq][D] with T = query_start_loc[-1]."""
     import torch
     lib = load_library()
-    shape = make_shape(q, k_cache, block_tables, partition_size)
+    shape = make_shape(q, k_cache, block_tables, partition_size, fp8_qk=fp8_qk)
     T = q.shape[0]
     S = context_lens.shape[0]
     if out is None:
@@ -202,12 +205,12 @@ def hybrid(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, sca
 def cascade(q, k_cache, v_cache, block_tables, context_lens, scale: float, groups, *,
             max_context_len: int, query_start_loc=None, max_query_len: int = 1, k_scale=None,
             v_scale=None, partition_size: int = 0, out=None, lse=None, workspace=None,
-            stream=None):
+            stream=None, fp8_qk: bool = False):
     """Paged attention with shared-prefix groups (``PrefixGroups``): plan
     with the groups, then the attention and merge passes. Same result as
     decode()/hybrid(); each group's prefix is read once for its members."""
     import torch
-    shape = make_shape(q, k_cache, block_tables, partition_size, cascade=True)
+    shape = make_shape(q, k_cache, block_tables, partition_size, cascade=True, fp8_qk=fp8_qk)
     T = q.shape[0]
     S = context_lens.shape[0]
     mq = max_query_len if query_start_loc is not None else 1
@@ -225,12 +228,13 @@ def cascade(q, k_cache, v_cache, block_tables, context_lens, scale: float, group
 
 def tree(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale: float,
          tree_mask, *, max_context_len: int, max_query_len: int, k_scale=None, v_scale=None,
-         partition_size: int = 0, out=None, lse=None, workspace=None, stream=None):
+         partition_size: int = 0, out=None, lse=None, workspace=None, stream=None,
+         fp8_qk: bool = False):
     """hybrid() whose spans are speculative candidate trees: ``tree_mask``
     [T] int64 (the bits of uint64 words), span token j sees span token
     k <= j where bit k of word j is set (spans of at most 64 tokens)."""
     import torch
-    shape = make_shape(q, k_cache, block_tables, partition_size)
+    shape = make_shape(q, k_cache, block_tables, partition_size, fp8_qk=fp8_qk)
     T = q.shape[0]
     S = context_lens.shape[0]
     if out is None:

@@ -57,7 +57,14 @@ int check_shape(const pa_shape* s) {
     if (!ok) return PA_EINVAL;
     if (s->partition_size < 0 || s->partition_size % PA_BLOCK_SIZE) return PA_EINVAL;
     if (s->cascade != 0 && s->cascade != 1) return PA_EINVAL;
+    if (s->fp8_qk != 0 && (s->fp8_qk != 1 || s->kv_dtype != PA_FP8_E4M3FN)) return PA_EINVAL;
     return PA_OK;
+}
+
+// The attention kernels' kind: the cache dtype, or fp8 with QK on the fp8
+// matrix cores.
+int kernel_kind(const pa_shape* s) {
+    return s->kv_dtype == PA_FP8_E4M3FN && s->fp8_qk ? pa::KIND_FP8_QK : s->kv_dtype;
 }
 
 // Upper bound of resident attention waves when no device can be queried
@@ -97,7 +104,7 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     off = align_up(off + sizeof(pa::TileDesc) * (size_t)l.max_tiles);
     int64_t splits = 0;
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
-        const int w = pa::resident_waves(s->kv_dtype, s->head_dim, st);
+        const int w = pa::resident_waves(kernel_kind(s), s->head_dim, st);
         l.waves[st] = w > 0 ? w : kWaveBound;
         // pieces per KV head substream: ceil(B / R) with B <= tiles * blocks
         // per tile, and R = P / 16, or R >= Hkv * B / waves when balanced
@@ -296,7 +303,7 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
             aa.pieces = (const pa::PieceStart*)(ws + l.off_pieces[st]);
             aa.part_lse = (float*)(ws + l.off_lse[st]);
             aa.part_o = (float*)(ws + l.off_o[st]);
-            if (pa::launch_attention(s->kv_dtype, s->head_dim, aa, l.max_pieces[st], hs) !=
+            if (pa::launch_attention(kernel_kind(s), s->head_dim, aa, l.max_pieces[st], hs) !=
                 hipSuccess)
                 return PA_EHIP;
         }
@@ -314,6 +321,7 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
         ma.num_q_heads = s->num_q_heads;
         ma.num_kv_heads = s->num_kv_heads;
         ma.group = s->num_q_heads / s->num_kv_heads;
+        ma.wide_nt = pa::wide_tiles(s->kv_dtype);
         const int64_t splits = l.max_pieces[0] + l.max_pieces[1];
         ma.max_splits = (int32_t)splits;
         int64_t records = splits > 1 ? splits : 0;  // one piece cuts nothing
@@ -512,6 +520,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 201; }
+int pa_version(void) { return 202; }
 
 }  // extern "C"

@@ -52,7 +52,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-enum KvKind { KV_F32 = PA_F32, KV_BF16 = PA_BF16, KV_FP8 = PA_FP8_E4M3FN };
+enum KvKind { KV_F32 = PA_F32, KV_BF16 = PA_BF16, KV_FP8 = PA_FP8_E4M3FN, KV_FP8Q = KIND_FP8_QK };
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -323,6 +323,136 @@ struct Tile<KV_FP8, D> {
         }
     }
 };
+
+// fp8 cache with S = K q^T on the fp8 matrix cores. The query row arrives as
+// two e4m3 terms over the lane's dims in the K tile's byte order: the row
+// scaled to the e4m3 range (hi) and 16 times what that rounding left
+// (lo), so q / sq = hi + lo / 16 to about 2^-8 of each value. One
+// v_mfma_scale_f32_16x16x128_f8f6f4 per term takes the lo term with an
+// E8M0 block scale of 2^-4 into the same accumulator. P V is unchanged.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ i32x8 join8(uint4 a, uint4 b) {
+    return i32x8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+}
+constexpr int kE8M0One = 127;          // E8M0 code of 2^0
+constexpr int kE8M0Sixteenth = 123;    // 2^-4
+template <int D>
+__device__ __forceinline__ f32x4 qk_fp8(const uint4 (&k)[D / 64], const uint4* q) {
+    // q[0], q[1]: hi term; q[2], q[3]: lo term (D = 64 fills only q[0], q[2])
+    i32x8 a;
+    if constexpr (D == 128) {
+        a = join8(k[0], k[1]);
+    } else {
+        a = join8(k[0], make_uint4(0, 0, 0, 0));
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, join8(q[0], q[1]), acc, 0, 0, 0,
+                                                           kE8M0One, 0, kE8M0One);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, join8(q[2], q[3]), acc, 0, 0, 0,
+                                                           kE8M0One, 0, kE8M0Sixteenth);
+    return acc;
+}
+
+// K kept in e4m3, V in bf16: the converted block of a tile whose K and V
+// serve several row tiles.
+template <int D>
+struct TileFp8QkV {
+    uint4 k[D / 64];
+    uint2 v[D / 16];
+    __device__ __forceinline__ f32x4 qk(const uint4* q) const { return qk_fp8<D>(k, q); }
+    __device__ __forceinline__ void mask_v(int nvalid) {
+        const uint32_t mx = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
+        const uint32_t my = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            v[dt].x &= mx;
+            v[dt].y &= my;
+        }
+    }
+    __device__ __forceinline__ void pv(s16x4 p, f32x4* o) const {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v[dt]), p,
+                                                              o[dt], 0, 0, 0);
+    }
+};
+
+template <int D>
+struct Tile<KV_FP8Q, D> : Tile<KV_FP8, D> {
+    __device__ __forceinline__ f32x4 qk(const uint4* q) const { return qk_fp8<D>(this->k, q); }
+    __device__ __forceinline__ TileFp8QkV<D> to_bf16() const {
+        TileFp8QkV<D> b;
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) b.k[j] = this->k[j];
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            b.v[dt].x = fp8x2_to_bf16x2<false>(this->v[dt]);
+            b.v[dt].y = fp8x2_to_bf16x2<true>(this->v[dt]);
+        }
+        return b;
+    }
+};
+
+// Row q (bf16) -> the two e4m3 terms of qk_fp8 for this lane's dims 16g +
+// [0, 16) and, for D = 128, 64 + 16g + [0, 16); returns the row's scale sq
+// (amax / 448; every lane of the row gets the same one). Rows of zeros get
+// sq = 0 and zero terms.
+__device__ __forceinline__ uint32_t pk_fp8(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+template <int D>
+__device__ __forceinline__ float quantize_q_fp8(const uint16_t* qrow, bool ok, int g,
+                                                uint4 (&out)[4]) {
+    constexpr int P = D / 64;  // 16-dim parts per lane
+    float x[P][16];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const uint4* src = (const uint4*)(qrow + 64 * p + 16 * g);
+        const uint4 a = ok ? src[0] : make_uint4(0, 0, 0, 0);
+        const uint4 b = ok ? src[1] : make_uint4(0, 0, 0, 0);
+        const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x[p][2 * i] = bf16_lo(w[i]);
+            x[p][2 * i + 1] = bf16_hi(w[i]);
+        }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[p][i]));
+    amax = row_max(amax);
+    const float inv = amax > 0.f ? 448.f / amax : 0.f;
+    uint32_t hi[8] = {0, 0, 0, 0, 0, 0, 0, 0}, lo[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float u[4], r[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u[e] = fminf(fmaxf(x[p][4 * i + e] * inv, -448.f), 448.f);
+            const uint32_t h = pk_fp8(u[0], u[1], u[2], u[3]);
+            const f32x2_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, false);
+            const f32x2_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, true);
+            r[0] = 16.f * (u[0] - h01.x);
+            r[1] = 16.f * (u[1] - h01.y);
+            r[2] = 16.f * (u[2] - h23.x);
+            r[3] = 16.f * (u[3] - h23.y);
+            hi[4 * p + i] = h;
+            lo[4 * p + i] = pk_fp8(r[0], r[1], r[2], r[3]);
+        }
+    }
+    out[0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    out[1] = make_uint4(hi[4], hi[5], hi[6], hi[7]);
+    out[2] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    out[3] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
+    return amax * (1.f / 448.f);
+}
 
 // ---- plan ------------------------------------------------------------------
 //
@@ -664,7 +794,10 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     using T = Tile<kv, D>;
     // single-token tiles read each block once; wide tiles share it through L2
     constexpr bool kStreamLoads = NT == 1 && PA_NT_LOADS;
-    using QReg = typename std::conditional<kv == KV_F32, float[D / 4], uint4[D / 32]>::type;
+    constexpr bool kFp8Cache = kv == KV_FP8 || kv == KV_FP8Q;
+    using QReg = typename std::conditional<
+        kv == KV_F32, float[D / 4],
+        typename std::conditional<kv == KV_FP8Q, uint4[4], uint4[D / 32]>::type>::type;
     const int lane = threadIdx.x & 63;
     const int n = lane & 15;  // query row owned in MFMA layouts (within a row tile)
     const int g = lane >> 4;  // lane group
@@ -677,6 +810,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     // this lane's query row in row tile r: tile row 16 r + n = token qj,
     // head kvh*G + (row % G)
     QReg qreg[NT];
+    float qscale[NT];  // fp8 q: the row's scale times the score scale (log2 units)
     int pos[NT];
     int64_t rowid[NT];
     bool row_ok[NT];
@@ -707,7 +841,11 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         // q operand (B of S = K q^T), holding the row's dims in the same order
         // as the K tile: f32 16m + 4g + e; bf16 32m + 8g + e; fp8
         // 64(m/2) + 16g + 8(m%2) + e for MFMA step m
-        if constexpr (kv == KV_F32) {
+        qscale[r] = 1.f;
+        if constexpr (kv == KV_FP8Q) {
+            const uint16_t* qp = (const uint16_t*)a.q + (row_ok[r] ? rowid[r] : 0) * D;
+            qscale[r] = a.scale_log2 * quantize_q_fp8<D>(qp, row_ok[r], g, qreg[r]);
+        } else if constexpr (kv == KV_F32) {
             const float* qp = (const float*)a.q + rowid[r] * D + 4 * g;
 #pragma unroll
             for (int m = 0; m < D / 16; ++m) {
@@ -762,7 +900,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         float my_ks = 1.f, my_vs = 1.f;
         if (lane < cnt) {
             my_phys = min(max(bt_row[td.b0 + j + c0 + lane], 0), a.num_blocks - 1);
-            if constexpr (kv == KV_FP8) {
+            if constexpr (kFp8Cache) {
                 my_ks = a.k_scale[(int64_t)my_phys * Hkv + kvh];
                 my_vs = a.v_scale[(int64_t)my_phys * Hkv + kvh];
             }
@@ -772,9 +910,9 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             const int jb = td.b0 + j + c0 + i;  // logical block
             const int t0 = jb * 16 + 4 * g;  // my first token in it
             const bool full = jb * 16 + 15 <= pos_first;  // wave-uniform
-            float c = a.scale_log2;
+            float c = kv == KV_FP8Q ? 1.f : a.scale_log2;
             float vsc = 1.f;
-            if constexpr (kv == KV_FP8) {
+            if constexpr (kFp8Cache) {
                 c *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                    __builtin_bit_cast(int, my_ks), i));
                 vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
@@ -786,8 +924,9 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 if (r >= nrt) break;  // row tiles without rows (wave-uniform)
                 const f32x4 sc = cur.qk(qreg[r]);
                 float x[4];  // scores relative to the reference
+                const float cr = kv == KV_FP8Q ? c * qscale[r] : c;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = fmaf(sc[e], c, -m_use[r]);
+                for (int e = 0; e < 4; ++e) x[e] = fmaf(sc[e], cr, -m_use[r]);
                 if (!full) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -831,7 +970,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 if (r < nrt) cur.pv(pk[r], o[r]);
         };
         auto consume = [&](T& cur, int i) {
-            if constexpr (kv == KV_FP8 && NT > 1) {
+            if constexpr (kFp8Cache && NT > 1) {
                 auto cb = cur.to_bf16();
                 consume_tile(cb, i);
             } else {
@@ -964,8 +1103,16 @@ __global__ __launch_bounds__(64) PA_NARROW_OCCUPANCY void attention_narrow(AttnA
 }
 
 // Wide tiles of chunked-prefill spans: matrix-core bound, one wave per SIMD.
+#ifndef PA_WIDE_MIN_WAVES
+#define PA_WIDE_MIN_WAVES 0
+#endif
+#if PA_WIDE_MIN_WAVES > 0
+#define PA_WIDE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WIDE_MIN_WAVES, 8)))
+#else
+#define PA_WIDE_OCCUPANCY
+#endif
 template <int kv, int D>
-__global__ __launch_bounds__(64) void attention_wide(AttnArgs a) {
+__global__ __launch_bounds__(64) PA_WIDE_OCCUPANCY void attention_wide(AttnArgs a) {
     attention_body<kv, D, wide_tiles(kv)>(a);
 }
 
@@ -1048,7 +1195,7 @@ __device__ __forceinline__ void merge_cascade(const MergeArgs& a, const CascadeR
             continue;
         }
         const int st = kind == CAS_PRE ? STREAM_WIDE : STREAM_NARROW;
-        const int nt = st == STREAM_WIDE ? wide_tiles(qd) : 1;
+        const int nt = st == STREAM_WIDE ? a.wide_nt : 1;
         const int rr = (kind == CAS_PRE ? rc.pre_pos * G : 0) + n;  // row in the slot
         const float4* po = (const float4*)a.part_o[st];
         // four pieces per round trip: all their loads are issued first
@@ -1084,7 +1231,7 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     const int lane = threadIdx.x;
     const int n = lane & 15, g = lane >> 4;  // the attention kernel's layout
     const int G = a.group;
-    const int nt = sp.stream == STREAM_WIDE ? wide_tiles(qd) : 1;  // row tiles per slot
+    const int nt = sp.stream == STREAM_WIDE ? a.wide_nt : 1;  // row tiles per slot
     const float* part_lse = a.part_lse[sp.stream];
     const float4* part_o = (const float4*)a.part_o[sp.stream];
     const int Hkv = a.num_kv_heads;
@@ -1215,14 +1362,16 @@ hipError_t launch_attention_d(const AttnArgs& a, int64_t max_pieces, hipStream_t
 
 }  // namespace
 
-int resident_waves(int kv_dtype, int head_dim, int stream) {
-    switch (kv_dtype * 1000 + head_dim) {
+int resident_waves(int kind, int head_dim, int stream) {
+    switch (kind * 1000 + head_dim) {
     case PA_F32 * 1000 + 64: return resident_waves_d<KV_F32, 64>(stream);
     case PA_F32 * 1000 + 128: return resident_waves_d<KV_F32, 128>(stream);
     case PA_BF16 * 1000 + 64: return resident_waves_d<KV_BF16, 64>(stream);
     case PA_BF16 * 1000 + 128: return resident_waves_d<KV_BF16, 128>(stream);
     case PA_FP8_E4M3FN * 1000 + 64: return resident_waves_d<KV_FP8, 64>(stream);
     case PA_FP8_E4M3FN * 1000 + 128: return resident_waves_d<KV_FP8, 128>(stream);
+    case KIND_FP8_QK * 1000 + 64: return resident_waves_d<KV_FP8Q, 64>(stream);
+    case KIND_FP8_QK * 1000 + 128: return resident_waves_d<KV_FP8Q, 128>(stream);
     default: return 0;
     }
 }
@@ -1232,15 +1381,17 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64_t max_pieces,
+hipError_t launch_attention(int kind, int head_dim, const AttnArgs& a, int64_t max_pieces,
                             hipStream_t s) {
-    switch (kv_dtype * 1000 + head_dim) {
+    switch (kind * 1000 + head_dim) {
     case PA_F32 * 1000 + 64: return launch_attention_d<KV_F32, 64>(a, max_pieces, s);
     case PA_F32 * 1000 + 128: return launch_attention_d<KV_F32, 128>(a, max_pieces, s);
     case PA_BF16 * 1000 + 64: return launch_attention_d<KV_BF16, 64>(a, max_pieces, s);
     case PA_BF16 * 1000 + 128: return launch_attention_d<KV_BF16, 128>(a, max_pieces, s);
     case PA_FP8_E4M3FN * 1000 + 64: return launch_attention_d<KV_FP8, 64>(a, max_pieces, s);
     case PA_FP8_E4M3FN * 1000 + 128: return launch_attention_d<KV_FP8, 128>(a, max_pieces, s);
+    case KIND_FP8_QK * 1000 + 64: return launch_attention_d<KV_FP8Q, 64>(a, max_pieces, s);
+    case KIND_FP8_QK * 1000 + 128: return launch_attention_d<KV_FP8Q, 128>(a, max_pieces, s);
     default: return hipErrorInvalidValue;
     }
 }

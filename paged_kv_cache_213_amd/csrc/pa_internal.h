@@ -69,7 +69,17 @@ enum { STREAM_WIDE = 0, STREAM_NARROW = 1, NUM_STREAMS = 2 };
 #ifndef PA_WIDE_TILES
 #define PA_WIDE_TILES 4
 #endif
-constexpr int wide_tiles(int dtype) { return dtype == PA_F32 ? 2 : PA_WIDE_TILES; }
+#ifndef PA_WIDE_TILES_FP8
+#define PA_WIDE_TILES_FP8 PA_WIDE_TILES
+#endif
+// Kernel kinds: the cache dtype, or an fp8 cache whose S = K q^T runs on
+// the fp8 matrix cores (pa_shape.fp8_qk).
+constexpr int KIND_FP8_QK = 3;
+constexpr int wide_tiles(int kind) {
+    return kind == PA_F32                                 ? 2
+           : kind == PA_FP8_E4M3FN || kind == KIND_FP8_QK ? PA_WIDE_TILES_FP8
+                                                          : PA_WIDE_TILES;
+}
 
 // Header words at the start of the workspace: per stream s, the blocks of
 // each KV head's substream, the piece size and the piece count at
@@ -192,6 +202,7 @@ struct MergeArgs {
     int32_t num_kv_heads;
     int32_t group;
     int32_t max_splits;  // workgroups [0, max_splits) complete cut segments
+    int32_t wide_nt;     // row tiles of the wide stream's slots (by cache dtype)
     const CascadeRec* cas_recs;  // the rest combine cascade parts
     const float* cas_lse[2];
     const float* cas_o[2];
@@ -224,11 +235,11 @@ struct CopyArgs {
 
 // Launchers (host side), defined next to their kernels.
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_attention(int kv_dtype, int head_dim, const AttnArgs& a, int64_t max_pieces,
+hipError_t launch_attention(int kind, int head_dim, const AttnArgs& a, int64_t max_pieces,
                             hipStream_t s);  // a.stream selects the wide or narrow kernel
 // Waves of the attention kernel of a stream that fit on the device at once
 // (> 0), or 0 if the device cannot be queried.
-int resident_waves(int kv_dtype, int head_dim, int stream);
+int resident_waves(int kind, int head_dim, int stream);
 // records: cut-segment workgroups (a.max_splits) plus cascade records
 hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t records,
                         hipStream_t s);

@@ -36,7 +36,7 @@ def dev_tensors(wl, vals, pre):
 
 
 def gpu_step(wl, t, *, partition_size=None, hybrid=None, with_lse=True, append=True,
-             groups=None):
+             groups=None, fp8_qk=False):
     """kv_append (in place on t's caches) then attention; returns (out, lse).
     groups: (lists of sequences, shared prefix blocks per list) for cascade
     attention."""
@@ -53,15 +53,16 @@ def gpu_step(wl, t, *, partition_size=None, hybrid=None, with_lse=True, append=T
                          max_context_len=wl.max_context_len,
                          query_start_loc=t["qsl"] if use_hybrid else None,
                          max_query_len=wl.max_query_len, k_scale=t["k_scale"],
-                         v_scale=t["v_scale"], partition_size=P, lse=lse)
+                         v_scale=t["v_scale"], partition_size=P, lse=lse, fp8_qk=fp8_qk)
     elif use_hybrid:
         out = pa.hybrid(t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], t["qsl"], wl.scale,
                         max_context_len=wl.max_context_len, max_query_len=wl.max_query_len,
-                        k_scale=t["k_scale"], v_scale=t["v_scale"], partition_size=P, lse=lse)
+                        k_scale=t["k_scale"], v_scale=t["v_scale"], partition_size=P, lse=lse,
+                        fp8_qk=fp8_qk)
     else:
         out = pa.decode(t["q"], t["k_cache"], t["v_cache"], t["bt"], t["cl"], wl.scale,
                         max_context_len=wl.max_context_len, k_scale=t["k_scale"],
-                        v_scale=t["v_scale"], partition_size=P, lse=lse)
+                        v_scale=t["v_scale"], partition_size=P, lse=lse, fp8_qk=fp8_qk)
     torch.cuda.synchronize()
     return out, lse
 
@@ -76,7 +77,8 @@ def prepare(wl, device="cuda"):
     return vals, pre
 
 
-def check_step(wl, partition_size=None, hybrid=None, seq_subset=None, groups=None):
+def check_step(wl, partition_size=None, hybrid=None, seq_subset=None, groups=None,
+               fp8_qk=False):
     """One step on the GPU against the oracle on the same inputs: the
     per-element tolerance, the relative-RMS guard and the lse bound.
     Returns (errors, device tensors, post-append host state)."""
@@ -84,7 +86,8 @@ def check_step(wl, partition_size=None, hybrid=None, seq_subset=None, groups=Non
     vals, pre = prepare(wl)
     post = H.oracle_append(wl, pre)
     t = dev_tensors(wl, vals, pre)
-    out, lse = gpu_step(wl, t, partition_size=partition_size, hybrid=hybrid, groups=groups)
+    out, lse = gpu_step(wl, t, partition_size=partition_size, hybrid=hybrid, groups=groups,
+                        fp8_qk=fp8_qk)
     ref, ref_lse = oracle.run_workload(wl, post, seq_subset=seq_subset)
     got = out_f64(out)
     got_lse = lse.cpu().numpy().astype(np.float64)

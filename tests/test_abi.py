@@ -50,7 +50,7 @@ def test_status_strings_and_version():
     assert b"invalid" in lib.pa_status_string(-1)
     assert b"workspace" in lib.pa_status_string(-2)
     assert lib.pa_status_string(-99) == b"unknown status"
-    assert lib.pa_version() >= 201
+    assert lib.pa_version() >= 202
 
 
 def _shape(**kw):
@@ -64,6 +64,7 @@ def _shape(**kw):
     dict(num_q_heads=30), dict(head_dim=96), dict(block_size=32), dict(partition_size=24),
     dict(q_dtype=pa.PA_F32, kv_dtype=pa.PA_BF16), dict(num_kv_heads=0), dict(num_blocks=0),
     dict(q_dtype=pa.PA_FP8_E4M3FN, kv_dtype=pa.PA_FP8_E4M3FN),
+    dict(fp8_qk=1), dict(kv_dtype=pa.PA_FP8_E4M3FN, fp8_qk=2), dict(cascade=3),
 ])
 def test_invalid_shapes_are_rejected(bad):
     lib = _lib()
@@ -102,6 +103,8 @@ def test_argument_checks_before_launch():
     assert call(S=0) == pa.PA_OK  # nothing to do, nothing enqueued
     s8 = _shape(kv_dtype=pa.PA_FP8_E4M3FN)
     ws8 = lib.pa_workspace_bytes(ctypes.byref(s8), 4, 4, 100, 1)
+    s8q = _shape(kv_dtype=pa.PA_FP8_E4M3FN, fp8_qk=1)
+    assert lib.pa_workspace_bytes(ctypes.byref(s8q), 4, 4, 100, 1) == ws8
     rc = lib.pa_paged_attn_decode(ctypes.byref(s8), F, None, F, F, F, None, None, F, F, 4, 100,
                                   0.1, F, ws8, None)
     assert rc == pa.PA_EINVAL  # fp8 without scales

@@ -1,0 +1,84 @@
+"""fp8 cache with S = K q^T on the fp8 matrix cores (pa_shape.fp8_qk): the
+query is quantized per (token, head) into two e4m3 terms, the value and its
+residual, and the scores come from two fp8 MFMAs ("Inference engines",
+recent developments: the attention matmuls themselves in FP8). The oracle
+is the same exact definition as for every other test; the tolerance is the
+fp8 one.
+
+One e4m3 term alone would not meet it: over short contexts its rounding of
+q (up to 2^-4 of a value) moves the softmax weights of a handful of keys
+by several percent. The short-context test below holds 2048 query rows
+over 2 to 8 keys; there a single-term q errs by up to about 0.1, the two
+terms by about 0.003."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_213_amd import workloads as W
+from tests import helpers as H
+from tests.gpu_common import check_step, dev_tensors, gpu_step, out_f64, prepare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("P", [None, 16, 0])
+def test_small_70b_decode(P):
+    wl = W.make_config("c5", small=True)
+    e, _, _ = check_step(wl, partition_size=P, fp8_qk=True)
+    print(f"c5 small fp8_qk P={P}: {e}", flush=True)
+
+
+@pytest.mark.parametrize("cascade", [False, True])
+def test_full_70b_decode_sampled(cascade):
+    """The full fp8 batch in the bench's launch configuration, with and
+    without its sampling groups; sampled sequences."""
+    wl = W.make_config("c5")
+    pick = np.array(sorted({0, 1, 37, 64, 90, wl.num_seqs - 1}), np.int32)
+    groups = (wl.shared_groups, wl.shared_prefix_blocks) if cascade else None
+    e, _, _ = check_step(wl, partition_size=0, seq_subset=pick, groups=groups, fp8_qk=True)
+    print(f"c5 full fp8_qk cascade={cascade}: {e}", flush=True)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_short_contexts(seed):
+    """256 decodes over 2 to 8 keys, GQA 8 (2048 query rows)."""
+    rng = np.random.default_rng(500 + seed)
+    lens = rng.integers(2, 9, 256)
+    wl = W.custom_workload(lens, num_q_heads=16, num_kv_heads=2, head_dim=128,
+                           q_dtype="bf16", kv_dtype="fp8", seed=600 + seed)
+    e, _, _ = check_step(wl, fp8_qk=True)
+    print(f"short fp8_qk seed={seed}: {e}", flush=True)
+
+
+@pytest.mark.parametrize("D,G", [(64, 4), (128, 16), (128, 2)])
+def test_hybrid_spans(D, G):
+    """Chunked-prefill spans (wide tiles) next to decodes, both head sizes,
+    including contexts of one key and a span that starts its sequence."""
+    lens = [1, 40, 300, 17, 64, 529, 90, 3]
+    qlens = [1, 1, 100, 17, 20, 1, 33, 3]
+    wl = W.custom_workload(lens, qlens, num_q_heads=2 * G if G <= 8 else G,
+                           num_kv_heads=2 if G <= 8 else 1, head_dim=D, q_dtype="bf16",
+                           kv_dtype="fp8", seed=D + G)
+    for P in (None, 16, 0):
+        e, _, _ = check_step(wl, partition_size=P, fp8_qk=True)
+        print(f"hybrid fp8_qk D={D} G={G} P={P}: {e}", flush=True)
+
+
+def test_query_scales_per_row():
+    """Query rows whose magnitudes differ by 2^8 across heads and tokens:
+    each row gets its own scale, so small rows keep their precision."""
+    lens = [50, 700, 1200, 9]
+    wl = W.custom_workload(lens, [1, 4, 1, 9], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                           q_dtype="bf16", kv_dtype="fp8", seed=17)
+    vals, _ = prepare(wl)
+    row_scale = torch.tensor([2.0 ** (-6 + (i * 5) % 9) for i in range(wl.num_tokens * 8)],
+                             dtype=torch.float32, device=vals.q.device).view(wl.num_tokens, 8, 1)
+    vals.q = (vals.q.float() * row_scale).to(vals.q.dtype)
+    pre = H.host_pre_append(wl, vals)
+    post = H.oracle_append(wl, pre)
+    t = dev_tensors(wl, vals, pre)
+    out, _ = gpu_step(wl, t, fp8_qk=True)
+    ref, _ = oracle.run_workload(wl, post)
+    e = H.assert_parity(out_f64(out), ref, "fp8", "row scales")
+    print(f"row scales fp8_qk: {e}", flush=True)
