@@ -788,12 +788,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 // share every K/V block the wave loads. Then either write the rows' output
 // (the wave saw the whole segment) or write a partial result into the
 // piece's slot for the merge pass.
-template <int kv, int D, int NT>
+template <int kv, int D, int NT, int NR, bool kOnce>
 __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td, const int kvh,
                                             const int j, const int take, const int piece) {
     using T = Tile<kv, D>;
-    // single-token tiles read each block once; wide tiles share it through L2
-    constexpr bool kStreamLoads = NT == 1 && PA_NT_LOADS;
+    // blocks that no other tile of the call reads (single-token tiles, and
+    // a shared prefix in its group tile) are streamed past the caches; the
+    // query tiles of a span share each block through L2
+    constexpr bool kStreamLoads = kOnce && PA_NT_LOADS;
     constexpr bool kFp8Cache = kv == KV_FP8 || kv == KV_FP8Q;
     using QReg = typename std::conditional<
         kv == KV_F32, float[D / 4],
@@ -805,22 +807,23 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     const int seq = td.seq;
     const int L = td.L, qs = td.qs, nspan = td.nspan;
     const int nrows = td.ntok * G;
-    const int nrt = (nrows + 15) >> 4;  // row tiles holding rows
+    // NR = ceil(nrows / 16) row tiles hold rows (the caller dispatches on
+    // it); slots keep the layout of NT row tiles
 
     // this lane's query row in row tile r: tile row 16 r + n = token qj,
     // head kvh*G + (row % G)
-    QReg qreg[NT];
-    float qscale[NT];  // fp8 q: the row's scale times the score scale (log2 units)
-    int pos[NT];
-    int64_t rowid[NT];
-    bool row_ok[NT];
+    QReg qreg[NR];
+    float qscale[NR];  // fp8 q: the row's scale times the score scale (log2 units)
+    int pos[NR];
+    int64_t rowid[NR];
+    bool row_ok[NR];
     // tree verification masks: span token k is visible to a row only where
     // bit k of its token's mask is set (spans of at most 64 tokens)
     const int span_start = L - nspan;
     const bool tree = td.flags == 0 && nspan <= 64 && a.hdr[HDR_TREE] != 0;
-    uint64_t tbits[NT];
+    uint64_t tbits[NR];
 #pragma unroll
-    for (int r = 0; r < NT; ++r) {
+    for (int r = 0; r < NR; ++r) {
         const int rr = 16 * r + n;
         const int qj = rr / G;  // token of the span (group tile: member)
         row_ok[r] = rr < nrows;
@@ -874,10 +877,10 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     // most blocks need neither a row reduction nor a rescale. thr is kLazy
     // once a row has a reference and -inf before its first visible key.
     constexpr float kLazy = 8.f;
-    f32x4 o[NT][D / 16];
-    float m_use[NT], thr[NT], l_run[NT];
+    f32x4 o[NR][D / 16];
+    float m_use[NR], thr[NR], l_run[NR];
 #pragma unroll
-    for (int r = 0; r < NT; ++r) {
+    for (int r = 0; r < NR; ++r) {
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) o[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m_use[r] = 0.f;
@@ -918,41 +921,56 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
                                                     __builtin_bit_cast(int, my_vs), i));
             }
-            typename std::conditional<kv == KV_F32, float[NT][4], s16x4[NT]>::type pk;
+            // The row tiles' steps are laid out phase by phase (all
+            // products, all scores, one shared test for a reference move,
+            // all weights, all P.V products), so the scheduler can overlap
+            // one tile's matrix-core work with another's vector work.
+            f32x4 sc[NR];
 #pragma unroll
-            for (int r = 0; r < NT; ++r) {
-                if (r >= nrt) break;  // row tiles without rows (wave-uniform)
-                const f32x4 sc = cur.qk(qreg[r]);
-                float x[4];  // scores relative to the reference
+            for (int r = 0; r < NR; ++r) sc[r] = cur.qk(qreg[r]);
+            float x[NR][4];  // scores relative to the reference
+            float mx[NR];
+            bool up = false;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
                 const float cr = kv == KV_FP8Q ? c * qscale[r] : c;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = fmaf(sc[e], cr, -m_use[r]);
+                for (int e = 0; e < 4; ++e) x[r][e] = fmaf(sc[r][e], cr, -m_use[r]);
                 if (!full) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = t0 + e, k = t - span_start;
                         const bool vis = t <= pos[r] && (k < 0 || ((tbits[r] >> (k & 63)) & 1u));
-                        x[e] = vis ? x[e] : -INFINITY;
+                        x[r][e] = vis ? x[r][e] : -INFINITY;
                     }
                 }
-                const float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-                if (__builtin_amdgcn_ballot_w64(mx > thr[r]) != 0) {
+                mx[r] = fmaxf(fmaxf(x[r][0], x[r][1]), fmaxf(x[r][2], x[r][3]));
+                up |= mx[r] > thr[r];
+            }
+            if (__builtin_amdgcn_ballot_w64(up) != 0) {
+#pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    if (__builtin_amdgcn_ballot_w64(mx[r] > thr[r]) == 0) continue;
                     // move the reference of the tile's rows up to their maxima
-                    const float rm = row_max(mx);
+                    const float rm = row_max(mx[r]);
                     const bool had = thr[r] != -INFINITY;
                     const float delta = had ? fmaxf(rm, 0.f) : (rm == -INFINITY ? 0.f : rm);
                     const float alpha = had ? fexp2(-delta) : 1.f;  // o, l are 0 before
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) x[e] -= delta;
+                    for (int e = 0; e < 4; ++e) x[r][e] -= delta;
                     m_use[r] += delta;
                     if (rm != -INFINITY) thr[r] = kLazy;
                     l_run[r] *= alpha;
 #pragma unroll
                     for (int dt = 0; dt < D / 16; ++dt) o[r][dt] *= alpha;
                 }
+            }
+            typename std::conditional<kv == KV_F32, float[NR][4], s16x4[NR]>::type pk;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
                 float p[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) p[e] = fexp2(x[e]);
+                for (int e = 0; e < 4; ++e) p[e] = fexp2(x[r][e]);
                 l_run[r] += (p[0] + p[1]) + (p[2] + p[3]);
                 if constexpr (kv == KV_F32) {
 #pragma unroll
@@ -966,8 +984,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             // zero V slots past the context (NaN there must not reach P.V)
             if (!full) cur.mask_v(L - t0);
 #pragma unroll
-            for (int r = 0; r < NT; ++r)
-                if (r < nrt) cur.pv(pk[r], o[r]);
+            for (int r = 0; r < NR; ++r) cur.pv(pk[r], o[r]);
         };
         auto consume = [&](T& cur, int i) {
             if constexpr (kFp8Cache && NT > 1) {
@@ -1015,7 +1032,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     const bool whole = j == 0 && take == td.nb;
     const int64_t slot = (int64_t)piece * 2 + (j > 0 ? SLOT_HEAD : SLOT_TAIL);
 #pragma unroll
-    for (int r = 0; r < NT; ++r) {
+    for (int r = 0; r < NR; ++r) {
         // row totals: l summed over the four lane groups that share a row
         const float l = row_sum(l_run[r]);
         const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -1062,6 +1079,23 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     }
 }
 
+// A wide segment, with the count of row tiles that hold rows made a
+// compile-time constant.
+template <int kv, int D, int NT, bool kOnce>
+__device__ __forceinline__ void run_wide_segment(const AttnArgs& a, const TileDesc& td,
+                                                 const int kvh, const int j, const int take,
+                                                 const int piece) {
+    const int nrt = (td.ntok * a.group + 15) >> 4;
+    if (nrt <= 1)
+        run_segment<kv, D, NT, 1, kOnce>(a, td, kvh, j, take, piece);
+    else if (NT == 2 || nrt == 2)
+        run_segment<kv, D, NT, (NT >= 2 ? 2 : 1), kOnce>(a, td, kvh, j, take, piece);
+    else if (nrt == 3)
+        run_segment<kv, D, NT, (NT >= 3 ? 3 : 1), kOnce>(a, td, kvh, j, take, piece);
+    else
+        run_segment<kv, D, NT, NT, kOnce>(a, td, kvh, j, take, piece);
+}
+
 // One wave per workgroup; wave w streams pieces w, w + grid, ... of its
 // stream (tiles of NT row tiles).
 template <int kv, int D, int NT>
@@ -1078,7 +1112,13 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
         int left = (int)min((int64_t)R, (int64_t)B - (int64_t)(v / Hkv) * R);
         while (left > 0) {
             const int take = min(left, td.nb - j);
-            run_segment<kv, D, NT>(a, td, kvh, j, take, v);
+            if constexpr (NT == 1) {
+                run_segment<kv, D, 1, 1, true>(a, td, kvh, j, take, v);
+            } else if (td.flags == TILE_GROUP) {
+                run_wide_segment<kv, D, NT, true>(a, td, kvh, j, take, v);
+            } else {
+                run_wide_segment<kv, D, NT, false>(a, td, kvh, j, take, v);
+            }
             left -= take;
             j = 0;
             ++t;
