@@ -142,3 +142,16 @@ def test_missing_library_fails_loudly(tmp_path):
             pa.load_library(str(tmp_path / "nope.so"))
         finally:
             pa._lib = pa._lib_saved
+
+
+def test_tile_limit_is_reported_before_any_launch():
+    """A decode call holds one tile per sequence, up to 8192; beyond that
+    the library answers PA_ENOTSUP before touching any pointer."""
+    lib = _lib()
+    s = _shape()
+    F = 0x1000
+    ok = lib.pa_workspace_bytes(ctypes.byref(s), 8192, 8192, 100, 1)
+    assert ok > 0
+    rc = lib.pa_paged_attn_decode(ctypes.byref(s), F, None, F, F, F, None, None, F, F, 8193, 100,
+                                  0.1, F, 1 << 40, None)
+    assert rc == pa.PA_ENOTSUP
