@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "pa_internal.h"
 #include "pagedattn_blocks.h"
 
@@ -29,6 +31,7 @@ struct Layout {
     int waves[pa::NUM_STREAMS] = {0, 0};
     int64_t max_tiles = 0;
     int64_t max_pieces[pa::NUM_STREAMS] = {0, 0};
+    int64_t max_splits = 0;  // bound of the cut-segment list
     size_t off_tiles = 0, off_splits = 0, total = 0;
     size_t off_pieces[pa::NUM_STREAMS] = {0, 0};
     size_t off_lse[pa::NUM_STREAMS] = {0, 0};
@@ -91,12 +94,14 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     // wide: spans' tiles, then shared-prefix groups' tiles (at most one per
     // group plus one per members_per_tile members, each sequence in at most
     // one group)
+    // (spans are disjoint, so no stream has more tiles than query tokens)
+    const int64_t T = num_tokens;
     const int64_t tiles_of[pa::NUM_STREAMS] = {
-        (spans ? (int64_t)num_seqs + cdiv(num_tokens, l.wide_tokens) : 0) +
+        (spans ? std::min((int64_t)num_seqs + cdiv(num_tokens, l.wide_tokens), T) : 0) +
             (l.cascade ? 2 * (int64_t)num_seqs : 0),
         // narrow: one per sequence, or every span cut into narrow tiles
         spans || decode ? (int64_t)num_seqs
-                        : (int64_t)num_seqs + cdiv(num_tokens, l.narrow_tokens)};
+                        : std::min((int64_t)num_seqs + cdiv(num_tokens, l.narrow_tokens), T)};
     l.max_tiles = tiles_of[0] + tiles_of[1];
     const int64_t blocks_per_tile = cdiv(max_context_len > 0 ? max_context_len : 1, PA_BLOCK_SIZE);
     size_t off = align_up(sizeof(int32_t) * pa::HDR_WORDS);
@@ -115,9 +120,12 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
         int64_t mp = H * per_head;
         if (tiles_of[st] == 0) mp = 0;
         l.max_pieces[st] = mp;
-        splits += mp;
+        // a cut segment holds an inner piece boundary of its substream (at
+        // most per_head - 1 each), and each (tile, KV head) is one segment
+        if (mp > 0) splits += std::min(mp - H, tiles_of[st] * H);
     }
-    l.off_splits = off;  // every cut segment holds a piece boundary of its stream
+    l.max_splits = splits;
+    l.off_splits = off;
     off = align_up(off + sizeof(pa::SplitSeg) * (size_t)(splits > 0 ? splits : 1));
     l.off_tree = off;
     off = align_up(off + sizeof(uint64_t) * (size_t)(num_tokens > 0 ? num_tokens : 1));
@@ -222,6 +230,7 @@ int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl
         pl.pieces[st] = (pa::PieceStart*)(ws + l.off_pieces[st]);
     }
     pl.splits = (pa::SplitSeg*)(ws + l.off_splits);
+    pl.max_splits = l.max_splits;
     pl.hdr = (int32_t*)ws;
     pl.tree_mask = grp.tree_mask;
     pl.tree_ws = (uint64_t*)(ws + l.off_tree);
@@ -322,11 +331,9 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
         ma.num_kv_heads = s->num_kv_heads;
         ma.group = s->num_q_heads / s->num_kv_heads;
         ma.wide_nt = pa::wide_tiles(s->kv_dtype);
-        const int64_t splits = l.max_pieces[0] + l.max_pieces[1];
-        ma.max_splits = (int32_t)splits;
-        int64_t records = splits > 1 ? splits : 0;  // one piece cuts nothing
+        ma.max_splits = (int32_t)l.max_splits;
+        int64_t records = l.max_splits;
         if (l.cascade) {
-            ma.max_splits = (int32_t)records;
             ma.cas_recs = (const pa::CascadeRec*)(ws + l.off_cas_recs);
             for (int k = 0; k < 2; ++k) {
                 ma.cas_lse[k] = (const float*)(ws + l.off_cas_lse[k]);

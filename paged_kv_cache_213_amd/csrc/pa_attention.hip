@@ -713,7 +713,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     // 4. segments cut by a piece boundary, for the merge pass (a segment is
     //    cut iff its first and last blocks fall in different pieces of its
     //    KV head's substream); cascade parts are combined per member (5.)
-    const int64_t max_splits = a.max_pieces[0] + a.max_pieces[1];
+    const int64_t max_splits = a.max_splits;
     for (int sg = threadIdx.x; sg < ntiles * H; sg += kPlanThreads) {
         const int t = sg / H, h = sg % H;
         const TileDesc td = a.tiles[t];

@@ -137,7 +137,8 @@ struct PlanArgs {
     int64_t max_pieces[NUM_STREAMS];
     TileDesc* tiles;
     PieceStart* pieces[NUM_STREAMS];
-    SplitSeg* splits;  // [max_pieces of both streams] segments the merge completes
+    SplitSeg* splits;    // [max_splits] segments the merge completes
+    int64_t max_splits;  // at most one per (tile, KV head), one per inner piece boundary
     int32_t* hdr;
     // shared-prefix groups (num_groups 0: none)
     int32_t num_groups;
