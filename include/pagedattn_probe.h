@@ -19,8 +19,10 @@ extern "C" {
 #endif
 
 /* Read `bytes` (a multiple of 16, 16-byte aligned) of `buf` once with
- * coalesced nontemporal 16-byte loads (the load kind the attention kernels
- * use for K/V); `sink` receives at most a few words so the loads
+ * nontemporal 16-byte loads (the load kind the attention kernels use for
+ * K/V), one wave per SIMD, each wave reading whole contiguous 8 KB chunks:
+ * the fastest plain read of this device, an upper bound for the gathers of
+ * the attention kernels. `sink` receives at most a few words so the loads
  * cannot be optimized away (it needs room for 8 words per compute unit). */
 int pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 

@@ -772,12 +772,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 #ifndef PA_WIDE_SCHED_BARRIER
 #define PA_WIDE_SCHED_BARRIER 1
 #endif
+// K/V blocks in flight per wave beyond the one in use. Both kernels run one
+// wave per SIMD; the narrow one keeps two blocks in flight, the wide one,
+// whose blocks also feed more row tiles, one.
 #ifndef PA_PREFETCH
-#define PA_PREFETCH 1
+#define PA_PREFETCH 2
 #endif
-// K/V blocks in flight per wave beyond the one in use: the narrow kernel
-// hides latency with two waves per SIMD; the wide kernel runs one wave per
-// SIMD with registers to spare, and its group tiles stream long prefixes.
 #ifndef PA_WIDE_PREFETCH
 #define PA_WIDE_PREFETCH 1
 #endif
@@ -1357,10 +1357,12 @@ __global__ void fp8_decode_kernel(const uint8_t* in, float* out, int n) {
 // ---- launch configuration ----------------------------------------------------
 
 // Waves per SIMD of the persistent narrow grid (0: as many as fit). Its
-// registers would allow three; two keep more of each wave's loads in flight
-// per byte of cache and measured faster.
+// registers would allow two or three. One wave per SIMD with two blocks in
+// flight beyond the one in use measured fastest: half the pieces of two
+// waves per SIMD, so fewer segments are cut (a cheaper merge) and fewer
+// waves restart their block ring at a segment boundary.
 #ifndef PA_NARROW_MAX_WAVES
-#define PA_NARROW_MAX_WAVES 2
+#define PA_NARROW_MAX_WAVES 1
 #endif
 
 template <typename K>

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "pagedattn_probe.h"
 
 namespace {
@@ -17,19 +19,27 @@ __device__ __forceinline__ u32x4_t ld_stream(const u32x4_t* p) {
     return __builtin_nontemporal_load(p);
 }
 
-__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4_t* __restrict__ src,
-                                                          int64_t n16, uint32_t* sink) {
+// One wave per workgroup; wave w reads 8 KB chunks w, w + grid, ... whole
+// (eight 16-byte loads per lane, all requested before any is used), then
+// the bytes past the last whole chunk. Contiguous 8 KB per wave is the read
+// shape this device serves fastest (a grid-stride loop of 16-byte loads,
+// each wave touching four places 16 MB apart, reads about 15% slower).
+constexpr int kChunk16 = 512;  // 16-byte elements per 8 KB chunk
+__global__ __launch_bounds__(64) void stream_read_kernel(const u32x4_t* __restrict__ src,
+                                                         int64_t n16, uint32_t* sink) {
+    const int lane = threadIdx.x;
     uint32_t acc = 0;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // four independent 16-byte loads in flight per thread per iteration
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4_t a = ld_stream(src + i), b = ld_stream(src + i + stride),
-                      c = ld_stream(src + i + 2 * stride), d = ld_stream(src + i + 3 * stride);
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^
-               d.y ^ d.z ^ d.w;
+    const int64_t nchunks = n16 / kChunk16;
+    for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+        const u32x4_t* p = src + c * kChunk16 + lane;
+        u32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = ld_stream(p + 64 * u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
     }
-    for (; i < n16; i += stride) {
+    for (int64_t i = nchunks * kChunk16 + (int64_t)blockIdx.x * 64 + lane; i < n16;
+         i += (int64_t)gridDim.x * 64) {
         const u32x4_t a = ld_stream(src + i);
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
@@ -57,8 +67,14 @@ int grid_for(int64_t n16) {
 extern "C" int pa_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
     if (!buf || !sink || (bytes & 15) || ((uintptr_t)buf & 15)) return PA_EINVAL;
     const int64_t n16 = (int64_t)(bytes / 16);
-    hipLaunchKernelGGL(stream_read_kernel, dim3(grid_for(n16)), dim3(256), 0,
-                       (hipStream_t)stream, (const u32x4_t*)buf, n16, sink);
+    // one wave per SIMD
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t need = (n16 + 63) / 64;
+    const int grid = (int)std::min<int64_t>((int64_t)cus * 4, need > 0 ? need : 1);
+    hipLaunchKernelGGL(stream_read_kernel, dim3(grid), dim3(64), 0, (hipStream_t)stream,
+                       (const u32x4_t*)buf, n16, sink);
     return hipGetLastError() == hipSuccess ? PA_OK : PA_EHIP;
 }
 
