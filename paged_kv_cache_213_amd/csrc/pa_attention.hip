@@ -781,6 +781,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 #ifndef PA_WIDE_PREFETCH
 #define PA_WIDE_PREFETCH 1
 #endif
+// A build with two wide blocks in flight faulted the GPU on the full
+// parallel-sampling batch with shared-prefix groups (fp8 cache); its wide
+// kernel spilled 212 VGPRs to AGPRs and 47 SGPRs. The cause is not known,
+// so only one block ahead is allowed.
+#if PA_WIDE_PREFETCH != 1
+#error "PA_WIDE_PREFETCH other than 1 is disabled (see above)"
+#endif
 
 // Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
 // each block through the block table, S = K q^T on the matrix cores, online
