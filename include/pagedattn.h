@@ -82,8 +82,8 @@ typedef enum pa_status {
  * positive multiple of 16 (pieces of that many tokens). Query rows are
  * grouped into tiles: a span of at most 16 / G tokens (every decode) is one
  * narrow tile of G * n_i rows; a longer span is cut into wide tiles of
- * 64 / G tokens (32 / G for F32). A call may hold at most 8192 tiles,
- * counted as 2 * num_seqs + ceil(num_q_tokens / (64 / G)) for a hybrid call
+ * 32 / G tokens. A call may hold at most 8192 tiles,
+ * counted as 2 * num_seqs + ceil(num_q_tokens / (32 / G)) for a hybrid call
  * and num_seqs for a decode call, plus 2 * num_seqs when cascade is 1;
  * beyond that it returns PA_ENOTSUP. */
 typedef struct pa_shape {

@@ -8,7 +8,7 @@
 //              trace on "03 -- Engines Papers" (whiteboard test), done on
 //              the device. Query rows are grouped into tiles: a narrow tile
 //              holds up to 16 rows (G query heads x 16/G tokens of one
-//              span); a wide tile holds 4 x 16 rows (2 x 16 for fp32) of a
+//              span); a wide tile holds 2 x 16 rows of a
 //              chunked-prefill span. Every (tile, KV head) pair is a segment
 //              of 16-token key blocks; the segments of each tile class form
 //              one stream of blocks, cut into pieces of equal size (one per
@@ -821,8 +821,9 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     // head kvh*G + (row % G)
     QReg qreg[NR];
     float qscale[NR];  // fp8 q: the row's scale times the score scale (log2 units)
-    int pos[NR];
-    int64_t rowid[NR];
+    // output row index of row tile r (token row * Hq + head; the output of a
+    // call is far below 2^31 rows, so 32 bits)
+    int rowid[NR];
     bool row_ok[NR];
     // tree verification masks: span token k is visible to a row only where
     // bit k of its token's mask is set (spans of at most 64 tokens)
@@ -841,11 +842,9 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             if (row_ok[r]) i = a.group_members[td.qtok0 + qj];
             row_ok[r] = i >= 0 && i < a.num_seqs && a.cas_prefix[i] == td.nb;
             const int qrow = row_ok[r] ? (a.qsl ? a.qsl[i] : i) : 0;
-            pos[r] = row_ok[r] ? L - 1 : -1;
-            rowid[r] = (int64_t)qrow * Hq + kvh * G + (rr - qj * G);
+            rowid[r] = qrow * Hq + kvh * G + (rr - qj * G);
         } else {
-            pos[r] = row_ok[r] ? L - nspan + td.qtok0 + qj : -1;
-            rowid[r] = (int64_t)(qs + td.qtok0 + qj) * Hq + kvh * G + (rr - qj * G);
+            rowid[r] = (qs + td.qtok0 + qj) * Hq + kvh * G + (rr - qj * G);
         }
         tbits[r] = (tree && row_ok[r]) ? a.tree[qs + td.qtok0 + qj] : ~0ull;
         // q operand (B of S = K q^T), holding the row's dims in the same order
@@ -853,10 +852,10 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         // 64(m/2) + 16g + 8(m%2) + e for MFMA step m
         qscale[r] = 1.f;
         if constexpr (kv == KV_FP8Q) {
-            const uint16_t* qp = (const uint16_t*)a.q + (row_ok[r] ? rowid[r] : 0) * D;
+            const uint16_t* qp = (const uint16_t*)a.q + (int64_t)(row_ok[r] ? rowid[r] : 0) * D;
             qscale[r] = a.scale_log2 * quantize_q_fp8<D>(qp, row_ok[r], g, qreg[r]);
         } else if constexpr (kv == KV_F32) {
-            const float* qp = (const float*)a.q + rowid[r] * D + 4 * g;
+            const float* qp = (const float*)a.q + (int64_t)rowid[r] * D + 4 * g;
 #pragma unroll
             for (int m = 0; m < D / 16; ++m) {
                 float4 x = row_ok[r] ? *(const float4*)(qp + 16 * m)
@@ -867,7 +866,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 qreg[r][4 * m + 3] = x.w;
             }
         } else {
-            const uint16_t* qp = (const uint16_t*)a.q + rowid[r] * D;
+            const uint16_t* qp = (const uint16_t*)a.q + (int64_t)rowid[r] * D;
 #pragma unroll
             for (int m = 0; m < D / 32; ++m) {
                 const int d0 =
@@ -876,6 +875,13 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             }
         }
     }
+
+    // the last key position row tile r's row of this lane sees (-1: no row);
+    // recomputed where a mask needs it rather than held through the loop
+    auto pos_of = [&](int r) {
+        const int qj = (16 * r + n) / G;
+        return !row_ok[r] ? -1 : td.flags == TILE_GROUP ? L - 1 : L - nspan + td.qtok0 + qj;
+    };
 
     // Online softmax with a lazily moved reference (log2 units): scores are
     // taken relative to m_use, the row maximum when the reference was last
@@ -947,7 +953,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = t0 + e, k = t - span_start;
-                        const bool vis = t <= pos[r] && (k < 0 || ((tbits[r] >> (k & 63)) & 1u));
+                        const bool vis = t <= pos_of(r) && (k < 0 || ((tbits[r] >> (k & 63)) & 1u));
                         x[r][e] = vis ? x[r][e] : -INFINITY;
                     }
                 }
@@ -1047,7 +1053,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         if (whole && td.flags != 0) {
             // a whole cascade part: normalized output and lse per row
             const int kind = td.flags == TILE_GROUP ? CAS_PRE : CAS_SUF;
-            float* bo = a.cas_o[kind] + rowid[r] * D;
+            float* bo = a.cas_o[kind] + (int64_t)rowid[r] * D;
 #pragma unroll
             for (int dt = 0; dt < D / 16; ++dt)
                 *(float4*)(bo + 16 * dt + 4 * g) =
@@ -1059,14 +1065,14 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             for (int dt = 0; dt < D / 16; ++dt) {
                 const int d = 16 * dt + 4 * g;
                 if constexpr (kv == KV_F32) {
-                    *(float4*)((float*)a.out + rowid[r] * D + d) =
+                    *(float4*)((float*)a.out + (int64_t)rowid[r] * D + d) =
                         make_float4(o[r][dt][0] * inv, o[r][dt][1] * inv, o[r][dt][2] * inv,
                                     o[r][dt][3] * inv);
                 } else {
                     uint2 w;
                     w.x = pack_bf16x2(o[r][dt][0] * inv, o[r][dt][1] * inv);
                     w.y = pack_bf16x2(o[r][dt][2] * inv, o[r][dt][3] * inv);
-                    *(uint2*)((uint16_t*)a.out + rowid[r] * D + d) = w;
+                    *(uint2*)((uint16_t*)a.out + (int64_t)rowid[r] * D + d) = w;
                 }
             }
             if (a.lse && g == 0)
@@ -1149,17 +1155,18 @@ __global__ __launch_bounds__(64) PA_NARROW_OCCUPANCY void attention_narrow(AttnA
     attention_body<kv, D, 1>(a);
 }
 
-// Wide tiles of chunked-prefill spans: matrix-core bound, one wave per SIMD.
+// Wide tiles of chunked-prefill spans and shared-prefix groups. With two
+// row tiles per wide tile, the bf16 and fp8 kernels are built for two waves
+// per SIMD: they then fit in 256 VGPRs with no AGPR or scratch spill space.
+// The f32 kernel keeps the compiler's own choice (its operands take twice
+// the registers).
 #ifndef PA_WIDE_MIN_WAVES
-#define PA_WIDE_MIN_WAVES 0
+#define PA_WIDE_MIN_WAVES 2
 #endif
-#if PA_WIDE_MIN_WAVES > 0
-#define PA_WIDE_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PA_WIDE_MIN_WAVES, 8)))
-#else
-#define PA_WIDE_OCCUPANCY
-#endif
+constexpr int wide_min_waves(int kv) { return kv == KV_F32 ? 1 : PA_WIDE_MIN_WAVES; }
 template <int kv, int D>
-__global__ __launch_bounds__(64) PA_WIDE_OCCUPANCY void attention_wide(AttnArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(wide_min_waves(kv), 8))) void
+attention_wide(AttnArgs a) {
     attention_body<kv, D, wide_tiles(kv)>(a);
 }
 

@@ -61,20 +61,19 @@ struct SplitSeg {
     int32_t pad[2];
 };
 
-// Two block streams: tiles of multi-token spans (wide: up to 64 rows, four
+// Two block streams: tiles of multi-token spans (wide: up to 32 rows, two
 // MFMA row tiles share each K/V block) and single-token tiles (narrow: up to
 // 16 rows). Each is cut into its own pieces and run by its own launch.
 enum { STREAM_WIDE = 0, STREAM_NARROW = 1, NUM_STREAMS = 2 };
-// 16-row MFMA tiles in a wide tile (fp32 operands take twice the registers)
+// 16-row MFMA tiles in a wide tile. Two keep the bf16 and fp8 wide kernels
+// within 256 VGPRs at two waves per SIMD, with nothing spilled to AGPRs or
+// scratch; four (the K/V bytes then serve twice the rows) needed 256 VGPRs
+// plus 136-160 AGPRs of spill space and SGPR spills.
 #ifndef PA_WIDE_TILES
-#define PA_WIDE_TILES 4
+#define PA_WIDE_TILES 2
 #endif
-// An fp8 cache uses two: its wide kernel then needs no AGPRs (239 VGPRs
-// against 256 + 142 AGPRs with four) and two waves fit per SIMD, which
-// measured faster on the fp8 parallel-sampling batch with shared-prefix
-// groups (attention 119.7 us against 124.7 us).
 #ifndef PA_WIDE_TILES_FP8
-#define PA_WIDE_TILES_FP8 2
+#define PA_WIDE_TILES_FP8 PA_WIDE_TILES
 #endif
 // Kernel kinds: the cache dtype, or an fp8 cache whose S = K q^T runs on
 // the fp8 matrix cores (pa_shape.fp8_qk).
@@ -132,7 +131,7 @@ struct PlanArgs {
     int32_t num_tokens;
     int32_t max_context_len;  // contexts are clamped to this
     int32_t narrow_tokens;    // query tokens per narrow tile (16 / G, 1 for decode)
-    int32_t wide_tokens;      // query tokens per wide tile (64 / G)
+    int32_t wide_tokens;      // query tokens per wide tile (16 * row tiles / G)
     int32_t num_kv_heads;
     int32_t part_blocks;  // blocks per piece; 0 = balance over the stream's waves
     int32_t waves[NUM_STREAMS];  // resident waves of each stream's kernel
