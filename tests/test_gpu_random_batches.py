@@ -1,0 +1,48 @@
+"""Seeded random hybrid batches on the GPU against the CPU oracle.
+
+Each case draws a batch shape the fixed configurations do not pin down: a
+mix of single-token decodes and chunked-prefill spans of ragged lengths
+(the hybrid batch of "03 -- Engines Papers", section 3), context lengths
+from one key to a few thousand, GQA group sizes from 1 to 16, both head
+sizes, the three cache kinds and several partition sizes (split-KV pieces
+merged by log-sum-exp, section 12). The oracle and the tolerances are those
+of every other parity test."""
+import numpy as np
+import pytest
+
+from paged_kv_cache_213_amd import workloads as W
+from tests.gpu_common import check_step
+
+pytestmark = pytest.mark.gpu
+
+KINDS = [("bf16", "bf16"), ("bf16", "fp8"), ("f32", "f32")]
+
+
+def _random_batch(seed: int):
+    rng = np.random.default_rng(seed)
+    S = int(rng.integers(1, 25))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2]))
+    D = int(rng.choice([64, 128]))
+    q_dtype, kv_dtype = KINDS[seed % len(KINDS)]
+    P = int(rng.choice([0, 16, 48, 256, 512]))
+    # context lengths: short, block-edge and long ones mixed
+    pool = np.concatenate([rng.integers(1, 40, S), rng.integers(1, 3000, S),
+                           16 * rng.integers(1, 40, S)])
+    lens = rng.choice(pool, S).astype(np.int32)
+    # most sequences decode one token; some carry a span up to 80 tokens
+    span = rng.random(S) < 0.35
+    ql = np.where(span, rng.integers(2, 81, S), 1).astype(np.int32)
+    ql = np.minimum(ql, lens).astype(np.int32)
+    return W.custom_workload(lens, ql, num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D,
+                             q_dtype=q_dtype, kv_dtype=kv_dtype, partition_size=P,
+                             seed=seed, name=f"random-{seed}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_hybrid_batch(seed):
+    wl = _random_batch(seed)
+    e, _, _ = check_step(wl, hybrid=True)
+    print(f"seed {seed}: S={wl.num_seqs} T={wl.num_tokens} Hq={wl.num_q_heads} "
+          f"Hkv={wl.num_kv_heads} D={wl.head_dim} {wl.q_dtype}/{wl.kv_dtype} "
+          f"P={wl.partition_size}: {e}", flush=True)
