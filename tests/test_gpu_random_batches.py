@@ -46,3 +46,51 @@ def test_random_hybrid_batch(seed):
     print(f"seed {seed}: S={wl.num_seqs} T={wl.num_tokens} Hq={wl.num_q_heads} "
           f"Hkv={wl.num_kv_heads} D={wl.head_dim} {wl.q_dtype}/{wl.kv_dtype} "
           f"P={wl.partition_size}: {e}", flush=True)
+
+
+def _random_sharing_batch(seed: int):
+    """Random shared-prefix groups (copy-on-write sharing of whole leading
+    blocks, "03 -- Engines Papers", section 2) next to unshared sequences;
+    members' own tokens lie past their group's prefix."""
+    rng = np.random.default_rng(1000 + seed)
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2]))
+    D = int(rng.choice([64, 128]))
+    q_dtype, kv_dtype = KINDS[seed % len(KINDS)]
+    P = int(rng.choice([0, 16, 48, 512]))
+    ngroups = int(rng.integers(1, 5))
+    groups, prefix, lens, ql = [], [], [], []
+    for _ in range(ngroups):
+        pb = int(rng.integers(1, 41))
+        members = []
+        for _ in range(int(rng.integers(2, 21))):
+            n = 1 if rng.random() < 0.85 else int(rng.integers(2, 40))
+            L = 16 * pb + n + int(rng.integers(0, 600))
+            members.append(len(lens))
+            lens.append(L)
+            ql.append(n)
+        groups.append(members)
+        prefix.append(pb)
+    for _ in range(int(rng.integers(0, 8))):  # sequences outside every group
+        L = int(rng.integers(1, 2000))
+        lens.append(L)
+        ql.append(1 if rng.random() < 0.8 else int(rng.integers(1, min(L, 60) + 1)))
+    wl = W.custom_workload(np.array(lens, np.int32), np.array(ql, np.int32),
+                           num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, q_dtype=q_dtype,
+                           kv_dtype=kv_dtype, partition_size=P, seed=seed,
+                           name=f"random-sharing-{seed}")
+    for members, pb in zip(groups, prefix):
+        lead = wl.block_tables[members[0], :pb].copy()
+        for i in members:
+            wl.block_tables[i, :pb] = lead
+    return wl, (groups, prefix)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_sharing_batch_cascade(seed):
+    wl, groups = _random_sharing_batch(seed)
+    e, _, _ = check_step(wl, groups=groups)
+    print(f"seed {seed}: S={wl.num_seqs} T={wl.num_tokens} Hq={wl.num_q_heads} "
+          f"Hkv={wl.num_kv_heads} D={wl.head_dim} {wl.q_dtype}/{wl.kv_dtype} "
+          f"P={wl.partition_size} groups={[len(g) for g in groups[0]]} "
+          f"prefix blocks={groups[1]}: {e}", flush=True)
