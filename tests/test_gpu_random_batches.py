@@ -94,3 +94,16 @@ def test_random_sharing_batch_cascade(seed):
           f"Hkv={wl.num_kv_heads} D={wl.head_dim} {wl.q_dtype}/{wl.kv_dtype} "
           f"P={wl.partition_size} groups={[len(g) for g in groups[0]]} "
           f"prefix blocks={groups[1]}: {e}", flush=True)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_tree_batch(seed):
+    """Random batches whose spans are candidate trees of draft tokens (one
+    ancestor-or-self word per token; spans past 64 tokens stay causal),
+    "03 -- Engines Papers", sections 5 to 7."""
+    from tests.test_gpu_tree import _tree_step
+    wl = _random_batch(100 + seed)
+    masks = W.batch_tree_masks(wl.query_lens, seed=seed)
+    e, _, _ = _tree_step(wl, masks)
+    print(f"seed {seed}: S={wl.num_seqs} T={wl.num_tokens} Hq={wl.num_q_heads} "
+          f"{wl.q_dtype}/{wl.kv_dtype} P={wl.partition_size}: {e}", flush=True)
