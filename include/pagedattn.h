@@ -85,7 +85,8 @@ typedef enum pa_status {
  * 32 / G tokens. A call may hold at most 8192 tiles,
  * counted as 2 * num_seqs + ceil(num_q_tokens / (32 / G)) for a hybrid call
  * and num_seqs for a decode call, plus 2 * num_seqs when cascade is 1;
- * beyond that it returns PA_ENOTSUP. */
+ * beyond that it returns PA_ENOTSUP, as it does when num_q_tokens *
+ * num_q_heads reaches 2^31 - 1 (output rows are indexed with 32 bits). */
 typedef struct pa_shape {
     int32_t num_q_heads;        /* Hq */
     int32_t num_kv_heads;       /* Hkv */

@@ -169,6 +169,8 @@ int check_batch(const pa_shape* s, const int32_t* context_lens, const int32_t* q
     if ((int64_t)max_context_len > (int64_t)PA_BLOCK_SIZE * s->max_blocks_per_seq)
         return PA_EINVAL;
     if (num_seqs > 0 && !context_lens) return PA_EINVAL;
+    // the kernels index output rows (query token x query head) with 32 bits
+    if ((int64_t)num_tokens * s->num_q_heads >= (int64_t)INT32_MAX) return PA_ENOTSUP;
     *l = make_layout(s, num_seqs, num_tokens, max_context_len, max_query_len, qsl == nullptr);
     if (l->max_tiles > pa::kMaxTiles) return PA_ENOTSUP;
     if (!workspace || workspace_bytes < l->total) return PA_EWORKSPACE;

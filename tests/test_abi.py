@@ -155,3 +155,15 @@ def test_tile_limit_is_reported_before_any_launch():
     rc = lib.pa_paged_attn_decode(ctypes.byref(s), F, None, F, F, F, None, None, F, F, 8193, 100,
                                   0.1, F, 1 << 40, None)
     assert rc == pa.PA_ENOTSUP
+
+
+def test_output_row_limit_is_reported_before_any_launch():
+    """Output rows (query tokens x query heads) are indexed with 32 bits in
+    the kernels: a call with 2^31 - 1 or more rows answers PA_ENOTSUP."""
+    lib = _lib()
+    s = _shape()
+    s.num_q_heads = s.num_kv_heads = 1 << 18
+    F = 0x1000
+    rc = lib.pa_paged_attn_decode(ctypes.byref(s), F, None, F, F, F, None, None, F, F, 8192, 100,
+                                  0.1, F, 1 << 40, None)
+    assert rc == pa.PA_ENOTSUP
