@@ -388,7 +388,7 @@ def main():
     # the roofline counts what the method must read: the logical bytes, or
     # with cascade the group prefixes once per group tile
     G = wl.num_q_heads // wl.num_kv_heads
-    mpt = max(1, (16 * (2 if wl.kv_dtype == "f32" else 4)) // G)
+    mpt = max(1, (16 * 2) // G)  # members per group tile: two 16-row tiles of G heads each
     read_bytes = cascade_read_bytes(wl, mpt) if use_cascade else kv_bytes
     achieved = read_bytes / (att_mean / 1e3) / 1e9
     layer_ms = ms_per_step / layers
