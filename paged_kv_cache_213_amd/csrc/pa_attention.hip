@@ -769,8 +769,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
 // ---- attention ---------------------------------------------------------------
 
+// The wide kernel's block steps stay in program order (a scheduling barrier
+// between steps). A build without it gave deterministically wrong rows in
+// bf16 shared-prefix group tiles, in a kernel with no register spilling; the
+// cause is not known, so the barrier is not optional.
 #ifndef PA_WIDE_SCHED_BARRIER
 #define PA_WIDE_SCHED_BARRIER 1
+#endif
+#if PA_WIDE_SCHED_BARRIER != 1
+#error "the wide kernel's block steps must keep their scheduling barrier (see above)"
 #endif
 // K/V blocks in flight per wave beyond the one in use. Both kernels run one
 // wave per SIMD; the narrow one keeps two blocks in flight, the wide one,
