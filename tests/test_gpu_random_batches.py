@@ -86,7 +86,7 @@ def _random_sharing_batch(seed: int):
     return wl, (groups, prefix)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_sharing_batch_cascade(seed):
     wl, groups = _random_sharing_batch(seed)
     e, _, _ = check_step(wl, groups=groups)
