@@ -9,6 +9,12 @@
 #include "pa_internal.h"
 #include "pagedattn_blocks.h"
 
+// 16-row tiles of query rows in a shared-prefix group tile (at most the wide
+// tile's count)
+#ifndef PA_GROUP_ROW_TILES
+#define PA_GROUP_ROW_TILES 2
+#endif
+
 #ifndef PA_WIDE_SPANS
 #define PA_WIDE_SPANS 1
 #endif
@@ -90,7 +96,10 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     const bool spans = PA_WIDE_SPANS && !decode && max_query_len > l.narrow_tokens;
     if (!spans) l.wide_tokens = 0;
     l.cascade = s->cascade != 0;
-    l.members_per_tile = (16 * wt) / G > 1 ? (16 * wt) / G : 1;
+    {
+        const int rt = PA_GROUP_ROW_TILES < wt ? PA_GROUP_ROW_TILES : wt;  // row tiles per group tile
+        l.members_per_tile = (16 * rt) / G > 1 ? (16 * rt) / G : 1;
+    }
     // wide: spans' tiles, then shared-prefix groups' tiles (at most one per
     // group plus one per members_per_tile members, each sequence in at most
     // one group)
