@@ -160,7 +160,7 @@ int pa_plan(const pa_shape* shape, const int32_t* context_lens, const int32_t* q
  * that hit the same cached prompt -- through copy-on-write ("03 -- Engines
  * Papers", section 2). Cascade attention (same page, section 12): each
  * group's prefix is read once for all of its members, in tiles of up to
- * 16 * 4 / G members (16 * 2 / G for F32), and each member reads only the
+ * max(16 / G, 1) members, and each member reads only the
  * blocks after the prefix; the run's merge pass combines the two parts of
  * every member by log-sum-exp. The outputs are the same attention as
  * without groups, up to rounding.
@@ -242,11 +242,53 @@ int pa_kv_append(const pa_shape* shape, void* k_cache, void* v_cache, const floa
  * (the one the attention kernels use), for inspecting a cache. */
 int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream);
 
+/* Workspace introspection, for tools and tests that read a plan back from
+ * device memory. Fills *info with the bounds and byte offsets of the
+ * workspace regions that pa_plan, pa_plan_cascade and pa_plan_tree write for
+ * this batch: the same computation that pa_workspace_bytes and the plan
+ * calls make (`decode` = 1 for a plan made with query_start_loc NULL).
+ * Region contents, all int32 fields in this order:
+ *   header   [64]: tiles, cut segments, cascade records, tree flag, then per
+ *            stream s (0 wide, 1 narrow) at 4 + 4 s: blocks per KV head,
+ *            blocks per piece, pieces
+ *   tiles    [max_tiles] x 12: seq, first query token, query tokens, blocks,
+ *            context length, first query row, span tokens, flags (1 suffix,
+ *            2 group), first block, 3 unused
+ *   pieces   per stream [max_pieces] x 16: tile, KV head, first block, unused,
+ *            then a copy of that tile's 12 fields
+ *   splits   [max_splits] x 8: first row, query tokens, KV head, first and
+ *            last piece, stream, 2 unused (past the header's count: k0 = -1)
+ *   cascade  cas_seq: 6 x [num_seqs] (member prefix blocks, suffix tile,
+ *            group tile, place in the group tile, member copy, group's
+ *            first tile); cas_recs [max_cas_recs] x 8: query row, KV head,
+ *            suffix first and last piece, prefix first and last piece, place
+ *            in the group tile, unused
+ * Host only; enqueues nothing. Returns PA_OK, or PA_EINVAL for an invalid
+ * shape or size. */
+typedef struct pa_layout_info {
+    int32_t waves[2];          /* resident waves of the wide, narrow kernels */
+    int32_t narrow_tokens;     /* query tokens per narrow tile */
+    int32_t wide_tokens;       /* query tokens per wide tile (0: no spans) */
+    int32_t part_blocks;       /* partition_size / 16 (0: balanced) */
+    int32_t members_per_tile;  /* cascade members per group tile */
+    int32_t wide_row_tiles;    /* 16-row tiles of a wide slot */
+    int32_t header_words;      /* int32 words of the header */
+    int64_t max_tiles, max_pieces[2], max_splits, max_cas_recs;
+    int64_t off_tiles, off_splits, off_tree, off_cas_seq, off_cas_recs;
+    int64_t off_cas_lse[2], off_cas_o[2];
+    int64_t off_pieces[2], off_part_lse[2], off_part_o[2];
+    int64_t total;             /* bytes */
+} pa_layout_info;
+int pa_workspace_layout(const pa_shape* shape, int num_seqs, int num_q_tokens,
+                        int max_context_len, int max_query_len, int decode,
+                        pa_layout_info* info);
+
 /* Static text for a status code. */
 const char* pa_status_string(int status);
 
 /* Library ABI version (major * 100 + minor): 200 added pa_shape.cascade
- * and pa_plan_cascade; 201 added pa_plan_tree; 202 added pa_shape.fp8_qk. */
+ * and pa_plan_cascade; 201 added pa_plan_tree; 202 added pa_shape.fp8_qk;
+ * 203 added pa_workspace_layout. */
 int pa_version(void);
 
 #ifdef __cplusplus

@@ -46,6 +46,34 @@ class PagedAttentionError(RuntimeError):
     pass
 
 
+class PaLayoutInfo(ctypes.Structure):
+    """Workspace regions of a batch (pa_workspace_layout)."""
+    _fields_ = [
+        ("waves", ctypes.c_int32 * 2),
+        ("narrow_tokens", ctypes.c_int32),
+        ("wide_tokens", ctypes.c_int32),
+        ("part_blocks", ctypes.c_int32),
+        ("members_per_tile", ctypes.c_int32),
+        ("wide_row_tiles", ctypes.c_int32),
+        ("header_words", ctypes.c_int32),
+        ("max_tiles", ctypes.c_int64),
+        ("max_pieces", ctypes.c_int64 * 2),
+        ("max_splits", ctypes.c_int64),
+        ("max_cas_recs", ctypes.c_int64),
+        ("off_tiles", ctypes.c_int64),
+        ("off_splits", ctypes.c_int64),
+        ("off_tree", ctypes.c_int64),
+        ("off_cas_seq", ctypes.c_int64),
+        ("off_cas_recs", ctypes.c_int64),
+        ("off_cas_lse", ctypes.c_int64 * 2),
+        ("off_cas_o", ctypes.c_int64 * 2),
+        ("off_pieces", ctypes.c_int64 * 2),
+        ("off_part_lse", ctypes.c_int64 * 2),
+        ("off_part_o", ctypes.c_int64 * 2),
+        ("total", ctypes.c_int64),
+    ]
+
+
 def load_library(path: str = LIB_PATH):
     """Load libpagedattn.so (raises if it is missing)."""
     global _lib
@@ -82,6 +110,8 @@ def load_library(path: str = LIB_PATH):
     lib.pa_kv_append.argtypes = [S, P, P, P, P, P, P, P, I, P]
     lib.pa_fp8_e4m3fn_to_f32.restype = I
     lib.pa_fp8_e4m3fn_to_f32.argtypes = [P, P, I, P]
+    lib.pa_workspace_layout.restype = I
+    lib.pa_workspace_layout.argtypes = [S, I, I, I, I, I, ctypes.POINTER(PaLayoutInfo)]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [I]
     lib.pa_version.restype = I
@@ -142,6 +172,17 @@ def workspace_bytes(shape: PaShape, num_seqs: int, num_q_tokens: int, max_contex
                     max_query_len: int) -> int:
     return int(load_library().pa_workspace_bytes(ctypes.byref(shape), num_seqs, num_q_tokens,
                                                  max_context_len, max_query_len))
+
+
+def workspace_layout(shape: PaShape, num_seqs: int, num_q_tokens: int, max_context_len: int,
+                     max_query_len: int, decode: bool) -> PaLayoutInfo:
+    """Bounds and offsets of the workspace regions a plan writes."""
+    info = PaLayoutInfo()
+    rc = load_library().pa_workspace_layout(ctypes.byref(shape), num_seqs, num_q_tokens,
+                                            max_context_len, max_query_len, int(bool(decode)),
+                                            ctypes.byref(info))
+    _check(rc, "pa_workspace_layout")
+    return info
 
 
 def _workspace(nbytes: int, device, workspace):

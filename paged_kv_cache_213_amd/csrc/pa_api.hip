@@ -10,9 +10,12 @@
 #include "pagedattn_blocks.h"
 
 // 16-row tiles of query rows in a shared-prefix group tile (at most the wide
-// tile's count)
+// tile's count). One: builds of the wide kernel whose bf16 group tiles held
+// two row tiles gave wrong rows in the second row tile, and two such builds
+// faulted on a large parallel-sampling batch; no cause has been shown, so
+// group tiles keep to the one-row-tile path that no build has failed on.
 #ifndef PA_GROUP_ROW_TILES
-#define PA_GROUP_ROW_TILES 2
+#define PA_GROUP_ROW_TILES 1
 #endif
 
 #ifndef PA_WIDE_SPANS
@@ -526,6 +529,45 @@ int pa_copy_blocks(const pa_shape* shape, void* k_cache, void* v_cache, float* k
                                                                                   : PA_EHIP;
 }
 
+int pa_workspace_layout(const pa_shape* shape, int num_seqs, int num_q_tokens,
+                        int max_context_len, int max_query_len, int decode,
+                        pa_layout_info* info) {
+    if (!info || check_shape(shape) != PA_OK || num_seqs < 0 || num_q_tokens < 0 ||
+        max_context_len < 0)
+        return PA_EINVAL;
+    const Layout l = make_layout(shape, num_seqs, num_q_tokens, max_context_len, max_query_len,
+                                 decode != 0);
+    pa_layout_info r{};
+    for (int st = 0; st < pa::NUM_STREAMS; ++st) {
+        r.waves[st] = l.waves[st];
+        r.max_pieces[st] = l.max_pieces[st];
+        r.off_pieces[st] = (int64_t)l.off_pieces[st];
+        r.off_part_lse[st] = (int64_t)l.off_lse[st];
+        r.off_part_o[st] = (int64_t)l.off_o[st];
+    }
+    r.narrow_tokens = l.narrow_tokens;
+    r.wide_tokens = l.wide_tokens;
+    r.part_blocks = l.part_blocks;
+    r.members_per_tile = l.members_per_tile;
+    r.wide_row_tiles = pa::wide_tiles(shape->kv_dtype);
+    r.header_words = pa::HDR_WORDS;
+    r.max_tiles = l.max_tiles;
+    r.max_splits = l.max_splits;
+    r.max_cas_recs = l.max_cas_recs;
+    r.off_tiles = (int64_t)l.off_tiles;
+    r.off_splits = (int64_t)l.off_splits;
+    r.off_tree = (int64_t)l.off_tree;
+    r.off_cas_seq = (int64_t)l.off_cas_seq;
+    r.off_cas_recs = (int64_t)l.off_cas_recs;
+    for (int k = 0; k < 2; ++k) {
+        r.off_cas_lse[k] = (int64_t)l.off_cas_lse[k];
+        r.off_cas_o[k] = (int64_t)l.off_cas_o[k];
+    }
+    r.total = (int64_t)l.total;
+    *info = r;
+    return PA_OK;
+}
+
 const char* pa_status_string(int status) {
     switch (status) {
     case PA_OK: return "ok";
@@ -538,6 +580,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 202; }
+int pa_version(void) { return 203; }
 
 }  // extern "C"

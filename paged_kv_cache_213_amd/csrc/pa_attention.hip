@@ -38,6 +38,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "pa_internal.h"
@@ -1397,17 +1398,31 @@ int resident_waves_of(K kernel, int cap_per_simd) {
     return (occ > 0 ? occ : 1) * num_cu;
 }
 
+// Resident waves per (kernel instance, device, stream), queried once per
+// device and kept for the life of the process. The value depends only on
+// the kernel's resources and the device's compute-unit count, so threads
+// that race on a first query compute the same number; the table is atomic
+// so that such a race is well defined, and the first value stored is the
+// one every later call sees. Devices past kMaxDevices are queried each call.
+constexpr int kMaxDevices = 64;
 template <int kv, int D>
 int resident_waves_d(int stream) {
-    static int cached[NUM_STREAMS] = {-1, -1};  // device properties do not change
-    if (cached[stream] < 0) {
-        const int w = stream == STREAM_WIDE
-                          ? resident_waves_of(attention_wide<kv, D>, 0)
-                          : resident_waves_of(attention_narrow<kv, D>, PA_NARROW_MAX_WAVES);
-        if (w <= 0) return 0;
-        cached[stream] = w;
+    static std::atomic<int> cached[kMaxDevices][NUM_STREAMS];  // 0: not yet queried
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    std::atomic<int>* slot = dev < kMaxDevices ? &cached[dev][stream] : nullptr;
+    if (slot) {
+        const int c = slot->load(std::memory_order_acquire);
+        if (c > 0) return c;
     }
-    return cached[stream];
+    const int w = stream == STREAM_WIDE
+                      ? resident_waves_of(attention_wide<kv, D>, 0)
+                      : resident_waves_of(attention_narrow<kv, D>, PA_NARROW_MAX_WAVES);
+    if (w <= 0) return 0;
+    if (!slot) return w;
+    int expected = 0;
+    slot->compare_exchange_strong(expected, w, std::memory_order_acq_rel);
+    return slot->load(std::memory_order_acquire);
 }
 
 template <int kv, int D>

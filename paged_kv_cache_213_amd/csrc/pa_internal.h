@@ -261,3 +261,9 @@ hipError_t launch_fp8_decode(const uint8_t* in, float* out, int n, hipStream_t s
 constexpr int kMinPieceBlocks = PA_MIN_PIECE_BLOCKS;
 
 }  // namespace pa
+
+// Record sizes published by pa_workspace_layout's description.
+static_assert(sizeof(pa::TileDesc) == 12 * 4, "tile record format");
+static_assert(sizeof(pa::PieceStart) == 16 * 4, "piece record format");
+static_assert(sizeof(pa::SplitSeg) == 8 * 4, "cut-segment record format");
+static_assert(sizeof(pa::CascadeRec) == 8 * 4, "cascade record format");

@@ -31,16 +31,13 @@ def test_small_configs_with_groups(name, P):
 
 
 @pytest.mark.parametrize("name", ["c4", "c5"])
-def test_full_configs_with_groups_sampled(name):
+def test_full_configs_with_groups(name):
     """Full-size batches with their groups, balanced split (the bench's
-    launch configuration); the oracle checks sharers and non-sharers."""
+    launch configuration); every row (sharers, their places in the group
+    tiles, and non-sharers) is compared with the oracle."""
     wl = W.make_config(name)
-    grp = wl.shared_groups
-    pick = {0, wl.num_seqs - 1, grp[0][0], grp[0][-1], grp[-1][0], grp[-1][-1]}
-    pick |= set(int(i) for i in np.linspace(0, wl.num_seqs - 1, 5).astype(int))
-    e, _, _ = check_step(wl, partition_size=0, groups=_groups(wl),
-                         seq_subset=np.array(sorted(pick), np.int32))
-    print(f"{name} full cascade sampled: {e}", flush=True)
+    e, _, _ = check_step(wl, partition_size=0, groups=_groups(wl))
+    print(f"{name} full cascade: {e}", flush=True)
 
 
 def _group_batch(G, kv, q, seed, lens, prefix_len):

@@ -30,13 +30,12 @@ def test_small_70b_decode(P):
 
 
 @pytest.mark.parametrize("cascade", [False, True])
-def test_full_70b_decode_sampled(cascade):
+def test_full_70b_decode(cascade):
     """The full fp8 batch in the bench's launch configuration, with and
-    without its sampling groups; sampled sequences."""
+    without its sampling groups; every row against the oracle."""
     wl = W.make_config("c5")
-    pick = np.array(sorted({0, 1, 37, 64, 90, wl.num_seqs - 1}), np.int32)
     groups = (wl.shared_groups, wl.shared_prefix_blocks) if cascade else None
-    e, _, _ = check_step(wl, partition_size=0, seq_subset=pick, groups=groups, fp8_qk=True)
+    e, _, _ = check_step(wl, partition_size=0, groups=groups, fp8_qk=True)
     print(f"c5 full fp8_qk cascade={cascade}: {e}", flush=True)
 
 

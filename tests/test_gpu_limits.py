@@ -52,6 +52,5 @@ def test_most_sequences_in_one_call():
     lens = rng.integers(1, 65, 8192)
     wl = W.custom_workload(lens, num_q_heads=8, num_kv_heads=2, head_dim=64,
                            q_dtype="bf16", kv_dtype="bf16", seed=76)
-    pick = np.array(sorted({0, 1, 4095, 4096, 8190, 8191} | set(range(100, 8192, 997))), np.int32)
-    e, _, _ = check_step(wl, seq_subset=pick)
+    e, _, _ = check_step(wl)
     print(f"8192 decodes: {e}", flush=True)

@@ -34,20 +34,17 @@ def test_c1_full_parity():
 
 @pytest.mark.parametrize("name,P", [("c2", None), ("c3", None), ("c3", 0), ("c4", None),
                                     ("c4", 0), ("c5", None)])
-def test_full_config_sampled_parity(name, P):
+def test_full_config_parity(name, P):
     """Full-size batches, with the configuration's own partition size and
     with the balanced split (partition_size 0, the launch configuration the
-    bench times); the oracle checks a sample of sequences (the longest, the
-    shortest and spread ones, plus the prefill span in the hybrid batch)."""
+    bench times). Every row of every sequence is compared with the oracle:
+    errors at piece boundaries and segment restarts depend on position, so
+    a sample of sequences could miss them."""
     wl = W.make_config(name)
     if P is not None:
         wl.partition_size = P
-    L = wl.context_lens
-    order = np.argsort(L)
-    pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2]), 0, wl.num_seqs - 1}
-    pick |= set(int(i) for i in np.linspace(0, wl.num_seqs - 1, 6).astype(int))
-    e, _, _ = _check_step(wl, seq_subset=np.array(sorted(pick), np.int32))
-    print(f"{name} full sampled, partition_size {wl.partition_size}: {e}", flush=True)
+    e, _, _ = _check_step(wl)
+    print(f"{name} full, partition_size {wl.partition_size}: {e}", flush=True)
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c5"])

@@ -1,0 +1,130 @@
+"""CPU replay of the attention library's work decomposition (plan records,
+piece walks, partial slots, cascade buffers and the merge's reads) over
+the batches on which builds of the wide kernel once gave wrong rows or
+faulted: the small hybrid batch with its sharing group at its 512-token
+partition size, the full parallel-sampling batch with its groups, and the
+64 random sharing batches of the GPU suite. Each replay asserts that
+every index is in range, that no two segments write one slot row, cascade
+row or output row, and that every merge read finds the partial the right
+segment wrote for the right row (tests/plan_model.py). Group tiles of one
+and of two 16-row tiles are both replayed; the wave counts include the
+device's (1024 narrow, 2048 wide) and odd ones."""
+import numpy as np
+import pytest
+
+from paged_kv_cache_213_amd import workloads as W
+from tests import plan_model as PM
+from tests.test_gpu_random_batches import _random_batch, _random_sharing_batch
+
+WAVES = [(2048, 1024), (1024, 1024), (37, 13), (8192, 8192), (512, 256)]
+
+
+def _groups(wl):
+    return (wl.shared_groups, wl.shared_prefix_blocks)
+
+
+@pytest.mark.parametrize("waves", WAVES)
+@pytest.mark.parametrize("rt", [1, 2])
+@pytest.mark.parametrize("P", [None, 16, 0])
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_small_sharing_batches(name, P, rt, waves):
+    wl = W.make_config(name, small=True)
+    _, _, c = PM.replay_workload(wl, waves=waves, groups=_groups(wl), partition_size=P,
+                                 group_row_tiles=rt)
+    assert c["cascade_records"] > 0
+
+
+@pytest.mark.parametrize("waves", WAVES[:3])
+@pytest.mark.parametrize("rt", [1, 2])
+def test_full_sampling_batch_with_groups(rt, waves):
+    wl = W.make_config("c5")
+    _, _, c = PM.replay_workload(wl, waves=waves, groups=_groups(wl), partition_size=0,
+                                 group_row_tiles=rt)
+    assert c["cascade_records"] == wl.num_seqs * wl.num_kv_heads
+
+
+@pytest.mark.parametrize("rt", [1, 2])
+def test_full_hybrid_batch_with_groups(rt):
+    wl = W.make_config("c4")
+    PM.replay_workload(wl, waves=(2048, 1024), groups=_groups(wl), partition_size=0,
+                       group_row_tiles=rt)
+
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_sharing_batches(seed):
+    wl, groups = _random_sharing_batch(seed)
+    for rt in (1, 2):
+        for waves in ((2048, 1024), (37, 13)):
+            PM.replay_workload(wl, waves=waves, groups=groups, group_row_tiles=rt)
+
+
+@pytest.mark.parametrize("name,P", [("c1", None), ("c2", None), ("c3", None), ("c3", 0),
+                                    ("c4", None), ("c4", 0), ("c5", 0)])
+def test_full_configs_without_groups(name, P):
+    wl = W.make_config(name)
+    PM.replay_workload(wl, waves=(2048, 1024), partition_size=P)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_hybrid_batches(seed):
+    wl = _random_batch(seed)
+    PM.replay_workload(wl, waves=(2048, 1024))
+
+
+def test_model_catches_a_planted_slot_slip():
+    """The replay is able to fail: a plan whose merge reads the head slot
+    of a segment's first piece (in place of its tail slot) is rejected."""
+    wl = W.make_config("c4", small=True)
+    lay = PM.make_layout(G=4, Hkv=wl.num_kv_heads, num_seqs=wl.num_seqs,
+                         num_tokens=wl.num_tokens, max_context_len=wl.max_context_len,
+                         max_query_len=wl.max_query_len, decode=False, partition_size=16,
+                         cascade=False, waves=(2048, 1024))
+    qsl = np.asarray(wl.query_start_loc)
+    plan = PM.build_plan(lay, Hkv=wl.num_kv_heads, context_lens=wl.context_lens, qsl=qsl,
+                         num_tokens=wl.num_tokens, max_context_len=wl.max_context_len)
+    assert plan.splits
+    row0, ntok, kvh, k0, k1, st = plan.splits[0]
+    plan.splits[0] = (row0, ntok, kvh, k0 + 1, k1, st)  # drops the first piece
+    with pytest.raises(AssertionError):
+        PM.check_plan(plan, lay, G=4, Hkv=wl.num_kv_heads, num_seqs=wl.num_seqs,
+                      num_tokens=wl.num_tokens, qsl=qsl, group_members=[])
+
+
+def _lib_layout(wl, groups, P, hybrid):
+    import paged_kv_cache_213_amd as pa
+    pa.load_library()
+    dt = {"f32": pa.PA_F32, "bf16": pa.PA_BF16, "fp8": pa.PA_FP8_E4M3FN}
+    shape = pa.PaShape(wl.num_q_heads, wl.num_kv_heads, wl.head_dim, 16, 1000,
+                       wl.block_tables.shape[1], dt[wl.q_dtype], dt[wl.kv_dtype], P,
+                       int(groups is not None), 0)
+    mq = wl.max_query_len if hybrid else 1
+    info = pa.workspace_layout(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len, mq,
+                               decode=not hybrid)
+    return shape, info
+
+
+@pytest.mark.parametrize("name,P,grouped", [("c2", 0, False), ("c3", 512, False),
+                                            ("c4", 0, True), ("c4", 512, False),
+                                            ("c5", 0, True), ("c1", 0, False)])
+def test_model_layout_equals_the_librarys(name, P, grouped):
+    """The model's workspace bounds are the library's (host-only call; with
+    no device to query, both take the 8192-wave bound)."""
+    import paged_kv_cache_213_amd as pa
+    wl = W.make_config(name)
+    groups = _groups(wl) if grouped else None
+    hybrid = not wl.is_decode
+    shape, info = _lib_layout(wl, groups, P, hybrid)
+    lay = PM.make_layout(G=wl.num_q_heads // wl.num_kv_heads, Hkv=wl.num_kv_heads,
+                         num_seqs=wl.num_seqs, num_tokens=wl.num_tokens,
+                         max_context_len=wl.max_context_len,
+                         max_query_len=wl.max_query_len if hybrid else 1, decode=not hybrid,
+                         partition_size=P, cascade=grouped, waves=tuple(info.waves),
+                         wide_nt=info.wide_row_tiles)
+    assert (lay.narrow_tokens, lay.wide_tokens, lay.part_blocks, lay.members_per_tile) == (
+        info.narrow_tokens, info.wide_tokens, info.part_blocks, info.members_per_tile)
+    assert lay.max_tiles == info.max_tiles and lay.max_splits == info.max_splits
+    assert lay.max_pieces == tuple(info.max_pieces)
+    assert lay.max_cas_recs == info.max_cas_recs
+    mq = wl.max_query_len if hybrid else 1
+    assert info.total <= pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens,
+                                            wl.max_context_len, mq)
