@@ -71,7 +71,9 @@ typedef enum pa_status {
     PA_EWORKSPACE = -2, /* workspace NULL or smaller than pa_workspace_bytes */
     PA_EHIP = -3,       /* a HIP runtime call or kernel launch failed */
     PA_ENOTSUP = -4,    /* valid request this build does not implement */
-    PA_ENOMEM = -5      /* no free physical block (block manager) */
+    PA_ENOMEM = -5,     /* no free physical block (block manager) */
+    PA_ESCRATCH = -6    /* batch needs more than the static scratch buffer
+                           of pa_paged_attn_hybrid_noalloc holds */
 } pa_status;
 
 /* Problem shape shared by all calls on one cache. Supported today:
@@ -140,6 +142,26 @@ int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const voi
                          int num_seqs, int num_q_tokens, int max_query_len,
                          int max_context_len, float scale, void* workspace,
                          size_t workspace_bytes, void* stream);
+
+/* pa_paged_attn_hybrid for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments and results as pa_paged_attn_hybrid (bit for
+ * bit), without the workspace: the plan, the pieces' partial results and
+ * the merge use a buffer of PA_NOALLOC_SCRATCH_BYTES that the library holds
+ * in static device memory, one per GPU it runs on, for the life of the
+ * process. The call allocates and frees nothing. Batches whose workspace
+ * (pa_workspace_bytes) exceeds that size return PA_ESCRATCH before anything
+ * is enqueued. Every call on one GPU shares that GPU's buffer: calls that
+ * overlap on one GPU (different streams, or threads) race, so a caller
+ * orders them, for instance on one stream. Nothing in the buffer needs to
+ * start at zero: each call's plan writes every record the call reads. */
+#define PA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int pa_paged_attn_hybrid_noalloc(const pa_shape* shape, void* out, float* lse, const void* q,
+                                 const void* k_cache, const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_tables,
+                                 const int32_t* context_lens, const int32_t* query_start_loc,
+                                 int num_seqs, int num_q_tokens, int max_query_len,
+                                 int max_context_len, float scale, void* stream);
 
 /* Plan a batch: turn (query spans, context lengths) into the work list the
  * attention kernel streams -- tiles of up to 16 query rows, one stream of
@@ -288,7 +310,7 @@ const char* pa_status_string(int status);
 
 /* Library ABI version (major * 100 + minor): 200 added pa_shape.cascade
  * and pa_plan_cascade; 201 added pa_plan_tree; 202 added pa_shape.fp8_qk;
- * 203 added pa_workspace_layout. */
+ * 203 added pa_workspace_layout; 204 added pa_paged_attn_hybrid_noalloc. */
 int pa_version(void);
 
 #ifdef __cplusplus

@@ -22,6 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3FN = 0, 1, 2
 PA_OK, PA_EINVAL, PA_EWORKSPACE, PA_EHIP, PA_ENOTSUP = 0, -1, -2, -3, -4
+PA_ESCRATCH = -6
+PA_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _lib = None
 
@@ -94,6 +96,9 @@ def load_library(path: str = LIB_PATH):
     lib.pa_paged_attn_decode.argtypes = [S, P, P, P, P, P, P, P, P, P, I, I, F, P, Z, P]
     lib.pa_paged_attn_hybrid.restype = I
     lib.pa_paged_attn_hybrid.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
+    lib.pa_paged_attn_hybrid_noalloc.restype = I
+    lib.pa_paged_attn_hybrid_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F,
+                                                 P]
     lib.pa_plan.restype = I
     lib.pa_plan.argtypes = [S, P, P, I, I, I, I, P, Z, P]
     lib.pa_plan_cascade.restype = I
@@ -240,6 +245,26 @@ def hybrid(q, k_cache, v_cache, block_tables, context_lens, query_start_loc, sca
                                   S, T, int(max_query_len), int(max_context_len), float(scale),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "pa_paged_attn_hybrid")
+    return out
+
+
+def hybrid_noalloc(q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                   scale: float, *, max_context_len: int, max_query_len: int, out, lse=None,
+                   k_scale=None, v_scale=None, partition_size: int = 0, stream=None,
+                   fp8_qk: bool = False):
+    """hybrid() without a workspace: the library's static per-GPU scratch
+    buffer serves the call, and nothing is allocated (``out`` is the
+    caller's). Calls that overlap on one GPU race on that buffer."""
+    lib = load_library()
+    shape = make_shape(q, k_cache, block_tables, partition_size, fp8_qk=fp8_qk)
+    T = q.shape[0]
+    S = context_lens.shape[0]
+    rc = lib.pa_paged_attn_hybrid_noalloc(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q),
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                          _ptr(v_scale), _ptr(block_tables), _ptr(context_lens),
+                                          _ptr(query_start_loc), S, T, int(max_query_len),
+                                          int(max_context_len), float(scale), _stream(stream))
+    _check(rc, "pa_paged_attn_hybrid_noalloc")
     return out
 
 

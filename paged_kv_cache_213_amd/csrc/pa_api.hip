@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "pa_internal.h"
 #include "pagedattn_blocks.h"
@@ -21,6 +22,13 @@
 #ifndef PA_WIDE_SPANS
 #define PA_WIDE_SPANS 1
 #endif
+
+// Scratch of pa_paged_attn_hybrid_noalloc, in static device memory: each
+// GPU the library runs on holds its own copy until the process ends. Host
+// code never passes this name to a kernel (on the host it is only a stand-in
+// for the symbol); it uses the device address that hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -529,6 +537,51 @@ int pa_copy_blocks(const pa_shape* shape, void* k_cache, void* v_cache, float* k
                                                                                   : PA_EHIP;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The scratch array's device address per device, looked up once per
+// device, with that device current, on the first no-alloc call there.
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+void* scratch_address() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_attn_hybrid_noalloc(const pa_shape* shape, void* out, float* lse, const void* q,
+                                 const void* k_cache, const void* v_cache, const float* k_scale,
+                                 const float* v_scale, const int32_t* block_tables,
+                                 const int32_t* context_lens, const int32_t* query_start_loc,
+                                 int num_seqs, int num_q_tokens, int max_query_len,
+                                 int max_context_len, float scale, void* stream) {
+    if (check_shape(shape) != PA_OK) return check_shape(shape);
+    if (num_seqs < 0 || num_q_tokens < 0 || max_context_len < 0) return PA_EINVAL;
+    const size_t need =
+        pa_workspace_bytes(shape, num_seqs, num_q_tokens, max_context_len, max_query_len);
+    if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ESCRATCH;
+    void* ws = scratch_address();
+    if (!ws) return PA_EHIP;
+    return pa_paged_attn_hybrid(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale,
+                                block_tables, context_lens, query_start_loc, num_seqs,
+                                num_q_tokens, max_query_len, max_context_len, scale, ws,
+                                (size_t)PA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int pa_workspace_layout(const pa_shape* shape, int num_seqs, int num_q_tokens,
                         int max_context_len, int max_query_len, int decode,
                         pa_layout_info* info) {
@@ -576,10 +629,11 @@ const char* pa_status_string(int status) {
     case PA_EHIP: return "HIP runtime or launch error";
     case PA_ENOTSUP: return "not supported";
     case PA_ENOMEM: return "no free block";
+    case PA_ESCRATCH: return "batch needs more than the static scratch buffer holds";
     default: return "unknown status";
     }
 }
 
-int pa_version(void) { return 203; }
+int pa_version(void) { return 204; }
 
 }  // extern "C"

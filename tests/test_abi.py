@@ -167,3 +167,17 @@ def test_output_row_limit_is_reported_before_any_launch():
     rc = lib.pa_paged_attn_decode(ctypes.byref(s), F, None, F, F, F, None, None, F, F, 8192, 100,
                                   0.1, F, 1 << 40, None)
     assert rc == pa.PA_ENOTSUP
+
+
+def test_noalloc_rejects_batches_past_its_buffer_on_the_host():
+    """The size check happens before any device work (no GPU needed)."""
+    lib = _lib()
+    shape = _shape(partition_size=16, num_blocks=4096, max_blocks_per_seq=2048)
+    S = 4096
+    need = lib.pa_workspace_bytes(ctypes.byref(shape), S, S * 64, 32768, 64)
+    assert need > pa.PA_NOALLOC_SCRATCH_BYTES
+    rc = lib.pa_paged_attn_hybrid_noalloc(ctypes.byref(shape), None, None, None, None, None,
+                                          None, None, None, None, None, S, S * 64, 64, 32768,
+                                          0.1, None)
+    assert rc == pa.PA_ESCRATCH
+    assert b"scratch" in lib.pa_status_string(pa.PA_ESCRATCH)
