@@ -39,61 +39,127 @@ def _threads() -> int:
         return os.cpu_count() or 1
 
 
-def cpu_baseline(wl, budget_s: float = 10.0):
-    """Time the CPU oracle (as it stands) on this workload's batch until
-    about ``budget_s`` of CPU work, on the host's cores."""
+# parity bounds of the check before timing: per element |gpu - ref| /
+# max(1, |ref|), and relative RMS over the sample (same as the test suite)
+TOL = {"f32": 1e-5, "bf16": 1e-2, "fp8": 3e-2}
+RRMS = {"f32": 1e-6, "bf16": 4e-3, "fp8": 4e-3}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_inputs(wl, vals) -> dict:
+    """Host copies of the GPU run's own inputs, taken before any append:
+    q and this step's new K/V rows (stored bits), and the pre-append cache
+    (for an fp8 cache: the source values and scales, which the oracle
+    leg encodes with its own e4m3 arithmetic)."""
     import torch
 
-    import oracle
-    from paged_kv_cache_213_amd import workloads as W
-
-    vals = W.materialize(wl, "cpu")
-
     def bits(t):
+        t = t.detach().cpu().contiguous()
         if t.dtype == torch.bfloat16:
-            return t.contiguous().view(torch.int16).numpy().view(np.uint16)
-        return t.contiguous().numpy()
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
 
-    host = {"q": bits(vals.q)}
+    h = {"q": bits(vals.q), "k_new": bits(vals.k_new), "v_new": bits(vals.v_new)}
     if wl.kv_dtype == "fp8":
-        host["k_scale"] = vals.k_scale.numpy()
-        host["v_scale"] = vals.v_scale.numpy()
-        host["k_cache"] = oracle.fp8_encode_blocks(vals.k_src.numpy(), host["k_scale"])
-        host["v_cache"] = oracle.fp8_encode_blocks(vals.v_src.numpy(), host["v_scale"])
+        h["k_src"], h["v_src"] = bits(vals.k_src), bits(vals.v_src)
+        h["k_scale"], h["v_scale"] = bits(vals.k_scale), bits(vals.v_scale)
     else:
-        host["k_cache"] = bits(vals.k_cache).copy()
-        host["v_cache"] = bits(vals.v_cache).copy()
-    oracle.kv_append(host["k_cache"], host["v_cache"], bits(vals.k_new), bits(vals.v_new),
-                     wl.slot_mapping, kv_dtype=wl.kv_dtype, new_dtype=wl.q_dtype,
-                     k_scale=host.get("k_scale"), v_scale=host.get("v_scale"),
-                     num_kv_heads=wl.num_kv_heads, head_dim=wl.head_dim)
+        h["k_cache"], h["v_cache"] = bits(vals.k_cache), bits(vals.v_cache)
+    return h
+
+
+def parity_sample(wl) -> np.ndarray:
+    """Sequences checked before timing: the shortest, the longest, the
+    median, the first and last, the first sequence with more than one
+    query token, and six spread over the batch."""
+    L = wl.context_lens
+    order = np.argsort(L, kind="stable")
+    pick = {int(order[0]), int(order[-1]), int(order[len(order) // 2]), 0, wl.num_seqs - 1}
+    spans = np.nonzero(wl.query_lens > 1)[0]
+    if spans.size:
+        pick.add(int(spans[0]))
+    pick |= set(int(i) for i in np.linspace(0, wl.num_seqs - 1, 6).astype(int))
+    return np.array(sorted(pick), np.int32)
+
+
+def oracle_leg(wl, host, gpu_out, budget_s: float = 10.0):
+    """The CPU oracle on the GPU run's own inputs. First it checks the timed
+    configuration's output (``gpu_out``, float64 [T][Hq][D]) on sampled
+    sequences against the oracle, then it times the oracle as it stands
+    on the host's cores (about ``budget_s``) and on one thread."""
+    import oracle
+
+    h = dict(host)
+    if wl.kv_dtype == "fp8":
+        h["k_cache"] = oracle.fp8_encode_blocks(h.pop("k_src"), h["k_scale"])
+        h["v_cache"] = oracle.fp8_encode_blocks(h.pop("v_src"), h["v_scale"])
+    else:
+        h["k_cache"], h["v_cache"] = h["k_cache"].copy(), h["v_cache"].copy()
+    oracle.kv_append(h["k_cache"], h["v_cache"], h["k_new"], h["v_new"], wl.slot_mapping,
+                     kv_dtype=wl.kv_dtype, new_dtype=wl.q_dtype, k_scale=h.get("k_scale"),
+                     v_scale=h.get("v_scale"), num_kv_heads=wl.num_kv_heads,
+                     head_dim=wl.head_dim)
     threads = _threads()
-    # grow the sample (a prefix of the batch's sequences, then whole-batch
-    # repeats) until the budget is spent
-    reps, t_total, seqs_done, bytes_done = 0, 0.0, 0, 0
+    # parity of the timed configuration on sampled sequences
+    sample = parity_sample(wl)
+    ref, _ = oracle.run_workload(wl, h, seq_subset=sample, threads=threads)
+    qsl = wl.query_start_loc
+    rows = np.concatenate([np.arange(qsl[i], qsl[i + 1]) for i in sample])
+    g, r = gpu_out[rows], ref[rows]
+    key = "fp8" if wl.kv_dtype == "fp8" else wl.q_dtype
+    diff = np.abs(g - r)
+    err = float(np.max(diff / np.maximum(1.0, np.abs(r)))) if r.size else 0.0
+    rrms = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-300)) if r.size else 0.0
+    parity = {"sequences": int(sample.size), "rows": int(rows.size), "max_tol_err": err,
+              "rel_rms": rrms, "tol": TOL[key], "rrms_bound": RRMS[key],
+              "ok": bool(np.all(np.isfinite(g)) and err <= TOL[key] and rrms <= RRMS[key])}
+    # timing: a prefix of the batch's sequences, doubled until the budget
+    # is spent (then whole-batch repeats)
     per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.kv_elem_bytes
-    n_sub = max(1, min(wl.num_seqs, 4))
-    while t_total < budget_s and reps < 1000:
-        sub = np.arange(n_sub, dtype=np.int32)
-        t0 = time.perf_counter()
-        oracle.run_workload(wl, host, seq_subset=sub, threads=threads)
-        dt = time.perf_counter() - t0
-        t_total += dt
-        seqs_done += n_sub
-        bytes_done += int(wl.context_lens[:n_sub].astype(np.int64).sum()) * per_tok
-        reps += 1
-        if n_sub < wl.num_seqs and dt < budget_s / 4:
-            n_sub = min(wl.num_seqs, n_sub * 2)
-    return {
+
+    def timed(nthreads, budget, n0):
+        reps, t_total, seqs_done, bytes_done = 0, 0.0, 0, 0
+        n_sub = max(1, min(wl.num_seqs, n0))
+        while t_total < budget and reps < 1000:
+            sub = np.arange(n_sub, dtype=np.int32)
+            t0 = time.perf_counter()
+            oracle.run_workload(wl, h, seq_subset=sub, threads=nthreads)
+            dt = time.perf_counter() - t0
+            t_total += dt
+            seqs_done += n_sub
+            bytes_done += int(wl.context_lens[:n_sub].astype(np.int64).sum()) * per_tok
+            reps += 1
+            if n_sub < wl.num_seqs and dt < budget / 4:
+                n_sub = min(wl.num_seqs, n_sub * 2)
+        return reps, t_total, seqs_done, bytes_done
+
+    reps, t_total, seqs_done, bytes_done = timed(threads, budget_s, 4)
+    r1, t1, s1, b1 = timed(1, max(budget_s / 5, 1.0), 1)
+    cpu = {
         "value": round(bytes_done / t_total / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"{seqs_done} sequence-layer calls of this batch ({reps} oracle calls over "
                   f"prefixes of the batch, {t_total:.1f} s, float64 gather-then-softmax, "
-                  f"{threads} threads)",
+                  f"{threads} threads) on the GPU run's own input arrays",
         "tokens_per_s": round(seqs_done / t_total, 2),
+        "single_thread": {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s",
+                          "tokens_per_s": round(s1 / t1, 2),
+                          "sample": f"{s1} sequence-layer calls, {t1:.1f} s, 1 thread"},
+        "cpu_model": cpu_model(),
     }
+    return parity, cpu
 
 
 PROFILE_FILES = {
@@ -110,7 +176,7 @@ def attention_source_sha256() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "paged_kv_cache_213_amd",
                         "csrc")
-    for f in ("pa_attention.hip", "pa_internal.h"):
+    for f in ("pa_attention.hip", "pa_span.hip", "pa_device.h", "pa_internal.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -197,7 +263,9 @@ def main():
     ap.add_argument("--partition-size", type=int, default=0,
                     help="split-KV piece in tokens (0: balanced over resident waves)")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle leg (its parity check before timing and the CPU "
+                         "baseline)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a graph")
     ap.add_argument("--cascade", choices=("auto", "on", "off"), default="auto",
                     help="read shared prefixes once per group (auto: when the workload's "
@@ -231,6 +299,8 @@ def main():
     dev = torch.device("cuda")
     torch.cuda.set_device(0)
     vals = W.materialize(wl, dev)
+    # the oracle leg runs on host copies of these very inputs (before any append)
+    host = None if args.no_cpu_baseline else host_inputs(wl, vals)
     k_scale = v_scale = None
     if wl.kv_dtype == "fp8":
         # build the e4m3 cache with the library's own append: every valid slot
@@ -318,10 +388,10 @@ def main():
                 model_step(s)
 
     def replay():
-        if graph is not None:
-            graph.replay()
-        else:
-            with torch.cuda.stream(s):
+        with torch.cuda.stream(s):
+            if graph is not None:
+                graph.replay()
+            else:
                 model_step(s)
 
     for _ in range(args.warmup):
@@ -329,6 +399,16 @@ def main():
     torch.cuda.synchronize()
     if not all(bool(torch.isfinite(o.float()).all()) for o in outs):
         raise SystemExit("non-finite attention output")
+    # before timing: the timed configuration's output against the oracle on
+    # sampled sequences, then the oracle's own timing (CPU baseline)
+    parity = cpu = None
+    if host is not None:
+        gpu_out = outs[0].float().cpu().numpy().astype(np.float64)
+        parity, cpu = oracle_leg(wl, host, gpu_out, args.cpu_budget)
+        del host, gpu_out
+        if not parity["ok"]:
+            print(json.dumps({"error": "parity check before timing failed", "parity": parity}))
+            sys.exit(3)
 
     # timed region: exactly `steps` model steps
     att_ms = []
@@ -338,6 +418,15 @@ def main():
         replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # spread: each of max(50, steps) further steps timed on its own
+    n_spread = max(50, args.steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
+    evs[0].record(s)
+    for i in range(n_spread):
+        replay()
+        evs[i + 1].record(s)
+    torch.cuda.synchronize()
+    step_ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(n_spread)])
     # the attention kernel's own duration: one event pair around the pass-1
     # launches of every layer, back to back on the stream (they are
     # independent); a GPU spin first lets the host enqueue ahead of the GPU,
@@ -388,7 +477,7 @@ def main():
     # the roofline counts what the method must read: the logical bytes, or
     # with cascade the group prefixes once per group tile
     G = wl.num_q_heads // wl.num_kv_heads
-    mpt = max(1, (16 * 2) // G)  # members per group tile: two 16-row tiles of G heads each
+    mpt = max(1, 16 // G)  # members per group tile: one 16-row tile of G heads each
     read_bytes = cascade_read_bytes(wl, mpt) if use_cascade else kv_bytes
     achieved = read_bytes / (att_mean / 1e3) / 1e9
     layer_ms = ms_per_step / layers
@@ -438,7 +527,7 @@ def main():
             "traffic_note": "HBM bytes per attention pass launch (calibrated FETCH_SIZE + "
                             "WRITE_SIZE, profiles/); null if not recorded for the current "
                             "attention source",
-            "kernel": "attention pass (attention_wide for chunked-prefill spans, then "
+            "kernel": "attention pass (attention_span for chunked-prefill spans, then "
                       "attention_narrow, one launch each per layer); HIP events around the "
                       "back-to-back pass-1 launches of all layers, divided by the layers",
             "launch_us_mean": round(att_mean * 1e3, 2),
@@ -449,9 +538,16 @@ def main():
         },
         "launch_us": {"plan_per_step": plan_us, "kv_append": append_us,
                       "attention": round(att_mean * 1e3, 2), "merge": merge_us},
+        "step_ms_spread": {"n": n_spread, "p10": round(float(np.percentile(step_ms, 10)), 5),
+                           "median": round(float(np.median(step_ms)), 5),
+                           "p90": round(float(np.percentile(step_ms, 90)), 5),
+                           "note": "each step timed alone with HIP events on the replay stream, "
+                                   "after the timed region"},
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    if parity is not None:
+        res["parity_before_timing"] = parity
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

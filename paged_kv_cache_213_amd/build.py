@@ -13,7 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedattn.so")
-SOURCES = ["pa_api.hip", "pa_attention.hip", "pa_append.hip", "pa_probe.hip", "pa_blocks.cpp"]
+SOURCES = ["pa_api.hip", "pa_attention.hip", "pa_span.hip", "pa_append.hip", "pa_probe.hip",
+           "pa_blocks.cpp"]
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -10,15 +10,6 @@
 #include "pa_internal.h"
 #include "pagedattn_blocks.h"
 
-// 16-row tiles of query rows in a shared-prefix group tile (at most the wide
-// tile's count). One: builds of the wide kernel whose bf16 group tiles held
-// two row tiles gave wrong rows in the second row tile, and two such builds
-// faulted on a large parallel-sampling batch; no cause has been shown, so
-// group tiles keep to the one-row-tile path that no build has failed on.
-#ifndef PA_GROUP_ROW_TILES
-#define PA_GROUP_ROW_TILES 1
-#endif
-
 #ifndef PA_WIDE_SPANS
 #define PA_WIDE_SPANS 1
 #endif
@@ -99,29 +90,28 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
                    int max_query_len, bool decode) {
     Layout l;
     const int G = s->num_q_heads / s->num_kv_heads;
-    const int wt = pa::wide_tiles(s->kv_dtype);
     l.narrow_tokens = decode ? 1 : (16 / G > 1 ? 16 / G : 1);
-    l.wide_tokens = (16 * wt) / G > 1 ? (16 * wt) / G : 1;
+    l.wide_tokens = pa::kSpanRows / G > 1 ? pa::kSpanRows / G : 1;
     l.part_blocks = s->partition_size / PA_BLOCK_SIZE;
-    // wide tiles for spans longer than a narrow tile (0: every span in narrow tiles)
-    const bool spans = PA_WIDE_SPANS && !decode && max_query_len > l.narrow_tokens;
+    // wide tiles for spans longer than a narrow tile (0: every span in narrow
+    // tiles). The span kernel computes on the bf16 matrix cores, so f32
+    // caches, which need f32 products, keep their spans in narrow tiles.
+    const bool spans = PA_WIDE_SPANS && !decode && max_query_len > l.narrow_tokens &&
+                       s->kv_dtype != PA_F32;
     if (!spans) l.wide_tokens = 0;
     l.cascade = s->cascade != 0;
-    {
-        const int rt = PA_GROUP_ROW_TILES < wt ? PA_GROUP_ROW_TILES : wt;  // row tiles per group tile
-        l.members_per_tile = (16 * rt) / G > 1 ? (16 * rt) / G : 1;
-    }
-    // wide: spans' tiles, then shared-prefix groups' tiles (at most one per
-    // group plus one per members_per_tile members, each sequence in at most
-    // one group)
+    // a group tile holds the single query tokens of up to 16 / G members
+    l.members_per_tile = 16 / G > 1 ? 16 / G : 1;
     // (spans are disjoint, so no stream has more tiles than query tokens)
     const int64_t T = num_tokens;
     const int64_t tiles_of[pa::NUM_STREAMS] = {
-        (spans ? std::min((int64_t)num_seqs + cdiv(num_tokens, l.wide_tokens), T) : 0) +
-            (l.cascade ? 2 * (int64_t)num_seqs : 0),
-        // narrow: one per sequence, or every span cut into narrow tiles
-        spans || decode ? (int64_t)num_seqs
-                        : std::min((int64_t)num_seqs + cdiv(num_tokens, l.narrow_tokens), T)};
+        spans ? std::min((int64_t)num_seqs + cdiv(num_tokens, l.wide_tokens), T) : 0,
+        // narrow: one per sequence, or every span cut into narrow tiles;
+        // then shared-prefix groups' tiles (at most one per group plus one
+        // per members_per_tile members, each sequence in at most one group)
+        (spans || decode ? (int64_t)num_seqs
+                         : std::min((int64_t)num_seqs + cdiv(num_tokens, l.narrow_tokens), T)) +
+            (l.cascade ? 2 * (int64_t)num_seqs : 0)};
     l.max_tiles = tiles_of[0] + tiles_of[1];
     const int64_t blocks_per_tile = cdiv(max_context_len > 0 ? max_context_len : 1, PA_BLOCK_SIZE);
     size_t off = align_up(sizeof(int32_t) * pa::HDR_WORDS);
@@ -164,7 +154,7 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
         }
     }
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
-        const int nt = st == pa::STREAM_WIDE ? wt : 1;
+        const int nt = st == pa::STREAM_WIDE ? pa::kSpanRowTiles : 1;
         const size_t slots = (size_t)l.max_pieces[st] * 2;
         l.off_pieces[st] = off;
         off = align_up(off + sizeof(pa::PieceStart) * (size_t)l.max_pieces[st]);
@@ -352,7 +342,7 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
         ma.num_q_heads = s->num_q_heads;
         ma.num_kv_heads = s->num_kv_heads;
         ma.group = s->num_q_heads / s->num_kv_heads;
-        ma.wide_nt = pa::wide_tiles(s->kv_dtype);
+        ma.wide_nt = pa::kSpanRowTiles;
         ma.max_splits = (int32_t)l.max_splits;
         int64_t records = l.max_splits;
         if (l.cascade) {
@@ -602,7 +592,7 @@ int pa_workspace_layout(const pa_shape* shape, int num_seqs, int num_q_tokens,
     r.wide_tokens = l.wide_tokens;
     r.part_blocks = l.part_blocks;
     r.members_per_tile = l.members_per_tile;
-    r.wide_row_tiles = pa::wide_tiles(shape->kv_dtype);
+    r.wide_row_tiles = pa::kSpanRowTiles;
     r.header_words = pa::HDR_WORDS;
     r.max_tiles = l.max_tiles;
     r.max_splits = l.max_splits;

@@ -41,108 +41,13 @@
 #include <atomic>
 #include <type_traits>
 
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kLog2e = 1.44269504088896340736f;
-
-enum KvKind { KV_F32 = PA_F32, KV_BF16 = PA_BF16, KV_FP8 = PA_FP8_E4M3FN, KV_FP8Q = KIND_FP8_QK };
-
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Reductions over the four lanes n, n + 16, n + 32, n + 48 that hold one
-// query row, with the gfx950 row swaps: permlane16_swap exchanges 16-lane
-// rows 1 <-> 0 and 3 <-> 2 between its two operands, permlane32_swap rows
-// 2, 3 <-> 0, 1; given the same value twice, the two results hold a lane's
-// own value and its partner's, in some order, so any symmetric op of them
-// reduces over the pair.
-__device__ __forceinline__ float pair16_max(float v) {
-    const auto w = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                    false);
-    return fmaxf(__uint_as_float(w[0]), __uint_as_float(w[1]));
-}
-__device__ __forceinline__ float pair32_max(float v) {
-    const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                    false);
-    return fmaxf(__uint_as_float(w[0]), __uint_as_float(w[1]));
-}
-__device__ __forceinline__ float row_max(float v) { return pair32_max(pair16_max(v)); }
-__device__ __forceinline__ float row_sum(float v) {
-    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                    false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                    false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-// Two floats -> two bf16 (round to nearest even) packed low, high: one
-// v_cvt_pk_bf16_f32.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    const f32x2_t f = {lo, hi};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-// Two e4m3fn bytes (the low or the high half of a dword, b0 low) -> two
-// bf16 packed in a dword, with one gfx950 conversion (scale 1). Every e4m3
-// value is exact in bf16, so the conversion rounds nothing.
-template <bool hi>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, hi));
-}
-
-// K/V loads. A block that one wave reads once per call (a decode's context)
-// is streamed with nontemporal loads, so it does not evict the block tables,
-// queries and partials from the caches; blocks that several query tiles read
-// (a chunked-prefill span's context) use ordinary loads, so the tiles after
-// the first find them in L2.
-#ifndef PA_NT_LOADS
-#define PA_NT_LOADS 1
-#endif
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-
-template <bool nt>
-__device__ __forceinline__ uint4 ld_kv(const uint4* p) {
-    if constexpr (nt) {
-        const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
-        return make_uint4(v.x, v.y, v.z, v.w);
-    } else {
-        return *p;
-    }
-}
-template <bool nt>
-__device__ __forceinline__ uint2 ld_kv(const uint2* p) {
-    if constexpr (nt) {
-        const u32x2_t v = __builtin_nontemporal_load((const u32x2_t*)p);
-        return make_uint2(v.x, v.y);
-    } else {
-        return *p;
-    }
-}
-template <bool nt>
-__device__ __forceinline__ uint32_t ld_kv(const uint32_t* p) {
-    if constexpr (nt) {
-        return __builtin_nontemporal_load(p);
-    } else {
-        return *p;
-    }
-}
-template <bool nt>
-__device__ __forceinline__ float4 ld_kv(const float4* p) {
-    const uint4 v = ld_kv<nt>((const uint4*)p);
-    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                       __uint_as_float(v.w));
-}
+using namespace dev;
 
 // ---- per-dtype register images of one 16-token block ---------------------
 
@@ -283,30 +188,6 @@ struct Tile<KV_FP8, D> {
         }
         return acc;
     }
-    // The bf16 image of the block (exact), for tiles whose K and V serve
-    // several row tiles: converted once, not once per row tile. K step m of
-    // the image holds dims 64(m/2) + 16g + 8(m%2) + e, the order of qk()
-    // below and of the fp8 q operand.
-    __device__ __forceinline__ Tile<KV_BF16, D> to_bf16() const {
-        Tile<KV_BF16, D> b;
-#pragma unroll
-        for (int j = 0; j < D / 64; ++j) {
-            const uint32_t w[4] = {k[j].x, k[j].y, k[j].z, k[j].w};
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                b.k[2 * j + h].x = fp8x2_to_bf16x2<false>(w[2 * h]);
-                b.k[2 * j + h].y = fp8x2_to_bf16x2<true>(w[2 * h]);
-                b.k[2 * j + h].z = fp8x2_to_bf16x2<false>(w[2 * h + 1]);
-                b.k[2 * j + h].w = fp8x2_to_bf16x2<true>(w[2 * h + 1]);
-            }
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            b.v[dt].x = fp8x2_to_bf16x2<false>(v[dt]);
-            b.v[dt].y = fp8x2_to_bf16x2<true>(v[dt]);
-        }
-        return b;
-    }
     __device__ __forceinline__ void mask_v(int nvalid) {
         const uint32_t m =
             nvalid >= 4 ? 0xffffffffu : (nvalid <= 0 ? 0u : ((1u << (8 * nvalid)) - 1u));
@@ -354,44 +235,9 @@ __device__ __forceinline__ f32x4 qk_fp8(const uint4 (&k)[D / 64], const uint4* q
     return acc;
 }
 
-// K kept in e4m3, V in bf16: the converted block of a tile whose K and V
-// serve several row tiles.
-template <int D>
-struct TileFp8QkV {
-    uint4 k[D / 64];
-    uint2 v[D / 16];
-    __device__ __forceinline__ f32x4 qk(const uint4* q) const { return qk_fp8<D>(k, q); }
-    __device__ __forceinline__ void mask_v(int nvalid) {
-        const uint32_t mx = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0x0000ffffu : 0u);
-        const uint32_t my = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            v[dt].x &= mx;
-            v[dt].y &= my;
-        }
-    }
-    __device__ __forceinline__ void pv(s16x4 p, f32x4* o) const {
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v[dt]), p,
-                                                              o[dt], 0, 0, 0);
-    }
-};
-
 template <int D>
 struct Tile<KV_FP8Q, D> : Tile<KV_FP8, D> {
     __device__ __forceinline__ f32x4 qk(const uint4* q) const { return qk_fp8<D>(this->k, q); }
-    __device__ __forceinline__ TileFp8QkV<D> to_bf16() const {
-        TileFp8QkV<D> b;
-#pragma unroll
-        for (int j = 0; j < D / 64; ++j) b.k[j] = this->k[j];
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-            b.v[dt].x = fp8x2_to_bf16x2<false>(this->v[dt]);
-            b.v[dt].y = fp8x2_to_bf16x2<true>(this->v[dt]);
-        }
-        return b;
-    }
 };
 
 // Row q (bf16) -> the two e4m3 terms of qk_fp8 for this lane's dims 16g +
@@ -557,9 +403,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         __syncthreads();
     }
 
-    // 1. tiles: spans longer than one narrow tile get wide tiles (stream 0),
-    //    followed by the groups' tiles; everything else narrow ones (stream
-    //    1); sequence order within each
+    // 1. tiles: spans longer than one narrow tile get wide tiles (stream 0);
+    //    everything else narrow ones (stream 1), followed by the groups'
+    //    tiles; sequence order within each
     int tile_base = 0, nwide = 0;
     for (int st = 0; st < NUM_STREAMS; ++st) {
         for (int c0 = 0; c0 < S; c0 += kPlanThreads) {
@@ -594,7 +440,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             }
             tile_base += total;
         }
-        if (st == STREAM_WIDE && a.num_groups > 0) {
+        if (st == STREAM_NARROW && a.num_groups > 0) {
             const int mpt = a.members_per_tile;
             for (int c0 = 0; c0 < a.num_groups; c0 += kPlanThreads) {
                 const int g = c0 + (int)threadIdx.x;
@@ -770,47 +616,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
 // ---- attention ---------------------------------------------------------------
 
-// The wide kernel's block steps stay in program order (a scheduling barrier
-// between steps). A build without it gave deterministically wrong rows in
-// bf16 shared-prefix group tiles, in a kernel with no register spilling; the
-// cause is not known, so the barrier is not optional.
-#ifndef PA_WIDE_SCHED_BARRIER
-#define PA_WIDE_SCHED_BARRIER 1
-#endif
-#if PA_WIDE_SCHED_BARRIER != 1
-#error "the wide kernel's block steps must keep their scheduling barrier (see above)"
-#endif
-// K/V blocks in flight per wave beyond the one in use. Both kernels run one
-// wave per SIMD; the narrow one keeps two blocks in flight, the wide one,
-// whose blocks also feed more row tiles, one.
+// K/V blocks in flight per wave beyond the one in use (one wave per SIMD).
 #ifndef PA_PREFETCH
 #define PA_PREFETCH 2
-#endif
-#ifndef PA_WIDE_PREFETCH
-#define PA_WIDE_PREFETCH 1
-#endif
-// A build with two wide blocks in flight faulted the GPU on the full
-// parallel-sampling batch with shared-prefix groups (fp8 cache); its wide
-// kernel spilled 212 VGPRs to AGPRs and 47 SGPRs. The cause is not known,
-// so only one block ahead is allowed.
-#if PA_WIDE_PREFETCH != 1
-#error "PA_WIDE_PREFETCH other than 1 is disabled (see above)"
 #endif
 
 // Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
 // each block through the block table, S = K q^T on the matrix cores, online
-// softmax in registers, O += V^T P, for NT 16-row tiles of query rows that
-// share every K/V block the wave loads. Then either write the rows' output
-// (the wave saw the whole segment) or write a partial result into the
-// piece's slot for the merge pass.
-template <int kv, int D, int NT, int NR, bool kOnce>
+// softmax in registers, O += V^T P, for one 16-row tile of query rows (the
+// G heads of up to 16 / G query tokens) that share every K/V block the wave
+// loads. Then either write the rows' output (the wave saw the whole
+// segment) or write a partial result into the piece's slot for the merge
+// pass.
+template <int kv, int D>
 __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td, const int kvh,
                                             const int j, const int take, const int piece) {
     using T = Tile<kv, D>;
-    // blocks that no other tile of the call reads (single-token tiles, and
-    // a shared prefix in its group tile) are streamed past the caches; the
-    // query tiles of a span share each block through L2
-    constexpr bool kStreamLoads = kOnce && PA_NT_LOADS;
+    constexpr int NT = 1, NR = 1;  // row tiles of a slot, and holding rows
+    // a single-token tile's blocks (a decode's context, a cascade member's
+    // suffix, a group's prefix in its group tile) are read by no other tile
+    // of the call, so they are streamed past the caches
+    constexpr bool kStreamLoads = PA_NT_LOADS;
     constexpr bool kFp8Cache = kv == KV_FP8 || kv == KV_FP8Q;
     using QReg = typename std::conditional<
         kv == KV_F32, float[D / 4],
@@ -822,8 +648,6 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     const int seq = td.seq;
     const int L = td.L, qs = td.qs, nspan = td.nspan;
     const int nrows = td.ntok * G;
-    // NR = ceil(nrows / 16) row tiles hold rows (the caller dispatches on
-    // it); slots keep the layout of NT row tiles
 
     // this lane's query row in row tile r: tile row 16 r + n = token qj,
     // head kvh*G + (row % G)
@@ -1007,19 +831,12 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 #pragma unroll
             for (int r = 0; r < NR; ++r) cur.pv(pk[r], o[r]);
         };
-        auto consume = [&](T& cur, int i) {
-            if constexpr (kFp8Cache && NT > 1) {
-                auto cb = cur.to_bf16();
-                consume_tile(cb, i);
-            } else {
-                consume_tile(cur, i);
-            }
-        };
+        auto consume = [&](T& cur, int i) { consume_tile(cur, i); };
         auto fetch = [&](T& dst, int i) {
             const int ph = __builtin_amdgcn_readlane(my_phys, i);
             dst.template load<kStreamLoads>(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
         };
-        constexpr int PF = NT == 1 ? PA_PREFETCH : PA_WIDE_PREFETCH;
+        constexpr int PF = PA_PREFETCH;
         // ring of PF + 1 register tiles: PF blocks stay in flight while one is
         // consumed. In the steady-state loop every refill is in range, so it
         // is straight-line code in which each wait covers exactly one block;
@@ -1037,7 +854,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 consume(ring[r], i0 + r);
                 // keep the steps in order: the scheduler would otherwise hoist
                 // later steps' products above their loads' waits
-                if constexpr (NT == 1 || PA_WIDE_SCHED_BARRIER) __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 #pragma unroll
@@ -1100,26 +917,9 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     }
 }
 
-// A wide segment, with the count of row tiles that hold rows made a
-// compile-time constant.
-template <int kv, int D, int NT, bool kOnce>
-__device__ __forceinline__ void run_wide_segment(const AttnArgs& a, const TileDesc& td,
-                                                 const int kvh, const int j, const int take,
-                                                 const int piece) {
-    const int nrt = (td.ntok * a.group + 15) >> 4;
-    if (nrt <= 1)
-        run_segment<kv, D, NT, 1, kOnce>(a, td, kvh, j, take, piece);
-    else if (NT == 2 || nrt == 2)
-        run_segment<kv, D, NT, (NT >= 2 ? 2 : 1), kOnce>(a, td, kvh, j, take, piece);
-    else if (nrt == 3)
-        run_segment<kv, D, NT, (NT >= 3 ? 3 : 1), kOnce>(a, td, kvh, j, take, piece);
-    else
-        run_segment<kv, D, NT, NT, kOnce>(a, td, kvh, j, take, piece);
-}
-
-// One wave per workgroup; wave w streams pieces w, w + grid, ... of its
-// stream (tiles of NT row tiles).
-template <int kv, int D, int NT>
+// One wave per workgroup; wave w streams pieces w, w + grid, ... of the
+// narrow stream.
+template <int kv, int D>
 __device__ __forceinline__ void attention_body(const AttnArgs& a) {
     const int* h = a.hdr + HDR_STREAM + 4 * a.stream;
     const int V = h[HDR_NPIECES], R = h[HDR_R], B = h[HDR_TOTAL];
@@ -1133,13 +933,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
         int left = (int)min((int64_t)R, (int64_t)B - (int64_t)(v / Hkv) * R);
         while (left > 0) {
             const int take = min(left, td.nb - j);
-            if constexpr (NT == 1) {
-                run_segment<kv, D, 1, 1, true>(a, td, kvh, j, take, v);
-            } else if (td.flags == TILE_GROUP) {
-                run_wide_segment<kv, D, NT, true>(a, td, kvh, j, take, v);
-            } else {
-                run_wide_segment<kv, D, NT, false>(a, td, kvh, j, take, v);
-            }
+            run_segment<kv, D>(a, td, kvh, j, take, v);
             left -= take;
             j = 0;
             ++t;
@@ -1160,22 +954,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
 #endif
 template <int kv, int D>
 __global__ __launch_bounds__(64) PA_NARROW_OCCUPANCY void attention_narrow(AttnArgs a) {
-    attention_body<kv, D, 1>(a);
-}
-
-// Wide tiles of chunked-prefill spans and shared-prefix groups. With two
-// row tiles per wide tile, the bf16 and fp8 kernels are built for two waves
-// per SIMD: they then fit in 256 VGPRs with no AGPR or scratch spill space.
-// The f32 kernel keeps the compiler's own choice (its operands take twice
-// the registers).
-#ifndef PA_WIDE_MIN_WAVES
-#define PA_WIDE_MIN_WAVES 2
-#endif
-constexpr int wide_min_waves(int kv) { return kv == KV_F32 ? 1 : PA_WIDE_MIN_WAVES; }
-template <int kv, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(wide_min_waves(kv), 8))) void
-attention_wide(AttnArgs a) {
-    attention_body<kv, D, wide_tiles(kv)>(a);
+    attention_body<kv, D>(a);
 }
 
 // ---- merge -------------------------------------------------------------------
@@ -1256,8 +1035,9 @@ __device__ __forceinline__ void merge_cascade(const MergeArgs& a, const CascadeR
             acc.add(a.cas_lse[kind][row], x);
             continue;
         }
-        const int st = kind == CAS_PRE ? STREAM_WIDE : STREAM_NARROW;
-        const int nt = st == STREAM_WIDE ? a.wide_nt : 1;
+        // both parts are narrow tiles (one 16-row tile per slot)
+        const int st = STREAM_NARROW;
+        const int nt = 1;
         const int rr = (kind == CAS_PRE ? rc.pre_pos * G : 0) + n;  // row in the slot
         const float4* po = (const float4*)a.part_o[st];
         // four pieces per round trip: all their loads are issued first
@@ -1398,7 +1178,7 @@ int resident_waves_of(K kernel, int cap_per_simd) {
     return (occ > 0 ? occ : 1) * num_cu;
 }
 
-// Resident waves per (kernel instance, device, stream), queried once per
+// Resident waves per (kernel instance, device), queried once per
 // device and kept for the life of the process. The value depends only on
 // the kernel's resources and the device's compute-unit count, so threads
 // that race on a first query compute the same number; the table is atomic
@@ -1406,18 +1186,16 @@ int resident_waves_of(K kernel, int cap_per_simd) {
 // one every later call sees. Devices past kMaxDevices are queried each call.
 constexpr int kMaxDevices = 64;
 template <int kv, int D>
-int resident_waves_d(int stream) {
-    static std::atomic<int> cached[kMaxDevices][NUM_STREAMS];  // 0: not yet queried
+int resident_waves_d() {
+    static std::atomic<int> cached[kMaxDevices];  // 0: not yet queried
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
-    std::atomic<int>* slot = dev < kMaxDevices ? &cached[dev][stream] : nullptr;
+    std::atomic<int>* slot = dev < kMaxDevices ? &cached[dev] : nullptr;
     if (slot) {
         const int c = slot->load(std::memory_order_acquire);
         if (c > 0) return c;
     }
-    const int w = stream == STREAM_WIDE
-                      ? resident_waves_of(attention_wide<kv, D>, 0)
-                      : resident_waves_of(attention_narrow<kv, D>, PA_NARROW_MAX_WAVES);
+    const int w = resident_waves_of(attention_narrow<kv, D>, PA_NARROW_MAX_WAVES);
     if (w <= 0) return 0;
     if (!slot) return w;
     int expected = 0;
@@ -1426,30 +1204,28 @@ int resident_waves_d(int stream) {
 }
 
 template <int kv, int D>
-hipError_t launch_attention_d(const AttnArgs& a, int64_t max_pieces, hipStream_t s) {
-    int64_t grid = resident_waves_d<kv, D>(a.stream);
+hipError_t launch_narrow_d(const AttnArgs& a, int64_t max_pieces, hipStream_t s) {
+    int64_t grid = resident_waves_d<kv, D>();
     if (grid <= 0) return hipErrorInvalidDevice;
     if (max_pieces < grid) grid = max_pieces;
     if (grid < 1) grid = 1;
-    if (a.stream == STREAM_WIDE)
-        hipLaunchKernelGGL((attention_wide<kv, D>), dim3((unsigned)grid), dim3(64), 0, s, a);
-    else
-        hipLaunchKernelGGL((attention_narrow<kv, D>), dim3((unsigned)grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((attention_narrow<kv, D>), dim3((unsigned)grid), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 int resident_waves(int kind, int head_dim, int stream) {
+    if (stream == STREAM_WIDE) return span_resident_groups(kind, head_dim);
     switch (kind * 1000 + head_dim) {
-    case PA_F32 * 1000 + 64: return resident_waves_d<KV_F32, 64>(stream);
-    case PA_F32 * 1000 + 128: return resident_waves_d<KV_F32, 128>(stream);
-    case PA_BF16 * 1000 + 64: return resident_waves_d<KV_BF16, 64>(stream);
-    case PA_BF16 * 1000 + 128: return resident_waves_d<KV_BF16, 128>(stream);
-    case PA_FP8_E4M3FN * 1000 + 64: return resident_waves_d<KV_FP8, 64>(stream);
-    case PA_FP8_E4M3FN * 1000 + 128: return resident_waves_d<KV_FP8, 128>(stream);
-    case KIND_FP8_QK * 1000 + 64: return resident_waves_d<KV_FP8Q, 64>(stream);
-    case KIND_FP8_QK * 1000 + 128: return resident_waves_d<KV_FP8Q, 128>(stream);
+    case PA_F32 * 1000 + 64: return resident_waves_d<KV_F32, 64>();
+    case PA_F32 * 1000 + 128: return resident_waves_d<KV_F32, 128>();
+    case PA_BF16 * 1000 + 64: return resident_waves_d<KV_BF16, 64>();
+    case PA_BF16 * 1000 + 128: return resident_waves_d<KV_BF16, 128>();
+    case PA_FP8_E4M3FN * 1000 + 64: return resident_waves_d<KV_FP8, 64>();
+    case PA_FP8_E4M3FN * 1000 + 128: return resident_waves_d<KV_FP8, 128>();
+    case KIND_FP8_QK * 1000 + 64: return resident_waves_d<KV_FP8Q, 64>();
+    case KIND_FP8_QK * 1000 + 128: return resident_waves_d<KV_FP8Q, 128>();
     default: return 0;
     }
 }
@@ -1461,15 +1237,16 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 
 hipError_t launch_attention(int kind, int head_dim, const AttnArgs& a, int64_t max_pieces,
                             hipStream_t s) {
+    if (a.stream == STREAM_WIDE) return launch_span(kind, head_dim, a, max_pieces, s);
     switch (kind * 1000 + head_dim) {
-    case PA_F32 * 1000 + 64: return launch_attention_d<KV_F32, 64>(a, max_pieces, s);
-    case PA_F32 * 1000 + 128: return launch_attention_d<KV_F32, 128>(a, max_pieces, s);
-    case PA_BF16 * 1000 + 64: return launch_attention_d<KV_BF16, 64>(a, max_pieces, s);
-    case PA_BF16 * 1000 + 128: return launch_attention_d<KV_BF16, 128>(a, max_pieces, s);
-    case PA_FP8_E4M3FN * 1000 + 64: return launch_attention_d<KV_FP8, 64>(a, max_pieces, s);
-    case PA_FP8_E4M3FN * 1000 + 128: return launch_attention_d<KV_FP8, 128>(a, max_pieces, s);
-    case KIND_FP8_QK * 1000 + 64: return launch_attention_d<KV_FP8Q, 64>(a, max_pieces, s);
-    case KIND_FP8_QK * 1000 + 128: return launch_attention_d<KV_FP8Q, 128>(a, max_pieces, s);
+    case PA_F32 * 1000 + 64: return launch_narrow_d<KV_F32, 64>(a, max_pieces, s);
+    case PA_F32 * 1000 + 128: return launch_narrow_d<KV_F32, 128>(a, max_pieces, s);
+    case PA_BF16 * 1000 + 64: return launch_narrow_d<KV_BF16, 64>(a, max_pieces, s);
+    case PA_BF16 * 1000 + 128: return launch_narrow_d<KV_BF16, 128>(a, max_pieces, s);
+    case PA_FP8_E4M3FN * 1000 + 64: return launch_narrow_d<KV_FP8, 64>(a, max_pieces, s);
+    case PA_FP8_E4M3FN * 1000 + 128: return launch_narrow_d<KV_FP8, 128>(a, max_pieces, s);
+    case KIND_FP8_QK * 1000 + 64: return launch_narrow_d<KV_FP8Q, 64>(a, max_pieces, s);
+    case KIND_FP8_QK * 1000 + 128: return launch_narrow_d<KV_FP8Q, 128>(a, max_pieces, s);
     default: return hipErrorInvalidValue;
     }
 }

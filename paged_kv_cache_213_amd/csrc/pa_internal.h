@@ -61,28 +61,22 @@ struct SplitSeg {
     int32_t pad[2];
 };
 
-// Two block streams: tiles of multi-token spans (wide: up to 32 rows, two
-// MFMA row tiles share each K/V block) and single-token tiles (narrow: up to
-// 16 rows). Each is cut into its own pieces and run by its own launch.
+// Two block streams: tiles of chunked-prefill spans (wide: up to
+// kSpanRows query rows, run by a workgroup of kSpanWaves waves that share
+// every K/V block through LDS) and tiles of at most 16 rows (narrow:
+// decodes, short spans, shared-prefix group tiles and cascade suffixes; one
+// wave each). Each is cut into its own pieces and run by its own launch.
 enum { STREAM_WIDE = 0, STREAM_NARROW = 1, NUM_STREAMS = 2 };
-// 16-row MFMA tiles in a wide tile. Two keep the bf16 and fp8 wide kernels
-// within 256 VGPRs at two waves per SIMD, with nothing spilled to AGPRs or
-// scratch; four (the K/V bytes then serve twice the rows) needed 256 VGPRs
-// plus 136-160 AGPRs of spill space and SGPR spills.
-#ifndef PA_WIDE_TILES
-#define PA_WIDE_TILES 2
+constexpr int kSpanRows = 128;                // query rows of a wide tile
+constexpr int kSpanRowTiles = kSpanRows / 16;  // 16-row tiles of a wide tile (and slot)
+#ifndef PA_SPAN_WAVES
+#define PA_SPAN_WAVES 4
 #endif
-#ifndef PA_WIDE_TILES_FP8
-#define PA_WIDE_TILES_FP8 PA_WIDE_TILES
-#endif
+constexpr int kSpanWaves = PA_SPAN_WAVES;      // waves of a span workgroup
+static_assert(kSpanWaves == 4 || kSpanWaves == 8, "two or one row tiles per wave");
 // Kernel kinds: the cache dtype, or an fp8 cache whose S = K q^T runs on
 // the fp8 matrix cores (pa_shape.fp8_qk).
 constexpr int KIND_FP8_QK = 3;
-constexpr int wide_tiles(int kind) {
-    return kind == PA_F32                                 ? 2
-           : kind == PA_FP8_E4M3FN || kind == KIND_FP8_QK ? PA_WIDE_TILES_FP8
-                                                          : PA_WIDE_TILES;
-}
 
 // Header words at the start of the workspace: per stream s, the blocks of
 // each KV head's substream, the piece size and the piece count at
@@ -131,10 +125,10 @@ struct PlanArgs {
     int32_t num_tokens;
     int32_t max_context_len;  // contexts are clamped to this
     int32_t narrow_tokens;    // query tokens per narrow tile (16 / G, 1 for decode)
-    int32_t wide_tokens;      // query tokens per wide tile (16 * row tiles / G)
+    int32_t wide_tokens;      // query tokens per wide tile (kSpanRows / G; 0: no spans)
     int32_t num_kv_heads;
     int32_t part_blocks;  // blocks per piece; 0 = balance over the stream's waves
-    int32_t waves[NUM_STREAMS];  // resident waves of each stream's kernel
+    int32_t waves[NUM_STREAMS];  // resident workgroups of each stream's kernel
     int32_t min_blocks;          // smallest piece when balancing
     int32_t max_tiles;
     int64_t max_pieces[NUM_STREAMS];
@@ -178,8 +172,8 @@ struct AttnArgs {
     const PieceStart* pieces;  // this stream's pieces
     const int32_t* hdr;
     int32_t stream;
-    float* part_lse;  // [pieces][2][NT * 16], log2 units
-    float* part_o;    // [pieces][2][NT][D/16][64 lanes] float4, normalized
+    float* part_lse;  // [pieces][2][row tiles * 16], log2 units
+    float* part_o;    // [pieces][2][row tiles][D/16][64 lanes] float4, normalized
     const int32_t* group_members;  // group tiles' members (sequence ids, workspace copy)
     const int32_t* cas_prefix;     // [num_seqs] shared blocks of a cascade member
     float* cas_lse[2];             // CAS_PRE, CAS_SUF per-row buffers
@@ -206,7 +200,7 @@ struct MergeArgs {
     int32_t num_kv_heads;
     int32_t group;
     int32_t max_splits;  // workgroups [0, max_splits) complete cut segments
-    int32_t wide_nt;     // row tiles of the wide stream's slots (by cache dtype)
+    int32_t wide_nt;     // row tiles of the wide stream's slots (kSpanRowTiles)
     const CascadeRec* cas_recs;  // the rest combine cascade parts
     const float* cas_lse[2];
     const float* cas_o[2];
@@ -238,11 +232,16 @@ struct CopyArgs {
 };
 
 // Launchers (host side), defined next to their kernels.
+// The span kernel (wide stream): workgroups that fit on the device at once.
+int span_resident_groups(int kind, int head_dim);
+hipError_t launch_span(int kind, int head_dim, const AttnArgs& a, int64_t max_pieces,
+                       hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attention(int kind, int head_dim, const AttnArgs& a, int64_t max_pieces,
                             hipStream_t s);  // a.stream selects the wide or narrow kernel
-// Waves of the attention kernel of a stream that fit on the device at once
-// (> 0), or 0 if the device cannot be queried.
+// Workgroups of the attention kernel of a stream that fit on the device at
+// once (narrow: waves; wide: span workgroups), or 0 if the device cannot be
+// queried.
 int resident_waves(int kind, int head_dim, int stream);
 // records: cut-segment workgroups (a.max_splits) plus cascade records
 hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t records,

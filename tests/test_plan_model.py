@@ -6,9 +6,9 @@ partition size, the full parallel-sampling batch with its groups, and the
 64 random sharing batches of the GPU suite. Each replay asserts that
 every index is in range, that no two segments write one slot row, cascade
 row or output row, and that every merge read finds the partial the right
-segment wrote for the right row (tests/plan_model.py). Group tiles of one
-and of two 16-row tiles are both replayed; the wave counts include the
-device's (1024 narrow, 2048 wide) and odd ones."""
+segment wrote for the right row (tests/plan_model.py). The resident
+counts include the device's (512 span workgroups, 1024 narrow waves) and
+odd ones."""
 import numpy as np
 import pytest
 
@@ -16,7 +16,7 @@ from paged_kv_cache_213_amd import workloads as W
 from tests import plan_model as PM
 from tests.test_gpu_random_batches import _random_batch, _random_sharing_batch
 
-WAVES = [(2048, 1024), (1024, 1024), (37, 13), (8192, 8192), (512, 256)]
+WAVES = [(512, 1024), (1024, 1024), (37, 13), (8192, 8192), (512, 256)]
 
 
 def _groups(wl):
@@ -24,51 +24,44 @@ def _groups(wl):
 
 
 @pytest.mark.parametrize("waves", WAVES)
-@pytest.mark.parametrize("rt", [1, 2])
 @pytest.mark.parametrize("P", [None, 16, 0])
 @pytest.mark.parametrize("name", ["c4", "c5"])
-def test_small_sharing_batches(name, P, rt, waves):
+def test_small_sharing_batches(name, P, waves):
     wl = W.make_config(name, small=True)
-    _, _, c = PM.replay_workload(wl, waves=waves, groups=_groups(wl), partition_size=P,
-                                 group_row_tiles=rt)
+    _, _, c = PM.replay_workload(wl, waves=waves, groups=_groups(wl), partition_size=P)
     assert c["cascade_records"] > 0
 
 
 @pytest.mark.parametrize("waves", WAVES[:3])
-@pytest.mark.parametrize("rt", [1, 2])
-def test_full_sampling_batch_with_groups(rt, waves):
+def test_full_sampling_batch_with_groups(waves):
     wl = W.make_config("c5")
-    _, _, c = PM.replay_workload(wl, waves=waves, groups=_groups(wl), partition_size=0,
-                                 group_row_tiles=rt)
+    _, _, c = PM.replay_workload(wl, waves=waves, groups=_groups(wl), partition_size=0)
     assert c["cascade_records"] == wl.num_seqs * wl.num_kv_heads
 
 
-@pytest.mark.parametrize("rt", [1, 2])
-def test_full_hybrid_batch_with_groups(rt):
+def test_full_hybrid_batch_with_groups():
     wl = W.make_config("c4")
-    PM.replay_workload(wl, waves=(2048, 1024), groups=_groups(wl), partition_size=0,
-                       group_row_tiles=rt)
+    PM.replay_workload(wl, waves=(512, 1024), groups=_groups(wl), partition_size=0)
 
 
 @pytest.mark.parametrize("seed", range(64))
 def test_random_sharing_batches(seed):
     wl, groups = _random_sharing_batch(seed)
-    for rt in (1, 2):
-        for waves in ((2048, 1024), (37, 13)):
-            PM.replay_workload(wl, waves=waves, groups=groups, group_row_tiles=rt)
+    for waves in ((512, 1024), (37, 13)):
+        PM.replay_workload(wl, waves=waves, groups=groups)
 
 
 @pytest.mark.parametrize("name,P", [("c1", None), ("c2", None), ("c3", None), ("c3", 0),
                                     ("c4", None), ("c4", 0), ("c5", 0)])
 def test_full_configs_without_groups(name, P):
     wl = W.make_config(name)
-    PM.replay_workload(wl, waves=(2048, 1024), partition_size=P)
+    PM.replay_workload(wl, waves=(512, 1024), partition_size=P)
 
 
 @pytest.mark.parametrize("seed", range(24))
 def test_random_hybrid_batches(seed):
     wl = _random_batch(seed)
-    PM.replay_workload(wl, waves=(2048, 1024))
+    PM.replay_workload(wl, waves=(512, 1024))
 
 
 def test_model_catches_a_planted_slot_slip():
@@ -78,7 +71,7 @@ def test_model_catches_a_planted_slot_slip():
     lay = PM.make_layout(G=4, Hkv=wl.num_kv_heads, num_seqs=wl.num_seqs,
                          num_tokens=wl.num_tokens, max_context_len=wl.max_context_len,
                          max_query_len=wl.max_query_len, decode=False, partition_size=16,
-                         cascade=False, waves=(2048, 1024))
+                         cascade=False, waves=(512, 1024))
     qsl = np.asarray(wl.query_start_loc)
     plan = PM.build_plan(lay, Hkv=wl.num_kv_heads, context_lens=wl.context_lens, qsl=qsl,
                          num_tokens=wl.num_tokens, max_context_len=wl.max_context_len)
@@ -119,7 +112,7 @@ def test_model_layout_equals_the_librarys(name, P, grouped):
                          max_context_len=wl.max_context_len,
                          max_query_len=wl.max_query_len if hybrid else 1, decode=not hybrid,
                          partition_size=P, cascade=grouped, waves=tuple(info.waves),
-                         wide_nt=info.wide_row_tiles)
+                         wide_nt=info.wide_row_tiles, f32=wl.kv_dtype == "f32")
     assert (lay.narrow_tokens, lay.wide_tokens, lay.part_blocks, lay.members_per_tile) == (
         info.narrow_tokens, info.wide_tokens, info.part_blocks, info.members_per_tile)
     assert lay.max_tiles == info.max_tiles and lay.max_splits == info.max_splits
