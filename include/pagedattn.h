@@ -271,8 +271,9 @@ int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream);
  * calls make (`decode` = 1 for a plan made with query_start_loc NULL).
  * Region contents, all int32 fields in this order:
  *   header   [64]: tiles, cut segments, cascade records, tree flag, then per
- *            stream s (0 wide, 1 narrow) at 4 + 4 s: blocks per KV head,
- *            blocks per piece, pieces
+ *            stream s (0 wide: chunked-prefill spans; 1 narrow: decodes,
+ *            short spans, cascade suffixes; 2 group: shared-prefix group
+ *            tiles) at 4 + 4 s: blocks per KV head, blocks per piece, pieces
  *   tiles    [max_tiles] x 12: seq, first query token, query tokens, blocks,
  *            context length, first query row, span tokens, flags (1 suffix,
  *            2 group), first block, 3 unused
@@ -288,17 +289,19 @@ int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream);
  * Host only; enqueues nothing. Returns PA_OK, or PA_EINVAL for an invalid
  * shape or size. */
 typedef struct pa_layout_info {
-    int32_t waves[2];          /* resident waves of the wide, narrow kernels */
+    int32_t waves[3];          /* resident workgroups of the wide, narrow and
+                                  group streams' kernels */
     int32_t narrow_tokens;     /* query tokens per narrow tile */
     int32_t wide_tokens;       /* query tokens per wide tile (0: no spans) */
     int32_t part_blocks;       /* partition_size / 16 (0: balanced) */
     int32_t members_per_tile;  /* cascade members per group tile */
     int32_t wide_row_tiles;    /* 16-row tiles of a wide slot */
     int32_t header_words;      /* int32 words of the header */
-    int64_t max_tiles, max_pieces[2], max_splits, max_cas_recs;
+    int32_t reserved;
+    int64_t max_tiles, max_pieces[3], max_splits, max_cas_recs;
     int64_t off_tiles, off_splits, off_tree, off_cas_seq, off_cas_recs;
     int64_t off_cas_lse[2], off_cas_o[2];
-    int64_t off_pieces[2], off_part_lse[2], off_part_o[2];
+    int64_t off_pieces[3], off_part_lse[3], off_part_o[3];
     int64_t total;             /* bytes */
 } pa_layout_info;
 int pa_workspace_layout(const pa_shape* shape, int num_seqs, int num_q_tokens,
@@ -310,7 +313,8 @@ const char* pa_status_string(int status);
 
 /* Library ABI version (major * 100 + minor): 200 added pa_shape.cascade
  * and pa_plan_cascade; 201 added pa_plan_tree; 202 added pa_shape.fp8_qk;
- * 203 added pa_workspace_layout; 204 added pa_paged_attn_hybrid_noalloc. */
+ * 203 added pa_workspace_layout; 204 added pa_paged_attn_hybrid_noalloc;
+ * 205 gave pa_layout_info a third block stream. */
 int pa_version(void);
 
 #ifdef __cplusplus

@@ -49,17 +49,19 @@ class PagedAttentionError(RuntimeError):
 
 
 class PaLayoutInfo(ctypes.Structure):
-    """Workspace regions of a batch (pa_workspace_layout)."""
+    """Workspace regions of a batch (pa_workspace_layout); streams 0 wide,
+    1 narrow, 2 group."""
     _fields_ = [
-        ("waves", ctypes.c_int32 * 2),
+        ("waves", ctypes.c_int32 * 3),
         ("narrow_tokens", ctypes.c_int32),
         ("wide_tokens", ctypes.c_int32),
         ("part_blocks", ctypes.c_int32),
         ("members_per_tile", ctypes.c_int32),
         ("wide_row_tiles", ctypes.c_int32),
         ("header_words", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
         ("max_tiles", ctypes.c_int64),
-        ("max_pieces", ctypes.c_int64 * 2),
+        ("max_pieces", ctypes.c_int64 * 3),
         ("max_splits", ctypes.c_int64),
         ("max_cas_recs", ctypes.c_int64),
         ("off_tiles", ctypes.c_int64),
@@ -69,9 +71,9 @@ class PaLayoutInfo(ctypes.Structure):
         ("off_cas_recs", ctypes.c_int64),
         ("off_cas_lse", ctypes.c_int64 * 2),
         ("off_cas_o", ctypes.c_int64 * 2),
-        ("off_pieces", ctypes.c_int64 * 2),
-        ("off_part_lse", ctypes.c_int64 * 2),
-        ("off_part_o", ctypes.c_int64 * 2),
+        ("off_pieces", ctypes.c_int64 * 3),
+        ("off_part_lse", ctypes.c_int64 * 3),
+        ("off_part_o", ctypes.c_int64 * 3),
         ("total", ctypes.c_int64),
     ]
 

@@ -36,14 +36,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 struct Layout {
     int part_blocks = 0;  // blocks per piece, 0 = balanced over resident waves
     int narrow_tokens = 0, wide_tokens = 0;
-    int waves[pa::NUM_STREAMS] = {0, 0};
+    int waves[pa::NUM_STREAMS] = {};
     int64_t max_tiles = 0;
-    int64_t max_pieces[pa::NUM_STREAMS] = {0, 0};
+    int64_t max_pieces[pa::NUM_STREAMS] = {};
     int64_t max_splits = 0;  // bound of the cut-segment list
     size_t off_tiles = 0, off_splits = 0, total = 0;
-    size_t off_pieces[pa::NUM_STREAMS] = {0, 0};
-    size_t off_lse[pa::NUM_STREAMS] = {0, 0};
-    size_t off_o[pa::NUM_STREAMS] = {0, 0};
+    size_t off_pieces[pa::NUM_STREAMS] = {};
+    size_t off_lse[pa::NUM_STREAMS] = {};
+    size_t off_o[pa::NUM_STREAMS] = {};
     // cascade (shared-prefix groups), when the shape allows them
     bool cascade = false;
     int members_per_tile = 0;
@@ -106,13 +106,13 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     const int64_t T = num_tokens;
     const int64_t tiles_of[pa::NUM_STREAMS] = {
         spans ? std::min((int64_t)num_seqs + cdiv(num_tokens, l.wide_tokens), T) : 0,
-        // narrow: one per sequence, or every span cut into narrow tiles;
-        // then shared-prefix groups' tiles (at most one per group plus one
-        // per members_per_tile members, each sequence in at most one group)
-        (spans || decode ? (int64_t)num_seqs
-                         : std::min((int64_t)num_seqs + cdiv(num_tokens, l.narrow_tokens), T)) +
-            (l.cascade ? 2 * (int64_t)num_seqs : 0)};
-    l.max_tiles = tiles_of[0] + tiles_of[1];
+        // narrow: one per sequence, or every span cut into narrow tiles
+        spans || decode ? (int64_t)num_seqs
+                        : std::min((int64_t)num_seqs + cdiv(num_tokens, l.narrow_tokens), T),
+        // shared-prefix groups' tiles (at most one per group plus one per
+        // members_per_tile members, each sequence in at most one group)
+        l.cascade ? 2 * (int64_t)num_seqs : 0};
+    l.max_tiles = tiles_of[0] + tiles_of[1] + tiles_of[2];
     const int64_t blocks_per_tile = cdiv(max_context_len > 0 ? max_context_len : 1, PA_BLOCK_SIZE);
     size_t off = align_up(sizeof(int32_t) * pa::HDR_WORDS);
     l.off_tiles = off;
@@ -624,6 +624,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 204; }
+int pa_version(void) { return 205; }
 
 }  // extern "C"

@@ -404,10 +404,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     }
 
     // 1. tiles: spans longer than one narrow tile get wide tiles (stream 0);
-    //    everything else narrow ones (stream 1), followed by the groups'
-    //    tiles; sequence order within each
-    int tile_base = 0, nwide = 0;
+    //    everything else narrow ones (stream 1); the groups' tiles form
+    //    stream 2; sequence order within each. Stream st holds tiles
+    //    [t_first[st], t_first[st + 1]).
+    int tile_base = 0;
+    __shared__ int t_first[NUM_STREAMS + 1];
     for (int st = 0; st < NUM_STREAMS; ++st) {
+        if (threadIdx.x == 0) t_first[st] = min(tile_base, cap);
+        if (st != STREAM_GROUP) {
         for (int c0 = 0; c0 < S; c0 += kPlanThreads) {
             const int i = c0 + (int)threadIdx.x;
             int n = 0, L = 0, ntl = 0, qs = 0, tt = 1;
@@ -440,7 +444,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             }
             tile_base += total;
         }
-        if (st == STREAM_NARROW && a.num_groups > 0) {
+        }
+        if (st == STREAM_GROUP && a.num_groups > 0) {
             const int mpt = a.members_per_tile;
             for (int c0 = 0; c0 < a.num_groups; c0 += kPlanThreads) {
                 const int g = c0 + (int)threadIdx.x;
@@ -482,9 +487,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
                 }
             }
         }
-        if (st == STREAM_WIDE) nwide = min(tile_base, cap);
     }
     const int ntiles = min(tile_base, cap);
+    if (threadIdx.x == 0) t_first[NUM_STREAMS] = ntiles;
     __syncthreads();
 
     // 2. exclusive prefix of blocks over tiles (in LDS)
@@ -508,8 +513,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     //    hold the same blocks, B = the stream's tiles' nb summed)
     int Rs[NUM_STREAMS];
     for (int st = 0; st < NUM_STREAMS; ++st) {
-        const int t_lo = st == STREAM_WIDE ? 0 : nwide;
-        const int t_hi = st == STREAM_WIDE ? nwide : ntiles;
+        const int t_lo = t_first[st], t_hi = t_first[st + 1];
         const int64_t B = s_tp[t_hi] - s_tp[t_lo];
         int64_t R = a.part_blocks;
         if (R <= 0) {
@@ -549,10 +553,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
     }
     // pieces of substream h holding a segment's first and last blocks
+    auto stream_of = [&](int t) {
+        return t < t_first[STREAM_NARROW] ? STREAM_WIDE
+               : t < t_first[STREAM_GROUP] ? STREAM_NARROW
+                                           : STREAM_GROUP;
+    };
     auto cut = [&](int t, int& k0, int& k1) {
-        const int st = t < nwide ? STREAM_WIDE : STREAM_NARROW;
-        const int t_lo = st == STREAM_WIDE ? 0 : nwide;
-        const int b0 = s_tp[t] - s_tp[t_lo];
+        const int st = stream_of(t);
+        const int b0 = s_tp[t] - s_tp[t_first[st]];
         k0 = b0 / Rs[st];
         k1 = (b0 + s_tp[t + 1] - s_tp[t] - 1) / Rs[st];
     };
@@ -571,7 +579,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             const int k = atomicAdd(&s_nsplit, 1);  // list order is irrelevant
             if (k < max_splits)
                 a.splits[k] = SplitSeg{td.qs + td.qtok0, td.ntok, h, k0, k1,
-                                       t < nwide ? STREAM_WIDE : STREAM_NARROW, {0, 0}};
+                                       stream_of(t), {0, 0}};
         }
     }
     __syncthreads();
@@ -617,8 +625,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 // ---- attention ---------------------------------------------------------------
 
 // K/V blocks in flight per wave beyond the one in use (one wave per SIMD).
+// An fp8 block is half the bytes of a bf16 one, so fp8 caches keep more
+// blocks in flight for the same bytes.
 #ifndef PA_PREFETCH
 #define PA_PREFETCH 2
+#endif
+#ifndef PA_PREFETCH_FP8
+#define PA_PREFETCH_FP8 2
+#endif
+// Group tiles (a shared prefix read for several members) load through L2
+// (1) or stream past it like the other narrow tiles (0).
+#ifndef PA_GROUP_L2
+#define PA_GROUP_L2 0
 #endif
 
 // Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
@@ -628,15 +646,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 // loads. Then either write the rows' output (the wave saw the whole
 // segment) or write a partial result into the piece's slot for the merge
 // pass.
-template <int kv, int D>
+template <int kv, int D, bool kStreamLoads>
 __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td, const int kvh,
                                             const int j, const int take, const int piece) {
     using T = Tile<kv, D>;
     constexpr int NT = 1, NR = 1;  // row tiles of a slot, and holding rows
-    // a single-token tile's blocks (a decode's context, a cascade member's
-    // suffix, a group's prefix in its group tile) are read by no other tile
-    // of the call, so they are streamed past the caches
-    constexpr bool kStreamLoads = PA_NT_LOADS;
     constexpr bool kFp8Cache = kv == KV_FP8 || kv == KV_FP8Q;
     using QReg = typename std::conditional<
         kv == KV_F32, float[D / 4],
@@ -836,7 +850,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             const int ph = __builtin_amdgcn_readlane(my_phys, i);
             dst.template load<kStreamLoads>(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
         };
-        constexpr int PF = PA_PREFETCH;
+        constexpr int PF = kFp8Cache ? PA_PREFETCH_FP8 : PA_PREFETCH;
         // ring of PF + 1 register tiles: PF blocks stay in flight while one is
         // consumed. In the steady-state loop every refill is in range, so it
         // is straight-line code in which each wait covers exactly one block;
@@ -933,7 +947,12 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
         int left = (int)min((int64_t)R, (int64_t)B - (int64_t)(v / Hkv) * R);
         while (left > 0) {
             const int take = min(left, td.nb - j);
-            run_segment<kv, D>(a, td, kvh, j, take, v);
+            // a decode's context and a cascade member's suffix are read by no
+            // other tile of the call, so they are streamed past the caches
+            if (PA_GROUP_L2 && td.flags == TILE_GROUP)
+                run_segment<kv, D, false>(a, td, kvh, j, take, v);
+            else
+                run_segment<kv, D, PA_NT_LOADS != 0>(a, td, kvh, j, take, v);
             left -= take;
             j = 0;
             ++t;
@@ -1035,8 +1054,8 @@ __device__ __forceinline__ void merge_cascade(const MergeArgs& a, const CascadeR
             acc.add(a.cas_lse[kind][row], x);
             continue;
         }
-        // both parts are narrow tiles (one 16-row tile per slot)
-        const int st = STREAM_NARROW;
+        // group tiles and suffix tiles hold one 16-row tile per slot
+        const int st = kind == CAS_PRE ? STREAM_GROUP : STREAM_NARROW;
         const int nt = 1;
         const int rr = (kind == CAS_PRE ? rc.pre_pos * G : 0) + n;  // row in the slot
         const float4* po = (const float4*)a.part_o[st];

@@ -57,16 +57,19 @@ struct SplitSeg {
     int32_t kvh;
     int32_t k0;
     int32_t k1;
-    int32_t stream;  // STREAM_WIDE or STREAM_NARROW
+    int32_t stream;  // STREAM_WIDE, STREAM_NARROW or STREAM_GROUP
     int32_t pad[2];
 };
 
-// Two block streams: tiles of chunked-prefill spans (wide: up to
+// Three block streams: tiles of chunked-prefill spans (wide: up to
 // kSpanRows query rows, run by a workgroup of kSpanWaves waves that share
-// every K/V block through LDS) and tiles of at most 16 rows (narrow:
-// decodes, short spans, shared-prefix group tiles and cascade suffixes; one
-// wave each). Each is cut into its own pieces and run by its own launch.
-enum { STREAM_WIDE = 0, STREAM_NARROW = 1, NUM_STREAMS = 2 };
+// every K/V block through LDS); tiles of at most 16 rows (narrow: decodes,
+// short spans and cascade suffixes; one wave each); and shared-prefix group
+// tiles (one wave each, as the narrow ones). Each is cut into its own
+// pieces and run by its own launch, so a stream's pieces balance among
+// segments of like cost: a group's long prefix does not share a piece
+// count with the one-block suffixes of its members.
+enum { STREAM_WIDE = 0, STREAM_NARROW = 1, STREAM_GROUP = 2, NUM_STREAMS = 3 };
 constexpr int kSpanRows = 128;                // query rows of a wide tile
 constexpr int kSpanRowTiles = kSpanRows / 16;  // 16-row tiles of a wide tile (and slot)
 #ifndef PA_SPAN_WAVES

@@ -6,8 +6,8 @@ rules (the workspace records of pa_internal.h):
 
 - tiles: query rows grouped per span (narrow tiles of up to 16 rows; wide
   tiles of up to 128 rows for chunked-prefill spans, which f32 caches keep
-  in narrow tiles), and, in the narrow stream, shared-prefix group tiles and
-  the suffix tiles of cascade members;
+  in narrow tiles), the suffix tiles of cascade members (narrow), and
+  shared-prefix group tiles (a stream of their own);
 - one stream of 16-token key blocks per tile class, one substream per KV
   head, cut into pieces of R blocks (balanced over the resident waves, or
   partition_size / 16); piece k of head h is piece k * Hkv + h;
@@ -29,7 +29,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-STREAM_WIDE, STREAM_NARROW = 0, 1
+STREAM_WIDE, STREAM_NARROW, STREAM_GROUP = 0, 1, 2
+STREAMS = (STREAM_WIDE, STREAM_NARROW, STREAM_GROUP)
 TILE_SUFFIX, TILE_GROUP = 1, 2
 SLOT_HEAD, SLOT_TAIL = 0, 1
 CAS_PRE, CAS_SUF = 0, 1
@@ -83,24 +84,24 @@ def make_layout(*, G, Hkv, num_seqs, num_tokens, max_context_len, max_query_len,
     mpt = max(16 // G, 1)
     T = num_tokens
     tiles_of = [min(num_seqs + cdiv(num_tokens, wide), T) if spans else 0,
-                (num_seqs if (spans or decode) else min(num_seqs + cdiv(num_tokens, narrow), T))
-                + (2 * num_seqs if cascade else 0)]
+                num_seqs if (spans or decode) else min(num_seqs + cdiv(num_tokens, narrow), T),
+                2 * num_seqs if cascade else 0]
     bpt = cdiv(max(max_context_len, 1), 16)
     max_pieces, splits = [], 0
-    for st in range(2):
+    for st in STREAMS:
         per_head = cdiv(tiles_of[st] * bpt, part) if part > 0 else cdiv(waves[st], Hkv)
         mp = Hkv * per_head if tiles_of[st] else 0
         max_pieces.append(mp)
         if mp > 0:
             splits += min(mp - Hkv, tiles_of[st] * Hkv)
-    return Layout(narrow, wide, part, tuple(waves), tiles_of[0] + tiles_of[1],
+    return Layout(narrow, wide, part, tuple(waves), sum(tiles_of),
                   tuple(max_pieces), splits, mpt, num_seqs * Hkv if cascade else 0, wide_nt)
 
 
 @dataclass
 class Plan:
     tiles: list
-    nwide: int
+    t_first: list  # stream st holds tiles [t_first[st], t_first[st + 1])
     R: list
     B: list
     pieces: list  # per stream: list of (tile, kvh, j)
@@ -151,9 +152,10 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
                 cas_prefix[i] = prefix[g]
 
     tiles = []
-    nwide = 0
-    for st in (STREAM_WIDE, STREAM_NARROW):
-        for i in range(S):
+    t_first = []
+    for st in STREAMS:
+        t_first.append(len(tiles))
+        for i in range(S if st != STREAM_GROUP else 0):
             qs, n, L = span_of(i)
             wide = lay.wide_tokens > 0 and n > lay.narrow_tokens
             tt = lay.wide_tokens if wide else lay.narrow_tokens
@@ -169,7 +171,7 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
                     td.flags, td.b0, td.nb = TILE_SUFFIX, pre, nb - pre
                     cas_tile[i] = len(tiles)
                 tiles.append(td)
-        if st == STREAM_NARROW and ngroups > 0:
+        if st == STREAM_GROUP and ngroups > 0:
             mpt = lay.members_per_tile
             gbase = []
             for g in range(ngroups):
@@ -189,8 +191,7 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
                     m = e - offsets[g]
                     cas_gtile[i] = gbase[g] + m // mpt
                     cas_pos[i] = m % mpt
-        if st == STREAM_WIDE:
-            nwide = len(tiles)
+    t_first.append(len(tiles))
     assert len(tiles) <= min(lay.max_tiles, MAX_TILES), "tiles past the plan's bound"
 
     tp = [0]
@@ -198,8 +199,8 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
         tp.append(tp[-1] + td.nb)
 
     R, B, pieces = [], [], []
-    for st in (STREAM_WIDE, STREAM_NARROW):
-        t_lo, t_hi = (0, nwide) if st == STREAM_WIDE else (nwide, len(tiles))
+    for st in STREAMS:
+        t_lo, t_hi = t_first[st], t_first[st + 1]
         b = tp[t_hi] - tp[t_lo]
         r = lay.part_blocks
         if r <= 0:
@@ -222,10 +223,12 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
         B.append(b)
         pieces.append(ps)
 
+    def stream_of(t):
+        return max(st for st in STREAMS if t_first[st] <= t)
+
     def cut(t):
-        st = STREAM_WIDE if t < nwide else STREAM_NARROW
-        t_lo = 0 if st == STREAM_WIDE else nwide
-        b0 = tp[t] - tp[t_lo]
+        st = stream_of(t)
+        b0 = tp[t] - tp[t_first[st]]
         return b0 // R[st], (b0 + tiles[t].nb - 1) // R[st]
 
     splits = []
@@ -235,8 +238,7 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
                 continue
             k0, k1 = cut(t)
             if k0 != k1:
-                splits.append((td.qs + td.qtok0, td.ntok, h, k0, k1,
-                               STREAM_WIDE if t < nwide else STREAM_NARROW))
+                splits.append((td.qs + td.qtok0, td.ntok, h, k0, k1, stream_of(t)))
     assert len(splits) <= lay.max_splits, "cut segments past the list's bound"
 
     cas_recs = []
@@ -247,7 +249,7 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
             for h in range(H):
                 cas_recs.append((tiles[cas_tile[i]].qs, h, sk0, sk1, pk0, pk1, cas_pos[i]))
     assert len(cas_recs) <= lay.max_cas_recs or not cas_recs
-    return Plan(tiles, nwide, R, B, pieces, splits, cas_recs, cas_prefix, cas_tile, cas_gtile,
+    return Plan(tiles, t_first, R, B, pieces, splits, cas_recs, cas_prefix, cas_tile, cas_gtile,
                 cas_pos, tp)
 
 
@@ -289,7 +291,7 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
                 res.append((r, n, row))
         return res
 
-    for st in (STREAM_WIDE, STREAM_NARROW):
+    for st in STREAMS:
         NT = lay.wide_nt if st == STREAM_WIDE else 1
         R, B = plan.R[st], plan.B[st]
         max_slots = 2 * lay.max_pieces[st]
@@ -298,7 +300,7 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
             left = min(R, B - (v // Hkv) * R)
             td = plan.tiles[t]
             while left > 0:
-                assert (t < plan.nwide) == (st == STREAM_WIDE), "piece walked into the other stream"
+                assert plan.t_first[st] <= t < plan.t_first[st + 1], "piece left its stream"
                 take = min(left, td.nb - j)
                 assert take > 0
                 nrt = cdiv(td.ntok * G, 16)
@@ -358,7 +360,7 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
                     assert tag[1:] == (kvh, row)
                     n_read += 1
                     continue
-                st = STREAM_NARROW  # group tiles and suffix tiles are narrow
+                st = STREAM_GROUP if kind == CAS_PRE else STREAM_NARROW
                 nt = 1
                 rr = (pos * G if kind == CAS_PRE else 0) + n
                 for k in range(k0, k1 + 1):

@@ -71,7 +71,7 @@ def _compare(wl, groups, P):
     want = np.array([[t.seq, t.qtok0, t.ntok, t.nb, t.L, t.qs, t.nspan, t.flags, t.b0]
                      for t in plan.tiles], np.int32).reshape(-1, 9)
     assert np.array_equal(tiles[:, :9], want), "tile records differ"
-    for st in (0, 1):
+    for st in (0, 1, 2):
         B, R, V = (int(x) for x in hdr[4 + 4 * st: 7 + 4 * st])
         assert (B, R, V) == (plan.B[st], plan.R[st], len(plan.pieces[st])), f"stream {st}"
         if V:

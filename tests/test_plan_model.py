@@ -7,8 +7,9 @@ partition size, the full parallel-sampling batch with its groups, and the
 every index is in range, that no two segments write one slot row, cascade
 row or output row, and that every merge read finds the partial the right
 segment wrote for the right row (tests/plan_model.py). The resident
-counts include the device's (512 span workgroups, 1024 narrow waves) and
-odd ones."""
+counts include the device's (512 span workgroups, 1024 narrow and group
+waves) and
+odd ones, for the wide, narrow and group streams."""
 import numpy as np
 import pytest
 
@@ -16,7 +17,7 @@ from paged_kv_cache_213_amd import workloads as W
 from tests import plan_model as PM
 from tests.test_gpu_random_batches import _random_batch, _random_sharing_batch
 
-WAVES = [(512, 1024), (1024, 1024), (37, 13), (8192, 8192), (512, 256)]
+WAVES = [(512, 1024, 1024), (1024, 1024, 1024), (37, 13, 29), (8192, 8192, 8192), (512, 256, 64)]
 
 
 def _groups(wl):
@@ -41,13 +42,13 @@ def test_full_sampling_batch_with_groups(waves):
 
 def test_full_hybrid_batch_with_groups():
     wl = W.make_config("c4")
-    PM.replay_workload(wl, waves=(512, 1024), groups=_groups(wl), partition_size=0)
+    PM.replay_workload(wl, waves=(512, 1024, 1024), groups=_groups(wl), partition_size=0)
 
 
 @pytest.mark.parametrize("seed", range(64))
 def test_random_sharing_batches(seed):
     wl, groups = _random_sharing_batch(seed)
-    for waves in ((512, 1024), (37, 13)):
+    for waves in ((512, 1024, 1024), (37, 13, 29)):
         PM.replay_workload(wl, waves=waves, groups=groups)
 
 
@@ -55,13 +56,13 @@ def test_random_sharing_batches(seed):
                                     ("c4", None), ("c4", 0), ("c5", 0)])
 def test_full_configs_without_groups(name, P):
     wl = W.make_config(name)
-    PM.replay_workload(wl, waves=(512, 1024), partition_size=P)
+    PM.replay_workload(wl, waves=(512, 1024, 1024), partition_size=P)
 
 
 @pytest.mark.parametrize("seed", range(24))
 def test_random_hybrid_batches(seed):
     wl = _random_batch(seed)
-    PM.replay_workload(wl, waves=(512, 1024))
+    PM.replay_workload(wl, waves=(512, 1024, 1024))
 
 
 def test_model_catches_a_planted_slot_slip():
@@ -71,7 +72,7 @@ def test_model_catches_a_planted_slot_slip():
     lay = PM.make_layout(G=4, Hkv=wl.num_kv_heads, num_seqs=wl.num_seqs,
                          num_tokens=wl.num_tokens, max_context_len=wl.max_context_len,
                          max_query_len=wl.max_query_len, decode=False, partition_size=16,
-                         cascade=False, waves=(512, 1024))
+                         cascade=False, waves=(512, 1024, 1024))
     qsl = np.asarray(wl.query_start_loc)
     plan = PM.build_plan(lay, Hkv=wl.num_kv_heads, context_lens=wl.context_lens, qsl=qsl,
                          num_tokens=wl.num_tokens, max_context_len=wl.max_context_len)
