@@ -84,11 +84,13 @@ typedef enum pa_status {
  * positive multiple of 16 (pieces of that many tokens). Query rows are
  * grouped into tiles: a span of at most 16 / G tokens (every decode) is one
  * narrow tile of G * n_i rows; a longer span is cut into wide tiles of
- * 32 / G tokens. A call may hold at most 8192 tiles,
- * counted as 2 * num_seqs + ceil(num_q_tokens / (32 / G)) for a hybrid call
- * and num_seqs for a decode call, plus 2 * num_seqs when cascade is 1;
- * beyond that it returns PA_ENOTSUP, as it does when num_q_tokens *
- * num_q_heads reaches 2^31 - 1 (output rows are indexed with 32 bits). */
+ * 128 / G tokens (F32 caches: into narrow tiles of 16 / G tokens). A call
+ * may hold at most 8192 tiles, counted as num_seqs for a decode call and,
+ * for a hybrid call, num_seqs + min(num_seqs + ceil(num_q_tokens /
+ * (128 / G)), num_q_tokens) (F32: min(num_seqs + ceil(num_q_tokens /
+ * (16 / G)), num_q_tokens)), plus 2 * num_seqs when cascade is 1; beyond
+ * that it returns PA_ENOTSUP, as it does when num_q_tokens * num_q_heads
+ * reaches 2^31 - 1 (output rows are indexed with 32 bits). */
 typedef struct pa_shape {
     int32_t num_q_heads;        /* Hq */
     int32_t num_kv_heads;       /* Hkv */
