@@ -9,8 +9,9 @@
  * Query heads are grouped onto KV heads (GQA; "References", GQA entry).
  * A batch may mix single-token decodes with chunked-prefill spans
  * ("03 -- Engines Papers", section 3). The key blocks of the whole batch
- * are split into pieces of equal size, one per resident wave, so long and
- * short contexts finish together; a context cut by a piece boundary is
+ * are split into pieces of equal work (blocks plus a fixed cost for each
+ * context a piece starts), one per resident wave, so long and short
+ * contexts finish together; a context cut by a piece boundary is
  * completed by a log-sum-exp merge of its pieces' partial results (the
  * split-K decode pattern of the playbook's Theme 4; the LSE merge of
  * "03 -- Engines Papers", section 12). The cache may be stored as FP8 E4M3
@@ -275,12 +276,13 @@ int pa_fp8_e4m3fn_to_f32(const uint8_t* in, float* out, int n, void* stream);
  *   header   [64]: tiles, cut segments, cascade records, tree flag, then per
  *            stream s (0 wide: chunked-prefill spans; 1 narrow: decodes,
  *            short spans, cascade suffixes; 2 group: shared-prefix group
- *            tiles) at 4 + 4 s: blocks per KV head, blocks per piece, pieces
+ *            tiles) at 4 + 4 s: blocks per KV head, work per piece (blocks
+ *            plus a fixed cost per segment started), pieces
  *   tiles    [max_tiles] x 12: seq, first query token, query tokens, blocks,
  *            context length, first query row, span tokens, flags (1 suffix,
  *            2 group), first block, 3 unused
- *   pieces   per stream [max_pieces] x 16: tile, KV head, first block, unused,
- *            then a copy of that tile's 12 fields
+ *   pieces   per stream [max_pieces] x 16: tile, KV head, first block,
+ *            blocks in the piece, then a copy of that tile's 12 fields
  *   splits   [max_splits] x 8: first row, query tokens, KV head, first and
  *            last piece, stream, 2 unused (past the header's count: k0 = -1)
  *   cascade  cas_seq: 6 x [num_seqs] (member prefix blocks, suffix tile,
@@ -299,7 +301,8 @@ typedef struct pa_layout_info {
     int32_t members_per_tile;  /* cascade members per group tile */
     int32_t wide_row_tiles;    /* 16-row tiles of a wide slot */
     int32_t header_words;      /* int32 words of the header */
-    int32_t reserved;
+    int32_t part_cost[3];      /* when balancing: a segment's start in blocks
+                                  of work, per stream */
     int64_t max_tiles, max_pieces[3], max_splits, max_cas_recs;
     int64_t off_tiles, off_splits, off_tree, off_cas_seq, off_cas_recs;
     int64_t off_cas_lse[2], off_cas_o[2];
@@ -316,7 +319,8 @@ const char* pa_status_string(int status);
 /* Library ABI version (major * 100 + minor): 200 added pa_shape.cascade
  * and pa_plan_cascade; 201 added pa_plan_tree; 202 added pa_shape.fp8_qk;
  * 203 added pa_workspace_layout; 204 added pa_paged_attn_hybrid_noalloc;
- * 205 gave pa_layout_info a third block stream. */
+ * 205 gave pa_layout_info a third block stream; 206 gave piece records
+ * their block counts and pa_layout_info the per-stream part costs. */
 int pa_version(void);
 
 #ifdef __cplusplus

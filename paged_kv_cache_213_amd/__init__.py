@@ -59,7 +59,7 @@ class PaLayoutInfo(ctypes.Structure):
         ("members_per_tile", ctypes.c_int32),
         ("wide_row_tiles", ctypes.c_int32),
         ("header_words", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("part_cost", ctypes.c_int32 * 3),
         ("max_tiles", ctypes.c_int64),
         ("max_pieces", ctypes.c_int64 * 3),
         ("max_splits", ctypes.c_int64),

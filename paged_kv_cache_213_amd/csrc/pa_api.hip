@@ -14,6 +14,19 @@
 #define PA_WIDE_SPANS 1
 #endif
 
+// The cost of a segment's start, in blocks of work, when pieces are
+// balanced (the plan cuts pieces at equal blocks + cost). A span segment
+// starts by loading 128 query rows and ends by writing 128 output rows, some
+// six blocks' worth of K/V traffic; a narrow segment's setup hides under its
+// first loads (measured: a cost of 2 to 5 left the decode batches' times
+// unchanged or slower, while the span kernel gained 7% at 6).
+#ifndef PA_PART_COST
+#define PA_PART_COST 0
+#endif
+#ifndef PA_PART_COST_WIDE
+#define PA_PART_COST_WIDE 6
+#endif
+
 // Scratch of pa_paged_attn_hybrid_noalloc, in static device memory: each
 // GPU the library runs on holds its own copy until the process ends. Host
 // code never passes this name to a kernel (on the host it is only a stand-in
@@ -37,6 +50,7 @@ struct Layout {
     int part_blocks = 0;  // blocks per piece, 0 = balanced over resident waves
     int narrow_tokens = 0, wide_tokens = 0;
     int waves[pa::NUM_STREAMS] = {};
+    int part_cost[pa::NUM_STREAMS] = {};
     int64_t max_tiles = 0;
     int64_t max_pieces[pa::NUM_STREAMS] = {};
     int64_t max_splits = 0;  // bound of the cut-segment list
@@ -121,6 +135,7 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
         const int w = pa::resident_waves(kernel_kind(s), s->head_dim, st);
         l.waves[st] = w > 0 ? w : kWaveBound;
+        l.part_cost[st] = st == pa::STREAM_WIDE ? PA_PART_COST_WIDE : PA_PART_COST;
         // pieces per KV head substream: ceil(B / R) with B <= tiles * blocks
         // per tile, and R = P / 16, or R >= Hkv * B / waves when balanced
         const int64_t H = s->num_kv_heads;
@@ -237,6 +252,7 @@ int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl
     pl.max_tiles = (int32_t)l.max_tiles;
     pl.tiles = (pa::TileDesc*)(ws + l.off_tiles);
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
+        pl.part_cost[st] = l.part_cost[st];
         pl.waves[st] = l.waves[st];
         pl.max_pieces[st] = l.max_pieces[st];
         pl.pieces[st] = (pa::PieceStart*)(ws + l.off_pieces[st]);
@@ -583,6 +599,7 @@ int pa_workspace_layout(const pa_shape* shape, int num_seqs, int num_q_tokens,
     pa_layout_info r{};
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
         r.waves[st] = l.waves[st];
+        r.part_cost[st] = l.part_cost[st];
         r.max_pieces[st] = l.max_pieces[st];
         r.off_pieces[st] = (int64_t)l.off_pieces[st];
         r.off_part_lse[st] = (int64_t)l.off_lse[st];
@@ -624,6 +641,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 205; }
+int pa_version(void) { return 206; }
 
 }  // extern "C"

@@ -510,40 +510,62 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     __syncthreads();
 
     // 3. per stream: piece size, piece starts (all KV heads' substreams
-    //    hold the same blocks, B = the stream's tiles' nb summed)
-    int Rs[NUM_STREAMS];
+    //    hold the same blocks, B = the stream's tiles' nb summed). When
+    //    balancing, pieces are cut at equal cost, where a segment costs its
+    //    blocks plus c blocks for its start (row setup, the first block's
+    //    latency, the epilogue): a piece that starts more segments gets
+    //    fewer blocks, so waves finish together. In the cost coordinate the
+    //    c units of a tile come before its blocks; a piece that starts
+    //    inside them starts at the tile's first block. With at least c + 1
+    //    units per piece no piece is empty. A fixed partition size uses c =
+    //    0, pieces of exactly P / 16 blocks.
+    int Rs[NUM_STREAMS], Cs[NUM_STREAMS];
     for (int st = 0; st < NUM_STREAMS; ++st) {
         const int t_lo = t_first[st], t_hi = t_first[st + 1];
         const int64_t B = s_tp[t_hi] - s_tp[t_lo];
+        const int c = a.part_blocks > 0 ? 0 : max(a.part_cost[st], 0);
+        const int64_t Bc = B + (int64_t)c * (t_hi - t_lo);  // cost of the substream
         int64_t R = a.part_blocks;
         if (R <= 0) {
-            R = ((int64_t)H * B + a.waves[st] - 1) / max(a.waves[st], 1);
-            R = max(R, (int64_t)a.min_blocks);
+            R = ((int64_t)H * Bc + a.waves[st] - 1) / max(a.waves[st], 1);
+            R = max(R, (int64_t)a.min_blocks + c);
         }
-        int64_t K = (B + R - 1) / R;  // pieces per substream
+        int64_t K = (Bc + R - 1) / R;  // pieces per substream
         const int64_t kmax = a.max_pieces[st] / H;
         if (kmax == 0) {  // no room: the caller understated max_query_len
             K = 0;
         } else if (K > kmax) {  // never for sizes the host planned for
-            R = (B + kmax - 1) / kmax;
-            K = (B + R - 1) / R;
+            R = max((Bc + kmax - 1) / kmax, (int64_t)c + 1);
+            K = (Bc + R - 1) / R;
         }
         R = max(R, (int64_t)1);
         Rs[st] = (int)R;
+        Cs[st] = c;
+        // the stream position (blocks) of cost coordinate x
+        auto position = [&](int64_t x, int& tile, int& jj) {
+            int lo = t_lo, hi = t_hi - 1;  // last tile whose cost prefix is <= x
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                const int64_t cp = (int64_t)(s_tp[mid] - s_tp[t_lo]) + (int64_t)c * (mid - t_lo);
+                if (cp <= x) lo = mid; else hi = mid - 1;
+            }
+            const int64_t cp = (int64_t)(s_tp[lo] - s_tp[t_lo]) + (int64_t)c * (lo - t_lo);
+            tile = lo;
+            jj = (int)max((int64_t)0, x - cp - c);
+        };
         const int64_t V = K * H;
         for (int64_t v = threadIdx.x; v < V; v += kPlanThreads) {
             const int h = (int)(v % H);
-            const int key = s_tp[t_lo] + (int)((v / H) * R);  // block offset in the tile prefix
-            int lo = t_lo, hi = t_hi - 1;  // last tile whose prefix is <= key
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (s_tp[mid] <= key) lo = mid; else hi = mid - 1;
-            }
+            const int64_t k = v / H;
+            int t0, j0, t1 = t_hi, j1 = 0;
+            position(k * R, t0, j0);
+            if (k + 1 < K) position((k + 1) * R, t1, j1);
             PieceStart ps{};
-            ps.tile = lo;
+            ps.tile = t0;
             ps.kvh = h;
-            ps.j = key - s_tp[lo];
-            ps.td = a.tiles[lo];
+            ps.j = j0;
+            ps.nblocks = (s_tp[t1] + j1) - (s_tp[t0] + j0);
+            ps.td = a.tiles[t0];
             a.pieces[st][v] = ps;
         }
         if (threadIdx.x == 0) {
@@ -552,17 +574,20 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
             a.hdr[HDR_STREAM + 4 * st + HDR_NPIECES] = (int)V;
         }
     }
-    // pieces of substream h holding a segment's first and last blocks
     auto stream_of = [&](int t) {
         return t < t_first[STREAM_NARROW] ? STREAM_WIDE
                : t < t_first[STREAM_GROUP] ? STREAM_NARROW
                                            : STREAM_GROUP;
     };
+    // pieces of substream h holding a segment's first and last blocks: the
+    // block at stream offset b of tile t sits at cost b + c (t - t_lo + 1)
     auto cut = [&](int t, int& k0, int& k1) {
         const int st = stream_of(t);
-        const int b0 = s_tp[t] - s_tp[t_first[st]];
-        k0 = b0 / Rs[st];
-        k1 = (b0 + s_tp[t + 1] - s_tp[t] - 1) / Rs[st];
+        const int t_lo = t_first[st];
+        const int64_t x0 =
+            (int64_t)(s_tp[t] - s_tp[t_lo]) + (int64_t)Cs[st] * (t - t_lo + 1);
+        k0 = (int)(x0 / Rs[st]);
+        k1 = (int)((x0 + s_tp[t + 1] - s_tp[t] - 1) / Rs[st]);
     };
 
     // 4. segments cut by a piece boundary, for the merge pass (a segment is
@@ -936,15 +961,13 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 template <int kv, int D>
 __device__ __forceinline__ void attention_body(const AttnArgs& a) {
     const int* h = a.hdr + HDR_STREAM + 4 * a.stream;
-    const int V = h[HDR_NPIECES], R = h[HDR_R], B = h[HDR_TOTAL];
-    const int Hkv = a.num_kv_heads;
+    const int V = h[HDR_NPIECES];
     for (int v = blockIdx.x; v < V; v += gridDim.x) {
         const PieceStart ps = a.pieces[v];
         int t = ps.tile, j = ps.j;
         const int kvh = ps.kvh;
         TileDesc td = ps.td;
-        // the piece's blocks, within its KV head's substream
-        int left = (int)min((int64_t)R, (int64_t)B - (int64_t)(v / Hkv) * R);
+        int left = ps.nblocks;  // the piece's blocks, within its KV head's substream
         while (left > 0) {
             const int take = min(left, td.nb - j);
             // a decode's context and a cascade member's suffix are read by no

@@ -37,13 +37,13 @@ struct TileDesc {
 };
 
 // Where a piece of the block stream begins: segment (tile, kv head), block j
-// (counted from the tile's b0), with a copy of that tile's record so a wave
-// starts with one load.
+// (counted from the tile's b0), the piece's length in blocks, and a copy of
+// that tile's record so a wave starts with one load.
 struct PieceStart {
     int32_t tile;
     int32_t kvh;
     int32_t j;
-    int32_t pad;
+    int32_t nblocks;
     TileDesc td;
 };
 
@@ -82,8 +82,8 @@ static_assert(kSpanWaves == 4 || kSpanWaves == 8, "two or one row tiles per wave
 constexpr int KIND_FP8_QK = 3;
 
 // Header words at the start of the workspace: per stream s, the blocks of
-// each KV head's substream, the piece size and the piece count at
-// HDR_STREAM + 4 s.
+// each KV head's substream, the piece size (in blocks of cost when
+// balancing) and the piece count at HDR_STREAM + 4 s.
 enum {
     HDR_NTILES = 0,
     HDR_NSPLIT = 1,
@@ -131,6 +131,9 @@ struct PlanArgs {
     int32_t wide_tokens;      // query tokens per wide tile (kSpanRows / G; 0: no spans)
     int32_t num_kv_heads;
     int32_t part_blocks;  // blocks per piece; 0 = balance over the stream's waves
+    // when balancing: the cost of a segment's start in blocks of work (its
+    // row setup, the first block's latency, its epilogue), per stream
+    int32_t part_cost[NUM_STREAMS];
     int32_t waves[NUM_STREAMS];  // resident workgroups of each stream's kernel
     int32_t min_blocks;          // smallest piece when balancing
     int32_t max_tiles;

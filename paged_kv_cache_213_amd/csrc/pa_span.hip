@@ -519,14 +519,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kSpanW
 attention_span(AttnArgs a) {
     __shared__ __align__(16) uint8_t smem[2 * SpanLds<D>::kBufBytes];
     const int* h = a.hdr + HDR_STREAM + 4 * a.stream;
-    const int V = h[HDR_NPIECES], R = h[HDR_R], B = h[HDR_TOTAL];
-    const int Hkv = a.num_kv_heads;
+    const int V = h[HDR_NPIECES];
     for (int v = blockIdx.x; v < V; v += gridDim.x) {
         const PieceStart ps = a.pieces[v];
         int t = ps.tile, j = ps.j;
         const int kvh = ps.kvh;
         TileDesc td = ps.td;
-        int left = (int)min((int64_t)R, (int64_t)B - (int64_t)(v / Hkv) * R);
+        int left = ps.nblocks;
         while (left > 0) {
             const int take = min(left, td.nb - j);
             span_segment<kv, D>(a, smem, td, kvh, j, take, v);

@@ -67,13 +67,18 @@ class Layout:
     members_per_tile: int
     max_cas_recs: int
     wide_nt: int
+    part_cost: tuple
 
 
 SPAN_ROWS = 128  # query rows of a wide tile (four waves of 32)
+# when balancing, the cost of a segment's start in blocks of work, per stream
+# (wide, narrow, group)
+PART_COST = (6, 0, 0)
 
 
 def make_layout(*, G, Hkv, num_seqs, num_tokens, max_context_len, max_query_len, decode,
-                partition_size, cascade, waves, wide_nt=SPAN_ROWS // 16, f32=False):
+                partition_size, cascade, waves, wide_nt=SPAN_ROWS // 16, f32=False,
+                part_cost=PART_COST):
     """Workspace bounds of a batch, as the host sizes them."""
     narrow = 1 if decode else max(16 // G, 1)
     wide = max(SPAN_ROWS // G, 1)
@@ -95,7 +100,8 @@ def make_layout(*, G, Hkv, num_seqs, num_tokens, max_context_len, max_query_len,
         if mp > 0:
             splits += min(mp - Hkv, tiles_of[st] * Hkv)
     return Layout(narrow, wide, part, tuple(waves), sum(tiles_of),
-                  tuple(max_pieces), splits, mpt, num_seqs * Hkv if cascade else 0, wide_nt)
+                  tuple(max_pieces), splits, mpt, num_seqs * Hkv if cascade else 0, wide_nt,
+                  tuple(part_cost))
 
 
 @dataclass
@@ -104,7 +110,7 @@ class Plan:
     t_first: list  # stream st holds tiles [t_first[st], t_first[st + 1])
     R: list
     B: list
-    pieces: list  # per stream: list of (tile, kvh, j)
+    pieces: list  # per stream: list of (tile, kvh, first block, blocks)
     splits: list  # (row0, ntok, kvh, k0, k1, stream)
     cas_recs: list  # (row, kvh, suf_k0, suf_k1, pre_k0, pre_k1, pre_pos)
     cas_prefix: list
@@ -198,29 +204,42 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
     for td in tiles:
         tp.append(tp[-1] + td.nb)
 
-    R, B, pieces = [], [], []
+    R, B, C, pieces = [], [], [], []
     for st in STREAMS:
         t_lo, t_hi = t_first[st], t_first[st + 1]
         b = tp[t_hi] - tp[t_lo]
+        c = 0 if lay.part_blocks > 0 else lay.part_cost[st]
+        bc = b + c * (t_hi - t_lo)
         r = lay.part_blocks
         if r <= 0:
-            r = max(cdiv(H * b, max(lay.waves[st], 1)), min_blocks)
-        K = cdiv(b, r)
+            r = max(cdiv(H * bc, max(lay.waves[st], 1)), min_blocks + c)
+        K = cdiv(bc, r)
         kmax = lay.max_pieces[st] // H
         if kmax == 0:
             K = 0
         elif K > kmax:
-            r = cdiv(b, kmax)
-            K = cdiv(b, r)
+            r = max(cdiv(bc, kmax), c + 1)
+            K = cdiv(bc, r)
         r = max(r, 1)
+
+        def position(x):
+            # the last tile whose cost prefix is <= x; its blocks start c units in
+            lo = max(t for t in range(t_lo, t_hi)
+                     if (tp[t] - tp[t_lo]) + c * (t - t_lo) <= x)
+            cp = (tp[lo] - tp[t_lo]) + c * (lo - t_lo)
+            return lo, max(0, x - cp - c)
+
         ps = []
         for v in range(K * H):
-            h = v % H
-            key = tp[t_lo] + (v // H) * r
-            lo = max(t for t in range(t_lo, t_hi) if tp[t] <= key)
-            ps.append((lo, h, key - tp[lo]))
+            h, k = v % H, v // H
+            t0, j0 = position(k * r)
+            t1, j1 = position((k + 1) * r) if k + 1 < K else (t_hi, 0)
+            nblk = (tp[t1] + j1) - (tp[t0] + j0)
+            assert nblk > 0, "empty piece"
+            ps.append((t0, h, j0, nblk))
         R.append(r)
         B.append(b)
+        C.append(c)
         pieces.append(ps)
 
     def stream_of(t):
@@ -228,8 +247,8 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
 
     def cut(t):
         st = stream_of(t)
-        b0 = tp[t] - tp[t_first[st]]
-        return b0 // R[st], (b0 + tiles[t].nb - 1) // R[st]
+        x0 = (tp[t] - tp[t_first[st]]) + C[st] * (t - t_first[st] + 1)
+        return x0 // R[st], (x0 + tiles[t].nb - 1) // R[st]
 
     splits = []
     for t, td in enumerate(tiles):
@@ -293,11 +312,12 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
 
     for st in STREAMS:
         NT = lay.wide_nt if st == STREAM_WIDE else 1
-        R, B = plan.R[st], plan.B[st]
         max_slots = 2 * lay.max_pieces[st]
         assert len(plan.pieces[st]) <= lay.max_pieces[st], "pieces past their region"
-        for v, (t, kvh, j) in enumerate(plan.pieces[st]):
-            left = min(R, B - (v // Hkv) * R)
+        # the pieces of each head's substream cover its B blocks once, in order
+        for h in range(Hkv):
+            assert sum(p[3] for p in plan.pieces[st][h::Hkv]) == plan.B[st]
+        for v, (t, kvh, j, left) in enumerate(plan.pieces[st]):
             td = plan.tiles[t]
             while left > 0:
                 assert plan.t_first[st] <= t < plan.t_first[st + 1], "piece left its stream"
@@ -389,7 +409,8 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
             "splits": len(plan.splits), "cascade_records": len(plan.cas_recs)}
 
 
-def replay_workload(wl, *, waves, groups=None, partition_size=None, hybrid=None):
+def replay_workload(wl, *, waves, groups=None, partition_size=None, hybrid=None,
+                    part_cost=PART_COST):
     """Build and check the plan of a workload (``paged_kv_cache_213_amd.
     workloads``); returns (plan, layout, counts)."""
     G = wl.num_q_heads // wl.num_kv_heads
@@ -400,7 +421,7 @@ def replay_workload(wl, *, waves, groups=None, partition_size=None, hybrid=None)
                       max_context_len=wl.max_context_len,
                       max_query_len=wl.max_query_len if use_hybrid else 1,
                       decode=not use_hybrid, partition_size=P, cascade=groups is not None,
-                      waves=waves, f32=wl.kv_dtype == "f32")
+                      waves=waves, f32=wl.kv_dtype == "f32", part_cost=part_cost)
     plan = build_plan(lay, Hkv=wl.num_kv_heads, context_lens=wl.context_lens, qsl=qsl,
                       num_tokens=wl.num_tokens, max_context_len=wl.max_context_len, groups=groups)
     members = [int(i) for g in groups[0] for i in g] if groups is not None else []

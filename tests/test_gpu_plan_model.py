@@ -56,7 +56,7 @@ def _compare(wl, groups, P):
                          max_query_len=wl.max_query_len if hybrid else 1, decode=not hybrid,
                          partition_size=P, cascade=groups is not None,
                          waves=tuple(info.waves), wide_nt=info.wide_row_tiles,
-                         f32=wl.kv_dtype == "f32")
+                         f32=wl.kv_dtype == "f32", part_cost=tuple(info.part_cost))
     qsl = np.asarray(wl.query_start_loc) if hybrid else None
     plan = PM.build_plan(lay, Hkv=wl.num_kv_heads, context_lens=wl.context_lens, qsl=qsl,
                          num_tokens=wl.num_tokens, max_context_len=wl.max_context_len,
@@ -76,7 +76,7 @@ def _compare(wl, groups, P):
         assert (B, R, V) == (plan.B[st], plan.R[st], len(plan.pieces[st])), f"stream {st}"
         if V:
             ps = _ints(buf, info.off_pieces[st], V, 16)
-            assert np.array_equal(ps[:, :3], np.array(plan.pieces[st], np.int32)), \
+            assert np.array_equal(ps[:, :4], np.array(plan.pieces[st], np.int32)), \
                 f"piece records of stream {st} differ"
             assert np.array_equal(ps[:, 4:13], tiles[ps[:, 0], :9]), "piece tile copies differ"
     assert nsplit == len(plan.splits)

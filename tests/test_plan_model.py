@@ -65,6 +65,35 @@ def test_random_hybrid_batches(seed):
     PM.replay_workload(wl, waves=(512, 1024, 1024))
 
 
+@pytest.mark.parametrize("cost", [(0, 0, 0), (1, 3, 2), (12, 7, 40)])
+@pytest.mark.parametrize("seed", range(6))
+def test_part_costs(seed, cost):
+    """Pieces cut at equal blocks plus a cost per segment started: whatever
+    the costs, each head's pieces cover its blocks once, no piece is empty,
+    and the splits and merge reads stay consistent."""
+    wl, groups = _random_sharing_batch(seed)
+    for waves in ((512, 1024, 1024), (37, 13, 29)):
+        plan, _, _ = PM.replay_workload(wl, waves=waves, groups=groups, part_cost=cost)
+        for st in (0, 1, 2):
+            assert all(p[3] > 0 for p in plan.pieces[st])
+
+
+def test_part_cost_moves_blocks_off_pieces_that_start_many_segments():
+    """With a cost per segment, a piece that starts many short segments
+    holds fewer blocks than one inside a long segment."""
+    wl = W.make_config("c2")
+    plan, _, _ = PM.replay_workload(wl, waves=(512, 1024, 1024), part_cost=(0, 8, 0))
+    nb = {}
+    for (t, kvh, j, n) in plan.pieces[1]:
+        nb.setdefault(kvh, []).append(n)
+    spread = max(max(v) - min(v) for v in nb.values())
+    plan0, _, _ = PM.replay_workload(wl, waves=(512, 1024, 1024), part_cost=(0, 0, 0))
+    spread0 = max(max(p[3] for p in plan0.pieces[1][h::wl.num_kv_heads]) -
+                  min(p[3] for p in plan0.pieces[1][h::wl.num_kv_heads][:-1])
+                  for h in range(wl.num_kv_heads))
+    assert spread0 == 0 and spread > 0
+
+
 def test_model_catches_a_planted_slot_slip():
     """The replay is able to fail: a plan whose merge reads the head slot
     of a segment's first piece (in place of its tail slot) is rejected."""
@@ -119,6 +148,7 @@ def test_model_layout_equals_the_librarys(name, P, grouped):
     assert lay.max_tiles == info.max_tiles and lay.max_splits == info.max_splits
     assert lay.max_pieces == tuple(info.max_pieces)
     assert lay.max_cas_recs == info.max_cas_recs
+    assert lay.part_cost == tuple(info.part_cost)
     mq = wl.max_query_len if hybrid else 1
     assert info.total <= pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens,
                                             wl.max_context_len, mq)
