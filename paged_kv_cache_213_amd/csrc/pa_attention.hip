@@ -238,6 +238,18 @@ __device__ __forceinline__ f32x4 qk_fp8(const uint4 (&k)[D / 64], const uint4* q
 template <int D>
 struct Tile<KV_FP8Q, D> : Tile<KV_FP8, D> {
     __device__ __forceinline__ f32x4 qk(const uint4* q) const { return qk_fp8<D>(this->k, q); }
+    // O += V^T P on the fp8 matrix cores, one v_mfma_f32_16x16x32_fp8_fp8
+    // per 16 output dims: the 32-long contraction holds the block's 16 keys
+    // twice, once against P's e4m3 term and once against what that term's
+    // rounding left (p8 from p_fp8_two_term), so the e4m3 V bytes are used
+    // as stored and P keeps about 2^-8 of its value.
+    __device__ __forceinline__ void pv8(uint64_t p8, f32x4* o) const {
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+            const uint64_t a = (uint64_t)this->v[dt] | ((uint64_t)this->v[dt] << 32);
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a, (long)p8, o[dt], 0, 0, 0);
+        }
+    }
 };
 
 // Row q (bf16) -> the two e4m3 terms of qk_fp8 for this lane's dims 16g +
@@ -299,6 +311,26 @@ __device__ __forceinline__ float quantize_q_fp8(const uint16_t* qrow, bool ok, i
     out[2] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     out[3] = make_uint4(lo[4], lo[5], lo[6], lo[7]);
     return amax * (1.f / 448.f);
+}
+
+// Four probabilities (already scaled into the e4m3 range) -> the B operand
+// of Tile<KV_FP8Q>::pv8: bytes 0-3 their e4m3 roundings, bytes 4-7 the
+// e4m3 roundings of the remainders, so hi + lo matches each value to about
+// 2^-8 of it (remainders below the e4m3 normal range keep an absolute error
+// under 2^-10).
+__device__ __forceinline__ uint64_t p_fp8_two_term(const float (&p)[4], float s) {
+    float u[4], r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = fminf(p[e] * s, 448.f);
+    const uint32_t h = pk_fp8(u[0], u[1], u[2], u[3]);
+    const f32x2_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, false);
+    const f32x2_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, true);
+    r[0] = u[0] - h01.x;
+    r[1] = u[1] - h01.y;
+    r[2] = u[2] - h23.x;
+    r[3] = u[3] - h23.y;
+    const uint32_t l = pk_fp8(r[0], r[1], r[2], r[3]);
+    return (uint64_t)h | ((uint64_t)l << 32);
 }
 
 // ---- plan ------------------------------------------------------------------
@@ -763,6 +795,10 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     constexpr float kLazy = 8.f;
     f32x4 o[NR][D / 16];
     float m_use[NR], thr[NR], l_run[NR];
+    // fp8 P.V: o holds the output times osc, a power of two that keeps
+    // p * v_scale * osc in the e4m3 range for p <= 2^kLazy; it follows the
+    // blocks' V scales, and o is rescaled when it moves
+    float osc[NR];
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
 #pragma unroll
@@ -770,6 +806,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         m_use[r] = 0.f;
         thr[r] = -INFINITY;
         l_run[r] = 0.f;
+        osc[r] = 1.f;
     }
     // blocks ending at or before the tile's first query position are visible
     // to every row and lie inside the context: no masks
@@ -849,7 +886,9 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                     for (int dt = 0; dt < D / 16; ++dt) o[r][dt] *= alpha;
                 }
             }
-            typename std::conditional<kv == KV_F32, float[NR][4], s16x4[NR]>::type pk;
+            typename std::conditional<kv == KV_F32, float[NR][4],
+                                      typename std::conditional<kv == KV_FP8Q, uint64_t[NR],
+                                                                s16x4[NR]>::type>::type pk;
 #pragma unroll
             for (int r = 0; r < NR; ++r) {
                 float p[4];
@@ -859,6 +898,21 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
                 if constexpr (kv == KV_F32) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) pk[r][e] = p[e];
+                } else if constexpr (kv == KV_FP8Q) {
+                    // p <= 2^kLazy, so p * v_scale * osc <= 384 while
+                    // v_scale * osc stays in [1/2, 3/2]; a block whose scale
+                    // leaves that range moves osc to the nearest power of two
+                    // of 1 / v_scale (wave-uniform)
+                    float xs = vsc * osc[r];
+                    if (vsc > 0.f && (xs > 1.5f || xs < 0.5f)) {
+                        const float nsc = ldexpf(1.f, -(int)rintf(__log2f(vsc)));
+                        const float ratio = nsc / osc[r];
+#pragma unroll
+                        for (int dt = 0; dt < D / 16; ++dt) o[r][dt] *= ratio;
+                        osc[r] = nsc;
+                        xs = vsc * nsc;
+                    }
+                    pk[r] = p_fp8_two_term(p, xs);
                 } else {
                     const uint32_t lo = pack_bf16x2(p[0] * vsc, p[1] * vsc);
                     const uint32_t hi = pack_bf16x2(p[2] * vsc, p[3] * vsc);
@@ -868,7 +922,12 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             // zero V slots past the context (NaN there must not reach P.V)
             if (!full) cur.mask_v(L - t0);
 #pragma unroll
-            for (int r = 0; r < NR; ++r) cur.pv(pk[r], o[r]);
+            for (int r = 0; r < NR; ++r) {
+                if constexpr (kv == KV_FP8Q)
+                    cur.pv8(pk[r], o[r]);
+                else
+                    cur.pv(pk[r], o[r]);
+            }
         };
         auto consume = [&](T& cur, int i) { consume_tile(cur, i); };
         auto fetch = [&](T& dst, int i) {
@@ -912,7 +971,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     for (int r = 0; r < NR; ++r) {
         // row totals: l summed over the four lane groups that share a row
         const float l = row_sum(l_run[r]);
-        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        const float inv = l > 0.f ? (1.0f / l) * (1.0f / osc[r]) : 0.f;
         if (!row_ok[r]) continue;
         if (whole && td.flags != 0) {
             // a whole cascade part: normalized output and lse per row

@@ -1,15 +1,19 @@
-"""fp8 cache with S = K q^T on the fp8 matrix cores (pa_shape.fp8_qk): the
-query is quantized per (token, head) into two e4m3 terms, the value and its
-residual, and the scores come from two fp8 MFMAs ("Inference engines",
-recent developments: the attention matmuls themselves in FP8). The oracle
-is the same exact definition as for every other test; the tolerance is the
-fp8 one.
+"""fp8 cache with both attention products on the fp8 matrix cores
+(pa_shape.fp8_qk; "Inference engines", recent developments: the QK and
+score-V matmuls themselves in FP8). S = K q^T: the query is quantized per
+(token, head) into two e4m3 terms, the value and its residual, and the
+scores come from two fp8 MFMAs. O += V^T P: the probabilities, scaled by
+the block's V scale and a power-of-two output scale, become two e4m3 terms
+in one 32-long contraction against the stored V bytes. The oracle is the
+same exact definition as for every other test; the tolerance is the fp8
+one. (Chunked-prefill spans run on the span kernel, which widens the fp8
+cache to bf16 in LDS.)
 
 One e4m3 term alone would not meet it: over short contexts its rounding of
-q (up to 2^-4 of a value) moves the softmax weights of a handful of keys
-by several percent. The short-context test below holds 2048 query rows
-over 2 to 8 keys; there a single-term q errs by up to about 0.1, the two
-terms by about 0.003."""
+q or p (up to 2^-4 of a value) moves the softmax weights of a handful of
+keys by several percent. The short-context test below holds 2048 query
+rows over 2 to 8 keys; there a single-term q errs by up to about 0.1, the
+two terms by about 0.003."""
 import numpy as np
 import pytest
 import torch
@@ -81,3 +85,29 @@ def test_query_scales_per_row():
     ref, _ = oracle.run_workload(wl, post)
     e = H.assert_parity(out_f64(out), ref, "fp8", "row scales")
     print(f"row scales fp8_qk: {e}", flush=True)
+
+
+def test_value_scales_across_blocks():
+    """V blocks whose magnitudes, and so their scales, differ by up to 2^10
+    along each context: P.V on the fp8 matrix cores keeps p * v_scale in
+    the e4m3 range by moving a power-of-two output scale as the block
+    scales change. (Blocks are only shrunk: an output mixing blocks 2^10
+    times larger than its own size loses the 2^-8 of those blocks'
+    weights that two e4m3 terms keep, which the fp8 tolerance, relative to
+    the output, does not allow for.)"""
+    lens = [33, 700, 1200, 9, 260]
+    wl = W.custom_workload(lens, num_q_heads=8, num_kv_heads=2, head_dim=128, q_dtype="bf16",
+                           kv_dtype="fp8", seed=23)
+    vals, _ = prepare(wl)
+    nb = vals.v_src.shape[0]
+    f = torch.tensor([2.0 ** -((b * 7) % 11) for b in range(nb)], dtype=torch.float32,
+                     device=vals.v_src.device)
+    vals.v_src = (vals.v_src * f.view(nb, 1, 1, 1)).contiguous()
+    vals.v_scale = (vals.v_scale * f.view(nb, 1)).contiguous()
+    pre = H.host_pre_append(wl, vals)
+    post = H.oracle_append(wl, pre)
+    t = dev_tensors(wl, vals, pre)
+    out, _ = gpu_step(wl, t, fp8_qk=True)
+    ref, _ = oracle.run_workload(wl, post)
+    e = H.assert_parity(out_f64(out), ref, "fp8", "value scales")
+    print(f"value scales fp8_qk: {e}", flush=True)
