@@ -104,13 +104,18 @@ typedef struct pa_shape {
     int32_t partition_size;     /* split-KV piece in tokens, 0 = balanced */
     int32_t cascade;            /* 1: plans may hold shared-prefix groups
                                    (pa_plan_cascade); reserves their room */
-    int32_t fp8_qk;             /* 1 (fp8 cache only): S = K q^T on the fp8
-                                   matrix cores, q quantized per (token, head)
-                                   into two e4m3 terms, value and residual
-                                   ("Inference engines", recent developments:
-                                   the QK matmul itself in FP8); results
-                                   within the fp8 tolerance, not bitwise
-                                   those of 0 */
+    int32_t fp8_qk;             /* 1 (fp8 cache only): both products of the
+                                   decode kernel on the fp8 matrix cores:
+                                   S = K q^T with q quantized per (token,
+                                   head) into two e4m3 terms, value and
+                                   residual, and O += V^T P with P (times the
+                                   block's V scale and a power-of-two output
+                                   scale) as two e4m3 terms against the
+                                   stored V bytes ("Inference engines",
+                                   recent developments: the QK and score-V
+                                   matmuls themselves in FP8); spans keep the
+                                   exact bf16 products; results within the
+                                   fp8 tolerance, not bitwise those of 0 */
 } pa_shape;
 
 /* Bytes of device workspace the attention calls need for this batch (work
@@ -320,7 +325,8 @@ const char* pa_status_string(int status);
  * and pa_plan_cascade; 201 added pa_plan_tree; 202 added pa_shape.fp8_qk;
  * 203 added pa_workspace_layout; 204 added pa_paged_attn_hybrid_noalloc;
  * 205 gave pa_layout_info a third block stream; 206 gave piece records
- * their block counts and pa_layout_info the per-stream part costs. */
+ * their block counts and pa_layout_info the per-stream part costs; 207
+ * runs P.V on the fp8 matrix cores too when fp8_qk is set. */
 int pa_version(void);
 
 #ifdef __cplusplus

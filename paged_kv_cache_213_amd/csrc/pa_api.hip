@@ -641,6 +641,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 206; }
+int pa_version(void) { return 207; }
 
 }  // extern "C"
