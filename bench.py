@@ -270,6 +270,10 @@ def main():
     ap.add_argument("--cascade", choices=("auto", "on", "off"), default="auto",
                     help="read shared prefixes once per group (auto: when the workload's "
                          "sequences share prefix blocks)")
+    ap.add_argument("--append", choices=("fused", "separate"), default="fused",
+                    help="decode batches: append the step's K/V rows in the attention pass "
+                         "(fused) or with their own launch before it (separate); chunked-"
+                         "prefill batches always use the separate launch")
     ap.add_argument("--fp8-qk", action="store_true",
                     help="fp8 cache: S = K q^T on the fp8 matrix cores (two-term fp8 q)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -341,6 +345,9 @@ def main():
                                 wl.max_query_len)
     ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
     mq = 1 if wl.is_decode else wl.max_query_len
+    fused = args.append == "fused" and wl.is_decode
+    app_kw = dict(k_new=vals.k_new, v_new=vals.v_new) if fused else {}
+
     def model_step(stream):
         if groups is not None:
             pa.plan_cascade(shape, cl, ws, groups, query_start_loc=qsl,
@@ -350,11 +357,13 @@ def main():
             pa.plan(shape, cl, ws, query_start_loc=qsl, num_q_tokens=wl.num_tokens,
                     max_query_len=mq, max_context_len=wl.max_context_len, stream=stream)
         for L_ in range(layers):
-            pa.kv_append(kc[L_], vc[L_], vals.k_new, vals.v_new, slots, k_scale=k_scale,
-                         v_scale=v_scale, stream=stream)
+            if not fused:
+                pa.kv_append(kc[L_], vc[L_], vals.k_new, vals.v_new, slots, k_scale=k_scale,
+                             v_scale=v_scale, stream=stream)
             pa.run(shape, qs[L_], kc[L_], vc[L_], bt, cl, wl.scale, ws, query_start_loc=qsl,
                    max_query_len=mq, max_context_len=wl.max_context_len, out=outs[L_],
-                   lse=lse, stream=stream, passes="partial", k_scale=k_scale, v_scale=v_scale)
+                   lse=lse, stream=stream, passes="partial", k_scale=k_scale, v_scale=v_scale,
+                   **app_kw)
             pa.run(shape, qs[L_], kc[L_], vc[L_], bt, cl, wl.scale, ws, query_start_loc=qsl,
                    max_query_len=mq, max_context_len=wl.max_context_len, out=outs[L_],
                    lse=lse, stream=stream, passes="merge")
@@ -439,7 +448,8 @@ def main():
             for L_ in range(layers):
                 pa.run(shape, qs[L_], kc[L_], vc[L_], bt, cl, wl.scale, ws, query_start_loc=qsl,
                        max_query_len=mq, max_context_len=wl.max_context_len, out=outs[L_],
-                       lse=lse, stream=s, passes="partial", k_scale=k_scale, v_scale=v_scale)
+                       lse=lse, stream=s, passes="partial", k_scale=k_scale, v_scale=v_scale,
+                       **app_kw)
             e1.record(s)
             s.synchronize()
             att_ms.append(e0.elapsed_time(e1) / layers)
@@ -461,7 +471,8 @@ def main():
                 per.append(e0.elapsed_time(e1) * 1e3 / layers)
         return round(float(np.mean(per)), 2)
 
-    append_us = back_to_back_us(lambda L_: pa.kv_append(
+    # (a fused append is inside the attention pass's time)
+    append_us = None if fused else back_to_back_us(lambda L_: pa.kv_append(
         kc[L_], vc[L_], vals.k_new, vals.v_new, slots, k_scale=k_scale, v_scale=v_scale,
         stream=s))
     merge_us = back_to_back_us(lambda L_: pa.run(
@@ -513,6 +524,7 @@ def main():
             "graph": graph is not None,
             "cascade": use_cascade,
             "fp8_qk": bool(args.fp8_qk),
+            "append": "fused into the attention pass" if fused else "separate launch",
             "kv_bytes_read_per_layer": read_bytes,
             "kv_bytes_unique_per_layer": wl.kv_bytes_unique() if wl.shared_groups else kv_bytes,
             "seed": wl.seed,
@@ -528,8 +540,10 @@ def main():
                             "WRITE_SIZE, profiles/); null if not recorded for the current "
                             "attention source",
             "kernel": "attention pass (attention_span for chunked-prefill spans, then "
-                      "attention_narrow, one launch each per layer); HIP events around the "
-                      "back-to-back pass-1 launches of all layers, divided by the layers",
+                      "attention_narrow, one launch each per layer; decode batches append "
+                      "the step's K/V rows in it unless --append separate); HIP events "
+                      "around the back-to-back pass-1 launches of all layers, divided by "
+                      "the layers",
             "launch_us_mean": round(att_mean * 1e3, 2),
             "launch_us_min_max": [round(float(att_ms.min()) * 1e3, 2),
                                   round(float(att_ms.max()) * 1e3, 2)],

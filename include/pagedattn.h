@@ -254,6 +254,40 @@ int pa_paged_attn_merge(const pa_shape* shape, void* out, float* lse, const int3
                         int max_query_len, int max_context_len, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* Decode with this step's K/V rows appended in the same attention pass.
+ * Equivalent to pa_kv_append of k_new / v_new ([num_seqs][Hkv][D] in
+ * q_dtype, 16-byte aligned) at slot block_tables[i][(L_i - 1) / 16] * 16 +
+ * (L_i - 1) % 16 with L_i = context_lens[i] (the context including the new
+ * token; the slot of the new position through the block table, "03 --
+ * Engines Papers", section 2), followed by the attention of the same call
+ * without append: the cache bytes written and out / lse are bit for bit
+ * those. The wave that reads a sequence's last block for a KV head puts
+ * the new token into the tile it loaded and writes it to the cache, so the
+ * step needs no append launch (one launch fewer per layer). Needs a decode
+ * plan (query_start_loc NULL; cascade plans allowed); sequences with L_i = 0
+ * append nothing; contexts past max_context_len are not supported (as for
+ * the attention). run_append: both passes with a plan made earlier;
+ * partial_append: the first pass only (pa_paged_attn_merge completes it);
+ * decode_append: plan and both passes. */
+int pa_paged_attn_run_append(const pa_shape* shape, void* out, float* lse, const void* q,
+                             const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int max_context_len, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream);
+int pa_paged_attn_partial_append(const pa_shape* shape, void* out, float* lse, const void* q,
+                                 const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int num_seqs, int max_context_len, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+int pa_paged_attn_decode_append(const pa_shape* shape, void* out, float* lse, const void* q,
+                                const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int num_seqs, int max_context_len, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 /* Append this step's new K/V rows into their slots before attention runs
  * on the same stream. k_new, v_new: [num_tokens][Hkv][D] in q_dtype.
  * slot_mapping: [num_tokens] int32, slot = physical_block * 16 + offset
@@ -326,7 +360,9 @@ const char* pa_status_string(int status);
  * 203 added pa_workspace_layout; 204 added pa_paged_attn_hybrid_noalloc;
  * 205 gave pa_layout_info a third block stream; 206 gave piece records
  * their block counts and pa_layout_info the per-stream part costs; 207
- * runs P.V on the fp8 matrix cores too when fp8_qk is set. */
+ * runs P.V on the fp8 matrix cores too when fp8_qk is set; 208 added
+ * pa_paged_attn_run_append, pa_paged_attn_partial_append and
+ * pa_paged_attn_decode_append. */
 int pa_version(void);
 
 #ifdef __cplusplus

@@ -96,6 +96,11 @@ def load_library(path: str = LIB_PATH):
     lib.pa_workspace_bytes.argtypes = [S, I, I, I, I]
     lib.pa_paged_attn_decode.restype = I
     lib.pa_paged_attn_decode.argtypes = [S, P, P, P, P, P, P, P, P, P, I, I, F, P, Z, P]
+    for name in ("pa_paged_attn_run_append", "pa_paged_attn_partial_append",
+                 "pa_paged_attn_decode_append"):
+        fn = getattr(lib, name)
+        fn.restype = I
+        fn.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, I, I, F, P, Z, P]
     lib.pa_paged_attn_hybrid.restype = I
     lib.pa_paged_attn_hybrid.argtypes = [S, P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P, Z, P]
     lib.pa_paged_attn_hybrid_noalloc.restype = I
@@ -203,12 +208,15 @@ def _workspace(nbytes: int, device, workspace):
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, *,
            max_context_len: int, k_scale=None, v_scale=None, partition_size: int = 0,
-           out=None, lse=None, workspace=None, stream=None, fp8_qk: bool = False):
+           out=None, lse=None, workspace=None, stream=None, fp8_qk: bool = False,
+           k_new=None, v_new=None):
     """Paged attention for one query token per sequence.
 
     q [S][Hq][D]; block_tables [S][max_blocks] int32; context_lens [S] int32
     (including the new token). Returns out [S][Hq][D] in q's dtype (and
-    fills ``lse`` [S][Hq] float32 when given)."""
+    fills ``lse`` [S][Hq] float32 when given). With k_new / v_new
+    ([S][Hkv][D], q's dtype) the step's rows are appended at each
+    sequence's last position in the same pass (pa_paged_attn_decode_append)."""
     import torch
     lib = load_library()
     shape = make_shape(q, k_cache, block_tables, partition_size, fp8_qk=fp8_qk)
@@ -217,6 +225,14 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, *,
         out = torch.empty_like(q)
     nbytes = workspace_bytes(shape, S, S, max_context_len, 1)
     ws = _workspace(nbytes, q.device, workspace)
+    if k_new is not None or v_new is not None:
+        rc = lib.pa_paged_attn_decode_append(
+            ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new),
+            _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+            _ptr(context_lens), S, int(max_context_len), float(scale), _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(stream))
+        _check(rc, "pa_paged_attn_decode_append")
+        return out
     rc = lib.pa_paged_attn_decode(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q),
                                   _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
                                   _ptr(block_tables), _ptr(context_lens), S,
@@ -381,9 +397,12 @@ def plan_cascade(shape: PaShape, context_lens, workspace, groups: PrefixGroups, 
 
 def run(shape: PaShape, q, k_cache, v_cache, block_tables, context_lens, scale: float, workspace,
         *, query_start_loc=None, max_query_len: int, max_context_len: int, k_scale=None,
-        v_scale=None, out=None, lse=None, stream=None, passes: str = "both"):
+        v_scale=None, out=None, lse=None, stream=None, passes: str = "both", k_new=None,
+        v_new=None):
     """Attention with a plan enqueued earlier by plan(): the attention pass
-    and the merge pass ("both"), or only "partial" (pass 1) or "merge"."""
+    and the merge pass ("both"), or only "partial" (pass 1) or "merge".
+    With k_new / v_new (decode plans only) the attention pass appends the
+    step's rows first (pa_paged_attn_run_append / _partial_append)."""
     import torch
     lib = load_library()
     T = q.shape[0]
@@ -396,6 +415,17 @@ def run(shape: PaShape, q, k_cache, v_cache, block_tables, context_lens, scale: 
                                      _ptr(query_start_loc), S, T, int(max_query_len),
                                      int(max_context_len), _ptr(workspace), wsb, _stream(stream))
         _check(rc, "pa_paged_attn_merge")
+        return out
+    if k_new is not None or v_new is not None:
+        if query_start_loc is not None:
+            raise ValueError("the fused append goes with decode plans only")
+        fn = {"both": lib.pa_paged_attn_run_append,
+              "partial": lib.pa_paged_attn_partial_append}[passes]
+        rc = fn(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new),
+                _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+                _ptr(context_lens), S, int(max_context_len), float(scale), _ptr(workspace),
+                wsb, _stream(stream))
+        _check(rc, "pa_paged_attn_" + ("run" if passes == "both" else passes) + "_append")
         return out
     fn = {"both": lib.pa_paged_attn_run, "partial": lib.pa_paged_attn_partial}[passes]
     rc = fn(ctypes.byref(shape), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache),

@@ -288,7 +288,8 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
              const void* v_cache, const float* k_scale, const float* v_scale,
              const int32_t* block_tables, const int32_t* context_lens, const int32_t* qsl,
              int num_seqs, int num_tokens, int max_query_len, int max_context_len, float scale,
-             void* workspace, size_t workspace_bytes, void* stream, int passes) {
+             void* workspace, size_t workspace_bytes, void* stream, int passes,
+             const void* k_new = nullptr, const void* v_new = nullptr) {
     Layout l;
     int rc = check_batch(s, context_lens, qsl, num_seqs, num_tokens, max_query_len,
                          max_context_len, workspace, workspace_bytes, &l);
@@ -297,6 +298,9 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
     if (passes & PASS_ATTENTION) {
         rc = check_io(s, out, q, k_cache, v_cache, k_scale, v_scale, block_tables);
         if (rc != PA_OK) return rc;
+        if ((k_new || v_new) &&
+            (!k_new || !v_new || qsl || !aligned16(k_new) || !aligned16(v_new)))
+            return PA_EINVAL;  // the append goes with decode plans only
     } else if (!out || !aligned16(out)) {
         return PA_EINVAL;
     }
@@ -325,6 +329,7 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
         aa.scale_log2 = scale * 1.44269504088896340736f;
         aa.num_seqs = num_seqs;
         aa.tree = (const uint64_t*)(ws + l.off_tree);
+
         if (l.cascade) {
             aa.cas_prefix = (const int32_t*)(ws + l.off_cas_seq);
             aa.group_members = (const int32_t*)(ws + l.off_cas_seq) + 4 * (size_t)num_seqs;
@@ -340,6 +345,10 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
             aa.pieces = (const pa::PieceStart*)(ws + l.off_pieces[st]);
             aa.part_lse = (float*)(ws + l.off_lse[st]);
             aa.part_o = (float*)(ws + l.off_o[st]);
+            // the new rows go with the stream that holds the decodes' last
+            // blocks (group tiles hold shared prefixes only)
+            aa.k_new = st == pa::STREAM_NARROW ? k_new : nullptr;
+            aa.v_new = st == pa::STREAM_NARROW ? v_new : nullptr;
             if (pa::launch_attention(kernel_kind(s), s->head_dim, aa, l.max_pieces[st], hs) !=
                 hipSuccess)
                 return PA_EHIP;
@@ -472,6 +481,48 @@ int pa_paged_attn_decode(const pa_shape* shape, void* out, float* lse, const voi
     return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                     context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len, scale,
                     workspace, workspace_bytes, stream, PASS_BOTH);
+}
+
+int pa_paged_attn_run_append(const pa_shape* shape, void* out, float* lse, const void* q,
+                             const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             int num_seqs, int max_context_len, float scale, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                    context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len, scale,
+                    workspace, workspace_bytes, stream, PASS_BOTH, k_new, v_new);
+}
+
+int pa_paged_attn_partial_append(const pa_shape* shape, void* out, float* lse, const void* q,
+                                 const void* k_new, const void* v_new, void* k_cache,
+                                 void* v_cache, const float* k_scale, const float* v_scale,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int num_seqs, int max_context_len, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                    context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len, scale,
+                    workspace, workspace_bytes, stream, PASS_ATTENTION, k_new, v_new);
+}
+
+int pa_paged_attn_decode_append(const pa_shape* shape, void* out, float* lse, const void* q,
+                                const void* k_new, const void* v_new, void* k_cache,
+                                void* v_cache, const float* k_scale, const float* v_scale,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int num_seqs, int max_context_len, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (check_shape(shape) != PA_OK) return check_shape(shape);
+    if (num_seqs > 0) {
+        int rc0 = check_io(shape, out, q, k_cache, v_cache, k_scale, v_scale, block_tables);
+        if (rc0 != PA_OK) return rc0;
+        if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return PA_EINVAL;
+    }
+    int rc = plan_impl(shape, context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len,
+                       Groups{}, workspace, workspace_bytes, stream);
+    if (rc != PA_OK) return rc;
+    return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                    context_lens, nullptr, num_seqs, num_seqs, 1, max_context_len, scale,
+                    workspace, workspace_bytes, stream, PASS_BOTH, k_new, v_new);
 }
 
 int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const void* q,
@@ -641,6 +692,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 207; }
+int pa_version(void) { return 208; }
 
 }  // extern "C"

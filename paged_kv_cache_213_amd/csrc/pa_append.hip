@@ -9,28 +9,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pa_device.h"
 #include "pa_internal.h"
 
 namespace pa {
 namespace {
 
-// fp32 -> OCP e4m3fn by bit manipulation: round to nearest, ties to even;
-// magnitudes at or above 448 saturate to 448 (0x7E); NaN -> 0x7F.
-__device__ __forceinline__ uint32_t encode_e4m3fn(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return 0x7fu;            // NaN
-    if (a >= 0x43e00000u) return sign | 0x7eu;    // >= 448 (and inf)
-    if (a >= 0x3c800000u) {                       // >= 2^-6: normal in e4m3
-        // keep 3 of 23 mantissa bits, rounding the dropped 20 to even
-        uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
-        return sign | (r - (120u << 3));          // rebias exponent 127 -> 7
-    }
-    // subnormal grid: multiples of 2^-9; the result 8 is 2^-6, code 0x08
-    const float q = __uint_as_float(a) * 512.0f;
-    return sign | (uint32_t)__builtin_rintf(q);
-}
+using dev::encode_e4m3fn;
+
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float((uint32_t)b << 16);

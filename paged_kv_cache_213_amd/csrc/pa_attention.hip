@@ -252,6 +252,38 @@ struct Tile<KV_FP8Q, D> : Tile<KV_FP8, D> {
     }
 };
 
+// Decode with this step's tokens appended in the same pass: the wave that
+// reads a sequence's last block for KV head h puts the new token's K row and
+// V column (key o = (L - 1) % 16 of that block) into the tile it loaded, in
+// place of what the cache held there, and writes them to the cache as the
+// append does (an fp8 cache gets e4m3fn(fp32(x) / scale) of the block).
+// NewRow holds a lane's share of the new row as given: dims lane + 64 m.
+template <int kv, int D>
+struct NewRow {
+    using Src = typename std::conditional<kv == KV_F32, float, uint16_t>::type;
+    static constexpr int kPer = (D + 63) / 64;
+    Src k[kPer], v[kPer];
+    __device__ __forceinline__ void load(const void* kn, const void* vn, int lane) {
+#pragma unroll
+        for (int m = 0; m < kPer; ++m) {
+            const int d = min(lane + 64 * m, D - 1);
+            k[m] = ((const Src*)kn)[d];
+            v[m] = ((const Src*)vn)[d];
+        }
+    }
+};
+
+// Replace 16-bit element e (0..3) of four packed in a uint2.
+__device__ __forceinline__ uint2 put16(uint2 w, int e, uint16_t x) {
+    const uint32_t sh = 16u * (e & 1);
+    const uint32_t m = 0xffffu << sh;
+    if (e < 2)
+        w.x = (w.x & ~m) | ((uint32_t)x << sh);
+    else
+        w.y = (w.y & ~m) | ((uint32_t)x << sh);
+    return w;
+}
+
 // Row q (bf16) -> the two e4m3 terms of qk_fp8 for this lane's dims 16g +
 // [0, 16) and, for D = 128, 64 + 16g + [0, 16); returns the row's scale sq
 // (amax / 448; every lane of the row gets the same one). Rows of zeros get
@@ -696,6 +728,107 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 #define PA_GROUP_L2 0
 #endif
 
+// New keys staged in LDS (the workgroup is one wave) in the cache's
+// encoding: each lane encodes its share of the row, and the lanes that hold
+// key o of the tile read their elements back from the staged row. The
+// cache write of a new key is a partial-line store (its V column is one
+// element in each 32-byte row of the block), and on gfx9 a wave's later
+// loads wait for its earlier stores: written where the wave goes on to read
+// blocks, it would hold the next block's wait until the line has been
+// filled and written. The attention pass never reads a new key from the
+// cache (it takes it from the tile), so the writes wait for the end of the
+// wave's work, where nothing waits for them. A wave that stages more than
+// kMax keys writes them out early.
+template <int kv, int D>
+struct NewStage {
+    using E = typename std::conditional<kv == KV_F32, float,
+                                        typename std::conditional<kv == KV_BF16, uint16_t,
+                                                                  uint8_t>::type>::type;
+    static constexpr int kMax = 16;
+    E* k;         // [kMax][D]: K rows in the cache's encoding
+    E* v;         // [kMax][D]: V columns
+    int64_t* bh;  // [kMax] block-head
+    int* o;       // [kMax] key in the block
+    int count = 0;
+
+    __device__ __forceinline__ static E enc(typename NewRow<kv, D>::Src x, float scale) {
+        if constexpr (kv == KV_F32 || kv == KV_BF16)
+            return x;
+        else
+            return (E)encode_e4m3fn(__fdiv_rn(__uint_as_float((uint32_t)x << 16), scale));
+    }
+
+    // Stage the new row nr (key o of block-head blk_head; ks, vs: the
+    // block's fp8 scales) and put it into tile cur.
+    __device__ __forceinline__ void add(const AttnArgs& a, Tile<kv, D>& cur,
+                                        const NewRow<kv, D>& nr, const int key,
+                                        const int64_t blk_head, const float ks, const float vs,
+                                        const int lane) {
+        if (count == kMax) flush(a, lane);
+        E* kr = k + count * D;
+        E* vr = v + count * D;
+#pragma unroll
+        for (int m = 0; m < NewRow<kv, D>::kPer; ++m) {
+            const int d = lane + 64 * m;
+            if (d < D) {
+                kr[d] = enc(nr.k[m], ks);
+                vr[d] = enc(nr.v[m], vs);
+            }
+        }
+        if (lane == 0) {
+            bh[count] = blk_head;
+            o[count] = key;
+        }
+        ++count;
+        const int t = lane & 15, g = lane >> 4, e = key & 3;
+        if (t == key) {
+            if constexpr (kv == KV_F32) {
+#pragma unroll
+                for (int j = 0; j < D / 16; ++j) cur.k[j] = *(const float4*)(kr + 16 * j + 4 * g);
+            } else if constexpr (kv == KV_BF16) {
+#pragma unroll
+                for (int j = 0; j < D / 32; ++j) cur.k[j] = *(const uint4*)(kr + 32 * j + 8 * g);
+            } else {
+#pragma unroll
+                for (int j = 0; j < D / 64; ++j) cur.k[j] = *(const uint4*)(kr + 64 * j + 16 * g);
+            }
+        }
+        if (g == (key >> 2)) {
+#pragma unroll
+            for (int dt = 0; dt < D / 16; ++dt) {
+                const E x = vr[16 * dt + t];
+                if constexpr (kv == KV_F32) {
+                    if (e == 0) cur.v[dt].x = x;
+                    if (e == 1) cur.v[dt].y = x;
+                    if (e == 2) cur.v[dt].z = x;
+                    if (e == 3) cur.v[dt].w = x;
+                } else if constexpr (kv == KV_BF16) {
+                    cur.v[dt] = put16(cur.v[dt], e, x);
+                } else {
+                    cur.v[dt] = (cur.v[dt] & ~(0xffu << (8 * e))) | ((uint32_t)x << (8 * e));
+                }
+            }
+        }
+    }
+
+    // Write the staged keys to the cache: K rows whole, V columns element
+    // by element.
+    __device__ __forceinline__ void flush(const AttnArgs& a, const int lane) {
+        for (int n = 0; n < count; ++n) {
+            const int64_t b = bh[n];
+            const int key = o[n];
+            E* kd = (E*)a.k_cache + (b * 16 + key) * D;
+            E* vd = (E*)a.v_cache + b * D * 16 + key;
+#pragma unroll
+            for (int d = lane; d < D; d += 64) {
+                kd[d] = k[n * D + d];
+                vd[d * 16] = v[n * D + d];
+            }
+        }
+        count = 0;
+    }
+};
+
 // Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
 // each block through the block table, S = K q^T on the matrix cores, online
 // softmax in registers, O += V^T P, for one 16-row tile of query rows (the
@@ -705,7 +838,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 // pass.
 template <int kv, int D, bool kStreamLoads>
 __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td, const int kvh,
-                                            const int j, const int take, const int piece) {
+                                            const int j, const int take, const int piece,
+                                            NewStage<kv, D>& stage) {
     using T = Tile<kv, D>;
     constexpr int NT = 1, NR = 1;  // row tiles of a slot, and holding rows
     constexpr bool kFp8Cache = kv == KV_FP8 || kv == KV_FP8Q;
@@ -719,6 +853,11 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     const int seq = td.seq;
     const int L = td.L, qs = td.qs, nspan = td.nspan;
     const int nrows = td.ntok * G;
+    // decode with append: the segment that holds its sequence's last block
+    // puts the step's new token (key L - 1) into the tile of that block in
+    // place of what the cache held there, and stages its cache write
+    const bool app = a.k_new != nullptr && td.flags != TILE_GROUP && td.ntok == 1 &&
+                     nspan == 1 && L >= 1 && j + take == td.nb;
 
     // this lane's query row in row tile r: tile row 16 r + n = token qj,
     // head kvh*G + (row % G)
@@ -813,6 +952,13 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     const int pos_first = td.flags == TILE_GROUP ? L - 1
                           : tree                 ? span_start - 1
                                                  : L - nspan + td.qtok0;
+
+    NewRow<kv, D> nrow;
+    if (app) {
+        constexpr int kEl = kv == KV_F32 ? 4 : 2;  // bytes of a new row's element
+        const int64_t off = ((int64_t)(qs + td.qtok0) * Hkv + kvh) * D * kEl;
+        nrow.load((const char*)a.k_new + off, (const char*)a.v_new + off, lane);
+    }
 
     const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
     for (int c0 = 0; c0 < take; c0 += 64) {
@@ -930,6 +1076,23 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             }
         };
         auto consume = [&](T& cur, int i) { consume_tile(cur, i); };
+        // the chunk's last blocks: the segment's last block takes the step's
+        // new token first
+        auto consume_tail = [&](T& cur, int i) {
+            if (app && c0 + i == take - 1) {
+                float ks = 1.f, vs = 1.f;
+                if constexpr (kFp8Cache) {
+                    ks = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks), i));
+                    vs = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_vs), i));
+                }
+                stage.add(a, cur, nrow, (L - 1) & 15,
+                          (int64_t)__builtin_amdgcn_readlane(my_phys, i) * Hkv + kvh, ks, vs,
+                          lane);
+            }
+            consume_tile(cur, i);
+        };
         auto fetch = [&](T& dst, int i) {
             const int ph = __builtin_amdgcn_readlane(my_phys, i);
             dst.template load<kStreamLoads>(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
@@ -960,7 +1123,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             const int i = i0 + r;
             if (i < cnt) {
                 if (i + PF < cnt) fetch(ring[(r + PF) % (PF + 1)], i + PF);
-                consume(ring[r % (PF + 1)], i);
+                consume_tail(ring[r % (PF + 1)], i);
             }
         }
     }
@@ -1021,6 +1184,18 @@ template <int kv, int D>
 __device__ __forceinline__ void attention_body(const AttnArgs& a) {
     const int* h = a.hdr + HDR_STREAM + 4 * a.stream;
     const int V = h[HDR_NPIECES];
+    // decode with append: the new keys' cache writes, staged until the end
+    using E = typename NewStage<kv, D>::E;
+    constexpr int kMax = NewStage<kv, D>::kMax;
+    __shared__ __align__(16) E s_new_k[kMax * D];
+    __shared__ __align__(16) E s_new_v[kMax * D];
+    __shared__ int64_t s_new_bh[kMax];
+    __shared__ int s_new_o[kMax];
+    NewStage<kv, D> stage;
+    stage.k = s_new_k;
+    stage.v = s_new_v;
+    stage.bh = s_new_bh;
+    stage.o = s_new_o;
     for (int v = blockIdx.x; v < V; v += gridDim.x) {
         const PieceStart ps = a.pieces[v];
         int t = ps.tile, j = ps.j;
@@ -1032,15 +1207,16 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
             // a decode's context and a cascade member's suffix are read by no
             // other tile of the call, so they are streamed past the caches
             if (PA_GROUP_L2 && td.flags == TILE_GROUP)
-                run_segment<kv, D, false>(a, td, kvh, j, take, v);
+                run_segment<kv, D, false>(a, td, kvh, j, take, v, stage);
             else
-                run_segment<kv, D, PA_NT_LOADS != 0>(a, td, kvh, j, take, v);
+                run_segment<kv, D, PA_NT_LOADS != 0>(a, td, kvh, j, take, v, stage);
             left -= take;
             j = 0;
             ++t;
             if (left > 0) td = a.tiles[t];
         }
     }
+    stage.flush(a, threadIdx.x & 63);
 }
 
 // Single-token tiles: bound by HBM. PA_NARROW_MIN_WAVES > 0 would make the

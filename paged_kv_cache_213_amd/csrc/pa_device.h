@@ -1,8 +1,9 @@
 // pa_device.h -- device helpers shared by the gfx950 attention kernels:
 // vector types, the hardware exp2, reductions over the four lanes that hold
 // one query row in the 16x16 matrix-core layouts, bf16 packing, the e4m3
-// to bf16 conversion and cache-line loads with or without the nontemporal
-// hint. Not part of the public ABI.
+// to bf16 conversion, the fp32 to e4m3 encoding of the append and
+// cache-line loads with or without the nontemporal hint. Not part of the
+// public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,6 +24,24 @@ constexpr float kLog2e = 1.44269504088896340736f;
 enum KvKind { KV_F32 = PA_F32, KV_BF16 = PA_BF16, KV_FP8 = PA_FP8_E4M3FN, KV_FP8Q = KIND_FP8_QK };
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> OCP e4m3fn by bit manipulation: round to nearest, ties to even;
+// magnitudes at or above 448 saturate to 448 (0x7E); NaN -> 0x7F.
+__device__ __forceinline__ uint32_t encode_e4m3fn(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return 0x7fu;            // NaN
+    if (a >= 0x43e00000u) return sign | 0x7eu;    // >= 448 (and inf)
+    if (a >= 0x3c800000u) {                       // >= 2^-6: normal in e4m3
+        // keep 3 of 23 mantissa bits, rounding the dropped 20 to even
+        uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) >> 20;
+        return sign | (r - (120u << 3));          // rebias exponent 127 -> 7
+    }
+    // subnormal grid: multiples of 2^-9; the result 8 is 2^-6, code 0x08
+    const float q = __uint_as_float(a) * 512.0f;
+    return sign | (uint32_t)__builtin_rintf(q);
+}
 
 // Reductions over the four lanes n, n + 16, n + 32, n + 48 that hold one
 // query row, with the gfx950 row swaps: permlane16_swap exchanges 16-lane

@@ -193,6 +193,10 @@ struct AttnArgs {
     int32_t max_blocks_per_seq;
     int32_t max_context_len;
     float scale_log2;  // softmax scale times log2(e)
+    // decode with append: this step's K/V rows [num_seqs][Hkv][D] (q dtype),
+    // put at position context_lens - 1 of each sequence (nullptr: none)
+    const void* k_new;
+    const void* v_new;
 };
 
 struct MergeArgs {

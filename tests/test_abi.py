@@ -33,7 +33,9 @@ def test_header_declares_the_entry_points():
     for want in ("pa_workspace_bytes", "pa_paged_attn_decode", "pa_paged_attn_hybrid",
                  "pa_kv_append", "pa_status_string", "pa_version", "pa_fp8_e4m3fn_to_f32",
                  "pa_probe_stream_read", "pa_probe_copy", "pa_plan", "pa_paged_attn_run",
-                 "pa_paged_attn_partial", "pa_paged_attn_merge", "pa_plan_cascade", "pa_plan_tree",
+                 "pa_paged_attn_partial", "pa_paged_attn_merge", "pa_paged_attn_run_append",
+                 "pa_paged_attn_partial_append", "pa_paged_attn_decode_append",
+                 "pa_plan_cascade", "pa_plan_tree",
                  "pa_copy_blocks", "pa_validate_batch", "pa_bm_create"):
         assert want in names
 
@@ -116,6 +118,15 @@ def test_argument_checks_before_launch():
     assert rc == pa.PA_EINVAL
     assert lib.pa_kv_append(ctypes.byref(s), F, F, None, None, F, F, F, 0, None) == pa.PA_OK
     assert lib.pa_fp8_e4m3fn_to_f32(None, None, -1, None) == pa.PA_EINVAL
+    # decode with append: both rows needed, 16-byte aligned
+    app = lambda fn, kn, vn: getattr(lib, fn)(ctypes.byref(s), F, None, F, kn, vn, F, F, None,
+                                              None, F, F, 4, 100, 0.1, F, ws, None)
+    for fn in ("pa_paged_attn_decode_append", "pa_paged_attn_run_append",
+               "pa_paged_attn_partial_append"):
+        assert app(fn, None, F) == pa.PA_EINVAL
+        assert app(fn, F, None) == pa.PA_EINVAL
+        assert app(fn, F + 8, F) == pa.PA_EINVAL
+        assert app(fn, F, F + 2) == pa.PA_EINVAL
 
 
 def test_workspace_sizes():
