@@ -378,7 +378,8 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
             }
             records += l.max_cas_recs;
         }
-        if (records > 0 && pa::launch_merge(s->q_dtype, s->head_dim, ma, records, hs) != hipSuccess)
+        if (records > 0 && pa::launch_merge(s->q_dtype, s->head_dim, ma, records,
+                                            l.max_pieces[pa::STREAM_WIDE] > 0, hs) != hipSuccess)
             return PA_EHIP;
     }
     return PA_OK;

@@ -719,6 +719,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 #ifndef PA_PREFETCH
 #define PA_PREFETCH 2
 #endif
+// Registers of block ids per lane: a chunk of the narrow kernel holds up to
+// 64 times this many blocks. Measured (decode step with append, three
+// alternating runs each): 2 left the Llama-3-8B-shaped step unchanged within
+// its run-to-run spread and made the 256-sequence long-context step 4%
+// slower than 1.
+#ifndef PA_ID_WINDOWS
+#define PA_ID_WINDOWS 1
+#endif
 #ifndef PA_PREFETCH_FP8
 #define PA_PREFETCH_FP8 2
 #endif
@@ -961,20 +969,54 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     }
 
     const int32_t* bt_row = a.block_tables + (int64_t)seq * a.max_blocks_per_seq;
-    for (int c0 = 0; c0 < take; c0 += 64) {
-        const int cnt = min(64, take - c0);
-        // block ids (and fp8 scales) of up to 64 blocks, one per lane; ids
-        // outside the pool are clamped into it: a wrong table gives undefined
-        // results, never an out-of-bounds access
-        int my_phys = 0;
-        float my_ks = 1.f, my_vs = 1.f;
-        if (lane < cnt) {
-            my_phys = min(max(bt_row[td.b0 + j + c0 + lane], 0), a.num_blocks - 1);
-            if constexpr (kFp8Cache) {
-                my_ks = a.k_scale[(int64_t)my_phys * Hkv + kvh];
-                my_vs = a.v_scale[(int64_t)my_phys * Hkv + kvh];
+    // blocks are taken in chunks of up to 64 NW, their ids (and fp8 scales)
+    // held one per lane in NW registers; the ring drains at a chunk's end
+    // and refills after the next chunk's ids arrive
+    constexpr int NW = PA_ID_WINDOWS;
+    for (int c0 = 0; c0 < take; c0 += 64 * NW) {
+        const int cnt = min(64 * NW, take - c0);
+        // ids outside the pool are clamped into it: a wrong table gives
+        // undefined results, never an out-of-bounds access
+        int my_phys_w[NW];
+        float my_ks_w[NW], my_vs_w[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            my_phys_w[w] = 0;
+            my_ks_w[w] = my_vs_w[w] = 1.f;
+            if (64 * w + lane < cnt)
+                my_phys_w[w] =
+                    min(max(bt_row[td.b0 + j + c0 + 64 * w + lane], 0), a.num_blocks - 1);
+        }
+        if constexpr (kFp8Cache) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                if (64 * w + lane < cnt) {
+                    my_ks_w[w] = a.k_scale[(int64_t)my_phys_w[w] * Hkv + kvh];
+                    my_vs_w[w] = a.v_scale[(int64_t)my_phys_w[w] * Hkv + kvh];
+                }
             }
         }
+        // the values of block i of the chunk (wave-uniform)
+        // (each register read out, the scalar results selected: no register
+        // is indexed by a runtime value)
+        auto phys_of = [&](int i) {
+            int x = __builtin_amdgcn_readlane(my_phys_w[0], i & 63);
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                const int y = __builtin_amdgcn_readlane(my_phys_w[w], i & 63);
+                x = (i >> 6) == w ? y : x;
+            }
+            return x;
+        };
+        auto scale_of = [&](const float (&arr)[NW], int i) {
+            int x = __builtin_amdgcn_readlane(__builtin_bit_cast(int, arr[0]), i & 63);
+#pragma unroll
+            for (int w = 1; w < NW; ++w) {
+                const int y = __builtin_amdgcn_readlane(__builtin_bit_cast(int, arr[w]), i & 63);
+                x = (i >> 6) == w ? y : x;
+            }
+            return __builtin_bit_cast(float, x);
+        };
         // per-block work on block i of the chunk
         auto consume_tile = [&](auto& cur, int i) {
             const int jb = td.b0 + j + c0 + i;  // logical block
@@ -983,10 +1025,8 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             float c = kv == KV_FP8Q ? 1.f : a.scale_log2;
             float vsc = 1.f;
             if constexpr (kFp8Cache) {
-                c *= __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                   __builtin_bit_cast(int, my_ks), i));
-                vsc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                    __builtin_bit_cast(int, my_vs), i));
+                c *= scale_of(my_ks_w, i);
+                vsc = scale_of(my_vs_w, i);
             }
             // The row tiles' steps are laid out phase by phase (all
             // products, all scores, one shared test for a reference move,
@@ -1082,19 +1122,16 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
             if (app && c0 + i == take - 1) {
                 float ks = 1.f, vs = 1.f;
                 if constexpr (kFp8Cache) {
-                    ks = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks), i));
-                    vs = __builtin_bit_cast(
-                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_vs), i));
+                    ks = scale_of(my_ks_w, i);
+                    vs = scale_of(my_vs_w, i);
                 }
-                stage.add(a, cur, nrow, (L - 1) & 15,
-                          (int64_t)__builtin_amdgcn_readlane(my_phys, i) * Hkv + kvh, ks, vs,
+                stage.add(a, cur, nrow, (L - 1) & 15, (int64_t)phys_of(i) * Hkv + kvh, ks, vs,
                           lane);
             }
             consume_tile(cur, i);
         };
         auto fetch = [&](T& dst, int i) {
-            const int ph = __builtin_amdgcn_readlane(my_phys, i);
+            const int ph = phys_of(i);
             dst.template load<kStreamLoads>(a.k_cache, a.v_cache, (int64_t)ph * Hkv + kvh, lane);
         };
         constexpr int PF = kFp8Cache ? PA_PREFETCH_FP8 : PA_PREFETCH;
@@ -1295,7 +1332,7 @@ __device__ __forceinline__ void write_row(const MergeArgs& a, int64_t row, int g
 // per-row buffers or the slots of the pieces that cut it.
 template <int qd, int D>
 __device__ __forceinline__ void merge_cascade(const MergeArgs& a, const CascadeRec rc) {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;
     const int G = a.group, Hkv = a.num_kv_heads;
     if (n >= G) return;
@@ -1338,16 +1375,19 @@ __device__ __forceinline__ void merge_cascade(const MergeArgs& a, const CascadeR
     write_row<qd, D>(a, row, g, acc.M, acc.W, acc.acc);
 }
 
+// One workgroup per record; a wide segment's row tiles are shared among the
+// workgroup's waves (one wave for the others).
 template <int qd, int D>
-__global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+    const int wave = (int)threadIdx.x >> 6, nwaves = (int)blockDim.x >> 6;
     if ((int)blockIdx.x >= a.max_splits) {
         const int c = (int)blockIdx.x - a.max_splits;
-        if (c < a.hdr[HDR_NCAS]) merge_cascade<qd, D>(a, a.cas_recs[c]);
+        if (wave == 0 && c < a.hdr[HDR_NCAS]) merge_cascade<qd, D>(a, a.cas_recs[c]);
         return;
     }
     const SplitSeg sp = a.splits[blockIdx.x];
     if (sp.k0 < 0) return;  // past the list of cut segments
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;  // the attention kernel's layout
     const int G = a.group;
     const int nt = sp.stream == STREAM_WIDE ? a.wide_nt : 1;  // row tiles per slot
@@ -1358,7 +1398,7 @@ __global__ __launch_bounds__(64) void merge_kernel(MergeArgs a) {
     auto slot_of = [&](int k) {
         return ((int64_t)k * Hkv + sp.kvh) * 2 + (k == sp.k0 ? SLOT_TAIL : SLOT_HEAD);
     };
-    for (int r = 0; r < nt; ++r) {
+    for (int r = wave; r < nt; r += nwaves) {
         const int rr = 16 * r + n;
         if (rr >= sp.ntok * G) break;  // rows past the tile hold no partials
         float M = -INFINITY, W = 0.f;
@@ -1529,9 +1569,10 @@ hipError_t launch_attention(int kind, int head_dim, const AttnArgs& a, int64_t m
 }
 
 hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t records,
-                        hipStream_t s) {
+                        bool wide, hipStream_t s) {
     if (records <= 0) return hipSuccess;
-    const dim3 grid((unsigned)records), block(64);
+    // a wide segment's eight row tiles go to four waves
+    const dim3 grid((unsigned)records), block(wide ? 256 : 64);
     if (q_dtype == PA_F32 && head_dim == 64)
         hipLaunchKernelGGL((merge_kernel<PA_F32, 64>), grid, block, 0, s, a);
     else if (q_dtype == PA_F32 && head_dim == 128)

@@ -255,7 +255,7 @@ hipError_t launch_attention(int kind, int head_dim, const AttnArgs& a, int64_t m
 int resident_waves(int kind, int head_dim, int stream);
 // records: cut-segment workgroups (a.max_splits) plus cascade records
 hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t records,
-                        hipStream_t s);
+                        bool wide, hipStream_t s);
 hipError_t launch_append(int new_dtype, int kv_dtype, const AppendArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);
 hipError_t launch_fp8_decode(const uint8_t* in, float* out, int n, hipStream_t s);
