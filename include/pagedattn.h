@@ -34,6 +34,11 @@
  *     q, out       [T][Hq][D]           dtype q_dtype (out has q's dtype)
  *     k_cache      [num_blocks][Hkv][16][D]   token rows of D values
  *     v_cache      [num_blocks][Hkv][D][16]   D rows of 16 token values
+ *                  (dim-major, unlike K: a departure from the token-major
+ *                  [16][D] block the plainest reading of the pages gives,
+ *                  so that the P.V matrix-core operand comes straight from
+ *                  16-byte loads; the price is that an append writes a
+ *                  token's V as D values 32 bytes apart)
  *     k_scale, v_scale [num_blocks][Hkv] float32 (FP8 caches only, else NULL)
  *     block_tables [num_seqs][max_blocks_per_seq] int32
  *     context_lens [num_seqs] int32: keys each sequence attends over, which
