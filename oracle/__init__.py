@@ -77,7 +77,7 @@ def _load():
                                            P, P, I]
         lib.or_paged_attention_split.restype = I
         lib.or_paged_attention_split.argtypes = [I, I, I, I, P, I, P, P, I, P, P, P, I, P, P, F,
-                                                 I, P, P]
+                                                 I, P, P, P]
         _lib = lib
     return _lib
 
@@ -169,8 +169,11 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale, *, q
 
 def paged_attention_split(q, k_cache, v_cache, block_tables, context_lens, scale,
                           partition_size, *, q_dtype, kv_dtype, num_q_heads, num_kv_heads,
-                          head_dim, query_start_loc=None, k_scale=None, v_scale=None):
-    """Partitioned computation merged by log-sum-exp (test-only pin)."""
+                          head_dim, query_start_loc=None, k_scale=None, v_scale=None,
+                          first_len=None):
+    """Partitioned computation merged by log-sum-exp (test-only pin).
+    first_len[i]: tokens of sequence i's first partition (default the
+    partition size), so the cuts can fall anywhere in a context."""
     qa = _c(q, _NP[q_dtype])
     kc = _c(k_cache, _NP[kv_dtype])
     vc = _c(v_cache, _NP[kv_dtype])
@@ -178,6 +181,7 @@ def paged_attention_split(q, k_cache, v_cache, block_tables, context_lens, scale
     cl = _c(context_lens, np.int32)
     qsl = _c(query_start_loc, np.int32)
     ks, vs = _c(k_scale, np.float32), _c(v_scale, np.float32)
+    fl = _c(first_len, np.int32)
     S = cl.shape[0]
     T = int(qsl[-1]) if qsl is not None else S
     out = np.full((T, num_q_heads, head_dim), np.nan, dtype=np.float64)
@@ -186,7 +190,7 @@ def paged_attention_split(q, k_cache, v_cache, block_tables, context_lens, scale
                                           _DT[q_dtype], _ptr(kc), _ptr(vc), _DT[kv_dtype],
                                           _ptr(ks), _ptr(vs), _ptr(bt), bt.shape[1], _ptr(cl),
                                           _ptr(qsl), float(scale), int(partition_size),
-                                          _ptr(out), _ptr(lse))
+                                          _ptr(fl), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError(f"or_paged_attention_split failed ({rc})")
     return out, lse

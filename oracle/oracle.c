@@ -369,20 +369,27 @@ static void or_partial(const or_args* a, long qrow, int h, const double* K, cons
 }
 
 /* Test-only: the same rows computed as partial results (m_p, l_p, o_p)
- * over fixed key ranges [pP, (p+1)P) and merged by log-sum-exp
- * ("03 -- Engines Papers", section 12; "The LLM inference engine
- * playbook", Theme 4, split-K decode):
+ * over key ranges and merged by log-sum-exp ("03 -- Engines Papers",
+ * section 12; "The LLM inference engine playbook", Theme 4, split-K
+ * decode):
  *   M = max_p m_p,  w_p = l_p exp(m_p - M),
  *   out = sum_p w_p o_p / sum_p w_p,  lse = M + ln sum_p w_p.
- * Used only to pin that splitting reaches the unsplit result. */
+ * The ranges of sequence i are [0, f_i), [f_i, f_i + P), ... with f_i =
+ * first_len[i] (first_len NULL: f_i = P), so the cuts can sit anywhere in
+ * a context, as where a stream of blocks cut into equal pieces meets a
+ * sequence's blocks at an arbitrary offset. Used only to pin that
+ * splitting reaches the unsplit result. */
 int or_paged_attention_split(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                              const void* q, int q_dtype, const void* k_cache,
                              const void* v_cache, int kv_dtype, const float* k_scale,
                              const float* v_scale, const int32_t* block_tables,
                              int max_blocks_per_seq, const int32_t* context_lens,
                              const int32_t* query_start_loc, float scale, int partition_size,
-                             double* out, double* lse) {
+                             const int32_t* first_len, double* out, double* lse) {
     if (partition_size <= 0 || num_q_heads % num_kv_heads) return -1;
+    if (first_len)
+        for (int i = 0; i < num_seqs; ++i)
+            if (first_len[i] <= 0 || first_len[i] > partition_size) return -1;
     or_args a = {num_seqs, num_q_heads, num_kv_heads, head_dim, q, q_dtype, k_cache, v_cache,
                  kv_dtype, k_scale, v_scale, block_tables, max_blocks_per_seq, context_lens,
                  query_start_loc, scale};
@@ -390,7 +397,7 @@ int or_paged_attention_split(int num_seqs, int num_q_heads, int num_kv_heads, in
     int maxL = 1;
     for (int i = 0; i < num_seqs; ++i)
         if (context_lens[i] > maxL) maxL = context_lens[i];
-    const int maxP = (maxL + partition_size - 1) / partition_size;
+    const int maxP = (maxL + partition_size - 1) / partition_size + 1;
     double* K = (double*)malloc(sizeof(double) * (size_t)maxL * D);
     double* V = (double*)malloc(sizeof(double) * (size_t)maxL * D);
     double* s = (double*)malloc(sizeof(double) * (size_t)partition_size);
@@ -407,14 +414,18 @@ int or_paged_attention_split(int num_seqs, int num_q_heads, int num_kv_heads, in
                 long pos = (long)L - n + j;
                 int nk = (int)(pos + 1);
                 if (nk > L) nk = L;
-                const int np = nk > 0 ? (nk + partition_size - 1) / partition_size : 0;
+                const int f = first_len ? first_len[i] : partition_size;
+                const int np = nk <= 0 ? 0
+                               : nk <= f ? 1
+                                         : 1 + (nk - f + partition_size - 1) / partition_size;
                 for (int hh = 0; hh < G; ++hh) {
                     const int h = g * G + hh;
                     const long r = q0 + j;
                     double* o = out + (r * Hq + h) * D;
                     for (int p = 0; p < np; ++p) {
-                        int t0 = p * partition_size;
-                        int t1 = t0 + partition_size < nk ? t0 + partition_size : nk;
+                        int t0 = p == 0 ? 0 : f + (p - 1) * partition_size;
+                        int t1 = p == 0 ? f : t0 + partition_size;
+                        if (t1 > nk) t1 = nk;
                         or_partial(&a, r, h, K, V, t0, t1, s, &mp[p], &lp[p], op + (long)p * D);
                     }
                     if (np == 0) {

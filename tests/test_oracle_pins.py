@@ -218,6 +218,46 @@ def test_split_merge_reaches_the_unsplit_result(P):
     np.testing.assert_allclose(l2, l1, rtol=1e-12, atol=1e-12)
 
 
+def test_split_at_stream_piece_boundaries():
+    """The attention kernels cut a KV head's stream of key blocks (all
+    sequences' blocks, one after another) into pieces of R blocks, so a
+    sequence's ranges start wherever a piece boundary meets its blocks.
+    Partials over those ranges, merged by log-sum-exp, equal the one-pass
+    result; and the number of ranges per sequence is the number of pieces
+    the plan gives its segment."""
+    from tests import plan_model as PM
+    lens = [5, 16, 17, 100, 511, 513, 700, 1, 48, 49, 300]
+    wl = W.custom_workload(lens, num_q_heads=4, num_kv_heads=2, head_dim=32, q_dtype="f32",
+                           kv_dtype="f32", seed=19)
+    _, _, post = H.oracle_host(wl)
+    kw = dict(q_dtype="f32", kv_dtype="f32", num_q_heads=4, num_kv_heads=2, head_dim=32)
+    o1, l1 = oracle.paged_attention(post["q"], post["k_cache"], post["v_cache"],
+                                    wl.block_tables, wl.context_lens, wl.scale, **kw)
+    for R in (1, 3, 7, 16, 40):
+        lay = PM.make_layout(G=2, Hkv=2, num_seqs=wl.num_seqs, num_tokens=wl.num_tokens,
+                             max_context_len=wl.max_context_len, max_query_len=1, decode=True,
+                             partition_size=16 * R, cascade=False, waves=(64, 64, 64))
+        plan = PM.build_plan(lay, Hkv=2, context_lens=wl.context_lens, qsl=None,
+                             num_tokens=wl.num_tokens, max_context_len=wl.max_context_len)
+        first, nparts = [], []
+        for t, td in enumerate(plan.tiles):
+            off = plan.tile_prefix[t] - plan.tile_prefix[plan.t_first[1]]  # blocks before it
+            k0 = off // R
+            k1 = (off + td.nb - 1) // R
+            first.append(16 * min(R * (k0 + 1) - off, td.nb) if td.L > 0 else 16 * R)
+            nparts.append(k1 - k0 + 1)
+        first = np.minimum(np.array(first), 16 * R)
+        o2, l2 = oracle.paged_attention_split(post["q"], post["k_cache"], post["v_cache"],
+                                              wl.block_tables, wl.context_lens, wl.scale,
+                                              16 * R, first_len=first, **kw)
+        np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(l2, l1, rtol=1e-12, atol=1e-12)
+        for i, L in enumerate(lens):
+            f = int(first[i])
+            want = 1 if L <= f else 1 + -(-(L - f) // (16 * R))
+            assert want == nparts[i], (R, i, L, f, want, nparts[i])
+
+
 def test_softmax_shift_invariance_at_huge_scores():
     """Adding a component to every key that raises all scores by ~1e4
     leaves the output unchanged (the max is subtracted) and finite."""
