@@ -539,11 +539,11 @@ def main():
             "traffic_note": "HBM bytes per attention pass launch (calibrated FETCH_SIZE + "
                             "WRITE_SIZE, profiles/); null if not recorded for the current "
                             "attention source",
-            "kernel": "attention pass (attention_span for chunked-prefill spans, then "
-                      "attention_narrow, one launch each per layer; decode batches append "
-                      "the step's K/V rows in it unless --append separate); HIP events "
-                      "around the back-to-back pass-1 launches of all layers, divided by "
-                      "the layers",
+            "kernel": "attention pass (attention_narrow per layer, beside attention_span "
+                      "on the library's second stream when the batch has chunked-prefill "
+                      "spans; decode batches append the step's K/V rows in it unless "
+                      "--append separate); HIP events on the caller's stream around the "
+                      "back-to-back pass-1 calls of all layers, divided by the layers",
             "launch_us_mean": round(att_mean * 1e3, 2),
             "launch_us_min_max": [round(float(att_ms.min()) * 1e3, 2),
                                   round(float(att_ms.max()) * 1e3, 2)],

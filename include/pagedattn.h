@@ -20,10 +20,26 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Every array argument is a DEVICE pointer owned by the caller. The
- *   library never allocates, frees or synchronizes; every call only
- *   enqueues kernels on `stream` (a hipStream_t passed as void*, NULL =
- *   the null stream) and returns. Scratch memory is the caller's
+ *   library never allocates device memory, frees or synchronizes; every
+ *   call only enqueues kernels on `stream` (a hipStream_t passed as void*,
+ *   NULL = the null stream) and returns. Scratch memory is the caller's
  *   `workspace`, sized by pa_workspace_bytes.
+ * - A call whose batch holds chunked-prefill spans beside single-token
+ *   tiles runs its span kernel on `stream` and its decode kernels on a
+ *   second stream of the library's, forked from `stream` after the work
+ *   queued before the call and joined back into it before the call's
+ *   merge (or, for pa_paged_attn_partial, before it returns), so the two
+ *   kinds of tile run side by side ("03 -- Engines Papers", section 3).
+ *   Work queued on `stream` after the call still waits for all of it, and
+ *   a graph capture of `stream` captures both branches. The library makes
+ *   that stream (default priority) and two events once per device, in the
+ *   first pa_workspace_bytes call for a batch that can hold spans (else in
+ *   the first such attention call: callers that capture graphs size their
+ *   workspace first), and keeps them until the process ends; calls from
+ *   several host threads on one device take a lock around the fork and
+ *   join. pa_paged_attn_hybrid_noalloc never makes them: it uses them if
+ *   they exist, else runs every kernel on `stream`. Results are the same
+ *   either way.
  * - Return value: PA_OK (0) or a negative pa_status. Arguments are checked
  *   on the host before anything is enqueued; a failed check enqueues
  *   nothing. Data-dependent contract breaches (a block id out of range, a
@@ -347,6 +363,9 @@ typedef struct pa_layout_info {
     int32_t header_words;      /* int32 words of the header */
     int32_t part_cost[3];      /* when balancing: a segment's start in blocks
                                   of work, per stream */
+    int32_t span_shared;       /* span workgroups when the span launch runs
+                                  beside the narrow and group launches (one
+                                  per compute unit; 0: never) */
     int64_t max_tiles, max_pieces[3], max_splits, max_cas_recs;
     int64_t off_tiles, off_splits, off_tree, off_cas_seq, off_cas_recs;
     int64_t off_cas_lse[2], off_cas_o[2];
@@ -367,7 +386,9 @@ const char* pa_status_string(int status);
  * their block counts and pa_layout_info the per-stream part costs; 207
  * runs P.V on the fp8 matrix cores too when fp8_qk is set; 208 added
  * pa_paged_attn_run_append, pa_paged_attn_partial_append and
- * pa_paged_attn_decode_append. */
+ * pa_paged_attn_decode_append; 209 runs a batch's span launch beside its
+ * narrow and group launches (a second stream of the library's) and gave
+ * pa_layout_info span_shared. */
 int pa_version(void);
 
 #ifdef __cplusplus

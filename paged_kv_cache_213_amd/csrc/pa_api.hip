@@ -1,10 +1,13 @@
 // pa_api.hip -- the C ABI: argument checks, workspace layout, launches.
 // Every function here only checks host-known arguments and enqueues
-// kernels on the caller's stream; nothing allocates or synchronizes.
+// kernels on the caller's stream (and, for a batch with spans beside
+// single-token tiles, on the library's side stream, forked from and joined
+// back into the caller's); nothing allocates device memory or synchronizes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 
 #include "pa_internal.h"
@@ -34,8 +37,15 @@
 // returns for the current device.
 static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
 
-namespace {
+// A call whose batch holds span tiles and single-token tiles runs the span
+// launch on the caller's stream and the narrow and group launches on a
+// second stream of the library's, so that the two run side by side (1); or
+// every launch on the caller's stream, one after another (0).
+#ifndef PA_SIDE_STREAM
+#define PA_SIDE_STREAM 1
+#endif
 
+namespace {
 
 constexpr size_t kAlign = 256;
 
@@ -51,6 +61,7 @@ struct Layout {
     int narrow_tokens = 0, wide_tokens = 0;
     int waves[pa::NUM_STREAMS] = {};
     int part_cost[pa::NUM_STREAMS] = {};
+    int span_shared = 0;  // span workgroups beside the narrow launches (0: none)
     int64_t max_tiles = 0;
     int64_t max_pieces[pa::NUM_STREAMS] = {};
     int64_t max_splits = 0;  // bound of the cut-segment list
@@ -113,6 +124,7 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     const bool spans = PA_WIDE_SPANS && !decode && max_query_len > l.narrow_tokens &&
                        s->kv_dtype != PA_F32;
     if (!spans) l.wide_tokens = 0;
+    if (spans && PA_SIDE_STREAM) l.span_shared = pa::span_shared_groups(kernel_kind(s), s->head_dim);
     l.cascade = s->cascade != 0;
     // a group tile holds the single query tokens of up to 16 / G members
     l.members_per_tile = 16 / G > 1 ? 16 / G : 1;
@@ -249,6 +261,7 @@ int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl
     pl.num_kv_heads = s->num_kv_heads;
     pl.part_blocks = l.part_blocks;
     pl.min_blocks = pa::kMinPieceBlocks;
+    pl.span_shared = l.span_shared;
     pl.max_tiles = (int32_t)l.max_tiles;
     pl.tiles = (pa::TileDesc*)(ws + l.off_tiles);
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
@@ -281,6 +294,40 @@ int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl
     return pa::launch_plan(pl, (hipStream_t)stream) == hipSuccess ? PA_OK : PA_EHIP;
 }
 
+// The library's second stream on a device (default priority), with the two
+// events that fork it from the caller's stream and join it back. Made once
+// per device, by pa_workspace_bytes for a batch that can hold spans or else
+// by the first such call, and kept until the process ends. The mutex keeps
+// one call's record / wait / launch sequence together when several host
+// threads enqueue work on one device.
+struct SideStream {
+    std::once_flag once;
+    std::atomic<bool> ok{false};
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    std::mutex m;
+};
+constexpr int kMaxSideDevices = 64;
+SideStream g_side[kMaxSideDevices];
+
+// The current device's side stream; made here if `create`, else only
+// returned when it exists (nullptr: the call runs on the caller's stream).
+SideStream* side_stream(bool create) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+    SideStream& d = g_side[dev];
+    if (create) {
+        std::call_once(d.once, [&d] {
+            d.ok.store(hipStreamCreateWithFlags(&d.s, hipStreamNonBlocking) == hipSuccess &&
+                           hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) ==
+                               hipSuccess &&
+                           hipEventCreateWithFlags(&d.join, hipEventDisableTiming) == hipSuccess,
+                       std::memory_order_release);
+        });
+    }
+    return d.ok.load(std::memory_order_acquire) ? &d : nullptr;
+}
+
 // Which passes of the attention a call enqueues.
 enum Passes { PASS_ATTENTION = 1, PASS_MERGE = 2, PASS_BOTH = 3 };
 
@@ -289,7 +336,8 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
              const int32_t* block_tables, const int32_t* context_lens, const int32_t* qsl,
              int num_seqs, int num_tokens, int max_query_len, int max_context_len, float scale,
              void* workspace, size_t workspace_bytes, void* stream, int passes,
-             const void* k_new = nullptr, const void* v_new = nullptr) {
+             const void* k_new = nullptr, const void* v_new = nullptr,
+             bool side_create = true) {
     Layout l;
     int rc = check_batch(s, context_lens, qsl, num_seqs, num_tokens, max_query_len,
                          max_context_len, workspace, workspace_bytes, &l);
@@ -338,8 +386,25 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
                 aa.cas_o[k] = (float*)(ws + l.off_cas_o[k]);
             }
         }
-        // spans first (matrix-core heavy), then the single-token tiles
-        for (int st = 0; st < pa::NUM_STREAMS; ++st) {
+        // spans first (matrix-core heavy), then the single-token tiles. A
+        // layout with span_shared > 0 forks the narrow and group launches
+        // onto the side stream, so that they run beside the span launch
+        // (the plan then cuts the span stream for one workgroup per compute
+        // unit whenever the other streams hold most of the work), and joins
+        // it back before the merge.
+        SideStream* side = nullptr;
+        if (l.span_shared > 0 && l.max_pieces[pa::STREAM_WIDE] > 0 &&
+            (l.max_pieces[pa::STREAM_NARROW] > 0 || l.max_pieces[pa::STREAM_GROUP] > 0))
+            side = side_stream(side_create);
+        std::unique_lock<std::mutex> side_lock;
+        if (side) {
+            side_lock = std::unique_lock<std::mutex>(side->m);
+            if (hipEventRecord(side->fork, hs) != hipSuccess ||
+                hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+                return PA_EHIP;
+        }
+        bool failed = false;
+        for (int st = 0; st < pa::NUM_STREAMS && !failed; ++st) {
             if (l.max_pieces[st] == 0) continue;
             aa.stream = st;
             aa.pieces = (const pa::PieceStart*)(ws + l.off_pieces[st]);
@@ -349,10 +414,16 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
             // blocks (group tiles hold shared prefixes only)
             aa.k_new = st == pa::STREAM_NARROW ? k_new : nullptr;
             aa.v_new = st == pa::STREAM_NARROW ? v_new : nullptr;
-            if (pa::launch_attention(kernel_kind(s), s->head_dim, aa, l.max_pieces[st], hs) !=
-                hipSuccess)
-                return PA_EHIP;
+            const hipStream_t ls = side && st != pa::STREAM_WIDE ? side->s : hs;
+            failed = pa::launch_attention(kernel_kind(s), s->head_dim, aa, l.max_pieces[st], ls) !=
+                     hipSuccess;
         }
+        // the join is enqueued even after a failed launch, so that a graph
+        // capture that forked the side stream gets it back
+        if (side && (hipEventRecord(side->join, side->s) != hipSuccess ||
+                     hipStreamWaitEvent(hs, side->join, 0) != hipSuccess))
+            failed = true;
+        if (failed) return PA_EHIP;
     }
     if (passes & PASS_MERGE) {
         pa::MergeArgs ma{};
@@ -385,19 +456,57 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
     return PA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t pa_workspace_bytes(const pa_shape* shape, int num_seqs, int num_q_tokens,
-                          int max_context_len, int max_query_len) {
+// Workspace bytes of a batch; *spans_beside: its span launch may run beside
+// the single-token launches (on the side stream).
+size_t workspace_bytes_of(const pa_shape* shape, int num_seqs, int num_q_tokens,
+                          int max_context_len, int max_query_len, bool* spans_beside) {
     if (check_shape(shape) != PA_OK || num_seqs < 0 || num_q_tokens < 0 || max_context_len < 0)
         return 0;
     const bool decode = max_query_len <= 1 && num_q_tokens == num_seqs;
     // a decode-shaped hybrid call may use either layout: size for the larger
     Layout a = make_layout(shape, num_seqs, num_q_tokens, max_context_len, max_query_len, decode);
     Layout b = make_layout(shape, num_seqs, num_q_tokens, max_context_len, max_query_len, false);
+    *spans_beside = b.span_shared > 0;
     return a.total > b.total ? a.total : b.total;
+}
+
+// One hybrid call: plan, attention and merge on the caller's stream (and
+// the side stream). side_create false: the side stream is used only if it
+// already exists (the no-alloc entry point makes nothing).
+int hybrid_impl(const pa_shape* shape, void* out, float* lse, const void* q, const void* k_cache,
+                const void* v_cache, const float* k_scale, const float* v_scale,
+                const int32_t* block_tables, const int32_t* context_lens,
+                const int32_t* query_start_loc, int num_seqs, int num_q_tokens,
+                int max_query_len, int max_context_len, float scale, void* workspace,
+                size_t workspace_bytes, void* stream, bool side_create) {
+    if (check_shape(shape) != PA_OK) return check_shape(shape);
+    if (!query_start_loc) return PA_EINVAL;
+    if (num_seqs > 0 && num_q_tokens > 0) {
+        int rc0 = check_io(shape, out, q, k_cache, v_cache, k_scale, v_scale, block_tables);
+        if (rc0 != PA_OK) return rc0;
+    }
+    int rc = plan_impl(shape, context_lens, query_start_loc, num_seqs, num_q_tokens,
+                       max_query_len, max_context_len, Groups{}, workspace, workspace_bytes, stream);
+    if (rc != PA_OK) return rc;
+    return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                    context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                    max_context_len, scale, workspace, workspace_bytes, stream, PASS_BOTH,
+                    nullptr, nullptr, side_create);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pa_workspace_bytes(const pa_shape* shape, int num_seqs, int num_q_tokens,
+                          int max_context_len, int max_query_len) {
+    bool spans_beside = false;
+    const size_t n = workspace_bytes_of(shape, num_seqs, num_q_tokens, max_context_len,
+                                        max_query_len, &spans_beside);
+    // a batch that can hold spans beside single-token tiles uses the side
+    // stream: make it now, before the caller can capture a call
+    if (spans_beside) side_stream(true);
+    return n;
 }
 
 int pa_plan(const pa_shape* shape, const int32_t* context_lens, const int32_t* query_start_loc,
@@ -533,18 +642,9 @@ int pa_paged_attn_hybrid(const pa_shape* shape, void* out, float* lse, const voi
                          int num_seqs, int num_q_tokens, int max_query_len,
                          int max_context_len, float scale, void* workspace,
                          size_t workspace_bytes, void* stream) {
-    if (check_shape(shape) != PA_OK) return check_shape(shape);
-    if (!query_start_loc) return PA_EINVAL;
-    if (num_seqs > 0 && num_q_tokens > 0) {
-        int rc0 = check_io(shape, out, q, k_cache, v_cache, k_scale, v_scale, block_tables);
-        if (rc0 != PA_OK) return rc0;
-    }
-    int rc = plan_impl(shape, context_lens, query_start_loc, num_seqs, num_q_tokens,
-                       max_query_len, max_context_len, Groups{}, workspace, workspace_bytes, stream);
-    if (rc != PA_OK) return rc;
-    return run_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
-                    context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
-                    max_context_len, scale, workspace, workspace_bytes, stream, PASS_BOTH);
+    return hybrid_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                       max_context_len, scale, workspace, workspace_bytes, stream, true);
 }
 
 int pa_kv_append(const pa_shape* shape, void* k_cache, void* v_cache, const float* k_scale,
@@ -629,15 +729,16 @@ int pa_paged_attn_hybrid_noalloc(const pa_shape* shape, void* out, float* lse, c
                                  int max_context_len, float scale, void* stream) {
     if (check_shape(shape) != PA_OK) return check_shape(shape);
     if (num_seqs < 0 || num_q_tokens < 0 || max_context_len < 0) return PA_EINVAL;
-    const size_t need =
-        pa_workspace_bytes(shape, num_seqs, num_q_tokens, max_context_len, max_query_len);
+    bool spans_beside = false;
+    const size_t need = workspace_bytes_of(shape, num_seqs, num_q_tokens, max_context_len,
+                                           max_query_len, &spans_beside);
     if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ESCRATCH;
     void* ws = scratch_address();
     if (!ws) return PA_EHIP;
-    return pa_paged_attn_hybrid(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale,
-                                block_tables, context_lens, query_start_loc, num_seqs,
-                                num_q_tokens, max_query_len, max_context_len, scale, ws,
-                                (size_t)PA_NOALLOC_SCRATCH_BYTES, stream);
+    return hybrid_impl(shape, out, lse, q, k_cache, v_cache, k_scale, v_scale, block_tables,
+                       context_lens, query_start_loc, num_seqs, num_q_tokens, max_query_len,
+                       max_context_len, scale, ws, (size_t)PA_NOALLOC_SCRATCH_BYTES, stream,
+                       false);
 }
 
 int pa_workspace_layout(const pa_shape* shape, int num_seqs, int num_q_tokens,
@@ -657,6 +758,7 @@ int pa_workspace_layout(const pa_shape* shape, int num_seqs, int num_q_tokens,
         r.off_part_lse[st] = (int64_t)l.off_lse[st];
         r.off_part_o[st] = (int64_t)l.off_o[st];
     }
+    r.span_shared = l.span_shared;
     r.narrow_tokens = l.narrow_tokens;
     r.wide_tokens = l.wide_tokens;
     r.part_blocks = l.part_blocks;
@@ -693,6 +795,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 208; }
+int pa_version(void) { return 209; }
 
 }  // extern "C"

@@ -583,15 +583,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     //    inside them starts at the tile's first block. With at least c + 1
     //    units per piece no piece is empty. A fixed partition size uses c =
     //    0, pieces of exactly P / 16 blocks.
+    //    The span stream is cut for a.span_shared workgroups (one per
+    //    compute unit, running beside the narrow launches) when the other
+    //    streams' cost is at least kSpanShareRatio times its own.
     int Rs[NUM_STREAMS], Cs[NUM_STREAMS];
+    int64_t cost_of[NUM_STREAMS];
+    for (int st = 0; st < NUM_STREAMS; ++st) {
+        const int t_lo = t_first[st], t_hi = t_first[st + 1];
+        const int c = a.part_blocks > 0 ? 0 : max(a.part_cost[st], 0);
+        cost_of[st] = (int64_t)(s_tp[t_hi] - s_tp[t_lo]) + (int64_t)c * (t_hi - t_lo);
+    }
+    const bool share = a.span_shared > 0 && a.part_blocks <= 0 && cost_of[STREAM_WIDE] > 0 &&
+                       cost_of[STREAM_NARROW] + cost_of[STREAM_GROUP] >=
+                           (int64_t)kSpanShareRatio * cost_of[STREAM_WIDE];
     for (int st = 0; st < NUM_STREAMS; ++st) {
         const int t_lo = t_first[st], t_hi = t_first[st + 1];
         const int64_t B = s_tp[t_hi] - s_tp[t_lo];
         const int c = a.part_blocks > 0 ? 0 : max(a.part_cost[st], 0);
-        const int64_t Bc = B + (int64_t)c * (t_hi - t_lo);  // cost of the substream
+        const int64_t Bc = cost_of[st];  // cost of the substream
+        const int waves = share && st == STREAM_WIDE ? a.span_shared : a.waves[st];
         int64_t R = a.part_blocks;
         if (R <= 0) {
-            R = ((int64_t)H * Bc + a.waves[st] - 1) / max(a.waves[st], 1);
+            R = ((int64_t)H * Bc + waves - 1) / max(waves, 1);
             R = max(R, (int64_t)a.min_blocks + c);
         }
         int64_t K = (Bc + R - 1) / R;  // pieces per substream

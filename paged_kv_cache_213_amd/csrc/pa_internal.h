@@ -135,6 +135,10 @@ struct PlanArgs {
     // row setup, the first block's latency, its epilogue), per stream
     int32_t part_cost[NUM_STREAMS];
     int32_t waves[NUM_STREAMS];  // resident workgroups of each stream's kernel
+    // span workgroups when the span stream runs beside the others (0: the
+    // span stream always gets waves[STREAM_WIDE]); used when the single-token
+    // streams' work is at least kSpanShareRatio times the span stream's
+    int32_t span_shared;
     int32_t min_blocks;          // smallest piece when balancing
     int32_t max_tiles;
     int64_t max_pieces[NUM_STREAMS];
@@ -244,6 +248,10 @@ struct CopyArgs {
 // Launchers (host side), defined next to their kernels.
 // The span kernel (wide stream): workgroups that fit on the device at once.
 int span_resident_groups(int kind, int head_dim);
+// Span workgroups that run beside the narrow launches of the same call (one
+// per compute unit, leaving each SIMD a wave slot for a narrow wave), or 0
+// when the span kernel's resources leave no such room.
+int span_shared_groups(int kind, int head_dim);
 hipError_t launch_span(int kind, int head_dim, const AttnArgs& a, int64_t max_pieces,
                        hipStream_t s);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
@@ -259,6 +267,13 @@ hipError_t launch_merge(int q_dtype, int head_dim, const MergeArgs& a, int64_t r
 hipError_t launch_append(int new_dtype, int kv_dtype, const AppendArgs& a, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyArgs& a, int num_pairs, hipStream_t s);
 hipError_t launch_fp8_decode(const uint8_t* in, float* out, int n, hipStream_t s);
+
+// The span stream runs on one workgroup per compute unit, beside the narrow
+// and group launches, when those streams' balanced work (blocks plus start
+// costs per KV head) is at least this many times the span stream's: then the
+// decodes' HBM-bound time hides the span tiles' longer run at half their
+// residency. Below it the span tiles keep the whole device.
+constexpr int kSpanShareRatio = 2;
 
 // Smallest piece (in 16-token blocks) when pieces are balanced over the
 // resident waves. One block: a wave that walked several short segments one

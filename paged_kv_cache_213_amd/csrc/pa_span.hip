@@ -564,6 +564,20 @@ int span_resident_d() {
     return slot->load(std::memory_order_acquire);
 }
 
+// Span workgroups that leave a narrow wave room on every SIMD: one per
+// compute unit when the span kernel's resources allow two (its four waves
+// then hold one wave slot of each SIMD), else 0.
+template <int kv, int D>
+int span_shared_d() {
+    const int w = span_resident_d<kv, D>();
+    int dev = 0, num_cu = 0;
+    if (w <= 0 || hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        num_cu <= 0)
+        return 0;
+    return w >= 2 * num_cu ? num_cu : 0;
+}
+
 template <int kv, int D>
 hipError_t launch_span_d(const AttnArgs& a, int64_t max_pieces, hipStream_t s) {
     int64_t grid = span_resident_d<kv, D>();
@@ -584,6 +598,16 @@ int span_resident_groups(int kind, int head_dim) {
     case PA_BF16 * 1000 + 128: return span_resident_d<KV_BF16, 128>();
     case PA_FP8_E4M3FN * 1000 + 64: return span_resident_d<KV_FP8, 64>();
     case PA_FP8_E4M3FN * 1000 + 128: return span_resident_d<KV_FP8, 128>();
+    default: return 0;
+    }
+}
+
+int span_shared_groups(int kind, int head_dim) {
+    switch ((kind == KIND_FP8_QK ? PA_FP8_E4M3FN : kind) * 1000 + head_dim) {
+    case PA_BF16 * 1000 + 64: return span_shared_d<KV_BF16, 64>();
+    case PA_BF16 * 1000 + 128: return span_shared_d<KV_BF16, 128>();
+    case PA_FP8_E4M3FN * 1000 + 64: return span_shared_d<KV_FP8, 64>();
+    case PA_FP8_E4M3FN * 1000 + 128: return span_shared_d<KV_FP8, 128>();
     default: return 0;
     }
 }

@@ -68,17 +68,21 @@ class Layout:
     max_cas_recs: int
     wide_nt: int
     part_cost: tuple
+    span_shared: int = 0  # span workgroups beside the narrow launches (0: never)
 
 
 SPAN_ROWS = 128  # query rows of a wide tile (four waves of 32)
 # when balancing, the cost of a segment's start in blocks of work, per stream
 # (wide, narrow, group)
 PART_COST = (6, 0, 0)
+# the span stream is cut for span_shared workgroups when the other streams'
+# balanced cost is at least this many times its own
+SPAN_SHARE_RATIO = 2
 
 
 def make_layout(*, G, Hkv, num_seqs, num_tokens, max_context_len, max_query_len, decode,
                 partition_size, cascade, waves, wide_nt=SPAN_ROWS // 16, f32=False,
-                part_cost=PART_COST):
+                part_cost=PART_COST, span_shared=0):
     """Workspace bounds of a batch, as the host sizes them."""
     narrow = 1 if decode else max(16 // G, 1)
     wide = max(SPAN_ROWS // G, 1)
@@ -101,7 +105,7 @@ def make_layout(*, G, Hkv, num_seqs, num_tokens, max_context_len, max_query_len,
             splits += min(mp - Hkv, tiles_of[st] * Hkv)
     return Layout(narrow, wide, part, tuple(waves), sum(tiles_of),
                   tuple(max_pieces), splits, mpt, num_seqs * Hkv if cascade else 0, wide_nt,
-                  tuple(part_cost))
+                  tuple(part_cost), span_shared if spans else 0)
 
 
 @dataclass
@@ -204,15 +208,25 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
     for td in tiles:
         tp.append(tp[-1] + td.nb)
 
+    def cost_of(st):
+        t_lo, t_hi = t_first[st], t_first[st + 1]
+        c = 0 if lay.part_blocks > 0 else lay.part_cost[st]
+        return (tp[t_hi] - tp[t_lo]) + c * (t_hi - t_lo)
+
+    # the span stream runs beside the others on span_shared workgroups when
+    # they hold at least SPAN_SHARE_RATIO times its work
+    share = (lay.span_shared > 0 and lay.part_blocks <= 0 and cost_of(0) > 0
+             and cost_of(1) + cost_of(2) >= SPAN_SHARE_RATIO * cost_of(0))
     R, B, C, pieces = [], [], [], []
     for st in STREAMS:
         t_lo, t_hi = t_first[st], t_first[st + 1]
         b = tp[t_hi] - tp[t_lo]
         c = 0 if lay.part_blocks > 0 else lay.part_cost[st]
-        bc = b + c * (t_hi - t_lo)
+        bc = cost_of(st)
+        waves = lay.span_shared if (share and st == 0) else lay.waves[st]
         r = lay.part_blocks
         if r <= 0:
-            r = max(cdiv(H * bc, max(lay.waves[st], 1)), min_blocks + c)
+            r = max(cdiv(H * bc, max(waves, 1)), min_blocks + c)
         K = cdiv(bc, r)
         kmax = lay.max_pieces[st] // H
         if kmax == 0:
@@ -410,7 +424,7 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
 
 
 def replay_workload(wl, *, waves, groups=None, partition_size=None, hybrid=None,
-                    part_cost=PART_COST):
+                    part_cost=PART_COST, span_shared=0):
     """Build and check the plan of a workload (``paged_kv_cache_213_amd.
     workloads``); returns (plan, layout, counts)."""
     G = wl.num_q_heads // wl.num_kv_heads
@@ -421,7 +435,8 @@ def replay_workload(wl, *, waves, groups=None, partition_size=None, hybrid=None,
                       max_context_len=wl.max_context_len,
                       max_query_len=wl.max_query_len if use_hybrid else 1,
                       decode=not use_hybrid, partition_size=P, cascade=groups is not None,
-                      waves=waves, f32=wl.kv_dtype == "f32", part_cost=part_cost)
+                      waves=waves, f32=wl.kv_dtype == "f32", part_cost=part_cost,
+                      span_shared=span_shared)
     plan = build_plan(lay, Hkv=wl.num_kv_heads, context_lens=wl.context_lens, qsl=qsl,
                       num_tokens=wl.num_tokens, max_context_len=wl.max_context_len, groups=groups)
     members = [int(i) for g in groups[0] for i in g] if groups is not None else []

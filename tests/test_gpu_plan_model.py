@@ -56,7 +56,8 @@ def _compare(wl, groups, P):
                          max_query_len=wl.max_query_len if hybrid else 1, decode=not hybrid,
                          partition_size=P, cascade=groups is not None,
                          waves=tuple(info.waves), wide_nt=info.wide_row_tiles,
-                         f32=wl.kv_dtype == "f32", part_cost=tuple(info.part_cost))
+                         f32=wl.kv_dtype == "f32", part_cost=tuple(info.part_cost),
+                         span_shared=info.span_shared)
     qsl = np.asarray(wl.query_start_loc) if hybrid else None
     plan = PM.build_plan(lay, Hkv=wl.num_kv_heads, context_lens=wl.context_lens, qsl=qsl,
                          num_tokens=wl.num_tokens, max_context_len=wl.max_context_len,

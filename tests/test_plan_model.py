@@ -65,6 +65,47 @@ def test_random_hybrid_batches(seed):
     PM.replay_workload(wl, waves=(512, 1024, 1024))
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_random_hybrid_batches_with_shared_spans(seed):
+    """With the span launch beside the narrow ones (span_shared workgroups),
+    the replay's checks still hold; the span stream gets span_shared
+    pieces per call exactly where the others hold twice its work."""
+    wl = _random_batch(seed)
+    plan, lay, _ = PM.replay_workload(wl, waves=(512, 1024, 1024), span_shared=256,
+                                      partition_size=0)
+    PM.replay_workload(wl, waves=(37, 13, 29), span_shared=11, partition_size=0)
+    plan0, _, _ = PM.replay_workload(wl, waves=(512, 1024, 1024), partition_size=0)
+    assert len(plan.pieces[1]) == len(plan0.pieces[1])
+    assert len(plan.pieces[2]) == len(plan0.pieces[2])
+    assert len(plan.pieces[0]) <= len(plan0.pieces[0])
+
+
+def test_hybrid_batch_shares_the_device_only_when_decodes_dominate():
+    """The 512-token chunk beside 128 decodes (decodes hold 8x the span's
+    work) is cut for one span workgroup per compute unit; the same chunk
+    alone, and the chunk with named 512-token partitions, keep the span
+    kernel's whole residency (or the partition size)."""
+    wl = W.make_config("c4")
+    H = wl.num_kv_heads
+    shared, _, _ = PM.replay_workload(wl, waves=(512, 1024, 1024), span_shared=256,
+                                      partition_size=0)
+    alone, _, _ = PM.replay_workload(wl, waves=(512, 1024, 1024), partition_size=0)
+    assert len(shared.pieces[0]) <= 256 < len(alone.pieces[0]) <= 512
+    assert len(shared.pieces[0]) % H == 0
+    # only the chunk: no single-token work, the span stream keeps 512
+    chunk = W.custom_workload([4096], num_q_heads=wl.num_q_heads, num_kv_heads=H,
+                              head_dim=wl.head_dim, q_dtype="bf16", kv_dtype="bf16", seed=5,
+                              query_lens=[512])
+    a, _, _ = PM.replay_workload(chunk, waves=(512, 1024, 1024), span_shared=256,
+                                 partition_size=0)
+    b, _, _ = PM.replay_workload(chunk, waves=(512, 1024, 1024), partition_size=0)
+    assert [p[:4] for p in a.pieces[0]] == [p[:4] for p in b.pieces[0]]
+    # fixed partitions: pieces of P / 16 blocks either way
+    a, _, _ = PM.replay_workload(wl, waves=(512, 1024, 1024), span_shared=256, partition_size=512)
+    b, _, _ = PM.replay_workload(wl, waves=(512, 1024, 1024), partition_size=512)
+    assert [p[:4] for p in a.pieces[0]] == [p[:4] for p in b.pieces[0]]
+
+
 @pytest.mark.parametrize("cost", [(0, 0, 0), (1, 3, 2), (12, 7, 40)])
 @pytest.mark.parametrize("seed", range(6))
 def test_part_costs(seed, cost):
@@ -142,13 +183,15 @@ def test_model_layout_equals_the_librarys(name, P, grouped):
                          max_context_len=wl.max_context_len,
                          max_query_len=wl.max_query_len if hybrid else 1, decode=not hybrid,
                          partition_size=P, cascade=grouped, waves=tuple(info.waves),
-                         wide_nt=info.wide_row_tiles, f32=wl.kv_dtype == "f32")
+                         wide_nt=info.wide_row_tiles, f32=wl.kv_dtype == "f32",
+                         span_shared=info.span_shared)
     assert (lay.narrow_tokens, lay.wide_tokens, lay.part_blocks, lay.members_per_tile) == (
         info.narrow_tokens, info.wide_tokens, info.part_blocks, info.members_per_tile)
     assert lay.max_tiles == info.max_tiles and lay.max_splits == info.max_splits
     assert lay.max_pieces == tuple(info.max_pieces)
     assert lay.max_cas_recs == info.max_cas_recs
     assert lay.part_cost == tuple(info.part_cost)
+    assert lay.span_shared == info.span_shared
     mq = wl.max_query_len if hybrid else 1
     assert info.total <= pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens,
                                             wl.max_context_len, mq)
