@@ -487,8 +487,9 @@ def main():
     att_mean = float(att_ms.mean())
     # the roofline counts what the method must read: the logical bytes, or
     # with cascade the group prefixes once per group tile
-    G = wl.num_q_heads // wl.num_kv_heads
-    mpt = max(1, 16 // G)  # members per group tile: one 16-row tile of G heads each
+    # members per group tile, as the library's layout gives them
+    mpt = pa.workspace_layout(shape, wl.num_seqs, wl.num_tokens, wl.max_context_len, mq,
+                              decode=wl.is_decode).members_per_tile
     read_bytes = cascade_read_bytes(wl, mpt) if use_cascade else kv_bytes
     achieved = read_bytes / (att_mean / 1e3) / 1e9
     layer_ms = ms_per_step / layers

@@ -211,7 +211,8 @@ int pa_plan(const pa_shape* shape, const int32_t* context_lens, const int32_t* q
  * that hit the same cached prompt -- through copy-on-write ("03 -- Engines
  * Papers", section 2). Cascade attention (same page, section 12): each
  * group's prefix is read once for all of its members, in tiles of up to
- * max(16 / G, 1) members, and each member reads only the
+ * max(32 / G, 1) members (two 16-row matrix-core tiles of G heads per
+ * member), and each member reads only the
  * blocks after the prefix; the run's merge pass combines the two parts of
  * every member by log-sum-exp. The outputs are the same attention as
  * without groups, up to rounding.
@@ -366,6 +367,8 @@ typedef struct pa_layout_info {
     int32_t span_shared;       /* span workgroups when the span launch runs
                                   beside the narrow and group launches (one
                                   per compute unit; 0: never) */
+    int32_t group_row_tiles;   /* 16-row tiles of a group tile and of a
+                                  group-stream slot */
     int64_t max_tiles, max_pieces[3], max_splits, max_cas_recs;
     int64_t off_tiles, off_splits, off_tree, off_cas_seq, off_cas_recs;
     int64_t off_cas_lse[2], off_cas_o[2];
@@ -388,7 +391,8 @@ const char* pa_status_string(int status);
  * pa_paged_attn_run_append, pa_paged_attn_partial_append and
  * pa_paged_attn_decode_append; 209 runs a batch's span launch beside its
  * narrow and group launches (a second stream of the library's) and gave
- * pa_layout_info span_shared. */
+ * pa_layout_info span_shared; 210 gave shared-prefix group tiles two
+ * 16-row tiles (pa_layout_info.group_row_tiles). */
 int pa_version(void);
 
 #ifdef __cplusplus

@@ -61,6 +61,7 @@ class PaLayoutInfo(ctypes.Structure):
         ("header_words", ctypes.c_int32),
         ("part_cost", ctypes.c_int32 * 3),
         ("span_shared", ctypes.c_int32),
+        ("group_row_tiles", ctypes.c_int32),
         ("max_tiles", ctypes.c_int64),
         ("max_pieces", ctypes.c_int64 * 3),
         ("max_splits", ctypes.c_int64),

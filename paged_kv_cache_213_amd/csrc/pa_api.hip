@@ -127,7 +127,7 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     if (spans && PA_SIDE_STREAM) l.span_shared = pa::span_shared_groups(kernel_kind(s), s->head_dim);
     l.cascade = s->cascade != 0;
     // a group tile holds the single query tokens of up to 16 / G members
-    l.members_per_tile = 16 / G > 1 ? 16 / G : 1;
+    l.members_per_tile = 16 * pa::kGroupRowTiles / G > 1 ? 16 * pa::kGroupRowTiles / G : 1;
     // (spans are disjoint, so no stream has more tiles than query tokens)
     const int64_t T = num_tokens;
     const int64_t tiles_of[pa::NUM_STREAMS] = {
@@ -181,7 +181,7 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
         }
     }
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
-        const int nt = st == pa::STREAM_WIDE ? pa::kSpanRowTiles : 1;
+        const int nt = pa::slot_row_tiles(st);
         const size_t slots = (size_t)l.max_pieces[st] * 2;
         l.off_pieces[st] = off;
         off = align_up(off + sizeof(pa::PieceStart) * (size_t)l.max_pieces[st]);
@@ -260,7 +260,8 @@ int plan_impl(const pa_shape* s, const int32_t* context_lens, const int32_t* qsl
     pl.wide_tokens = l.wide_tokens;
     pl.num_kv_heads = s->num_kv_heads;
     pl.part_blocks = l.part_blocks;
-    pl.min_blocks = pa::kMinPieceBlocks;
+    for (int st = 0; st < pa::NUM_STREAMS; ++st)
+        pl.min_blocks[st] = st == pa::STREAM_GROUP ? pa::kGroupMinPieceBlocks : pa::kMinPieceBlocks;
     pl.span_shared = l.span_shared;
     pl.max_tiles = (int32_t)l.max_tiles;
     pl.tiles = (pa::TileDesc*)(ws + l.off_tiles);
@@ -764,6 +765,7 @@ int pa_workspace_layout(const pa_shape* shape, int num_seqs, int num_q_tokens,
     r.part_blocks = l.part_blocks;
     r.members_per_tile = l.members_per_tile;
     r.wide_row_tiles = pa::kSpanRowTiles;
+    r.group_row_tiles = pa::kGroupRowTiles;
     r.header_words = pa::HDR_WORDS;
     r.max_tiles = l.max_tiles;
     r.max_splits = l.max_splits;
@@ -795,6 +797,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 209; }
+int pa_version(void) { return 210; }
 
 }  // extern "C"

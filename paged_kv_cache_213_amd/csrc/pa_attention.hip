@@ -605,7 +605,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         int64_t R = a.part_blocks;
         if (R <= 0) {
             R = ((int64_t)H * Bc + waves - 1) / max(waves, 1);
-            R = max(R, (int64_t)a.min_blocks + c);
+            R = max(R, (int64_t)a.min_blocks[st] + c);
         }
         int64_t K = (Bc + R - 1) / R;  // pieces per substream
         const int64_t kmax = a.max_pieces[st] / H;
@@ -852,17 +852,17 @@ struct NewStage {
 
 // Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
 // each block through the block table, S = K q^T on the matrix cores, online
-// softmax in registers, O += V^T P, for one 16-row tile of query rows (the
-// G heads of up to 16 / G query tokens) that share every K/V block the wave
-// loads. Then either write the rows' output (the wave saw the whole
-// segment) or write a partial result into the piece's slot for the merge
-// pass.
-template <int kv, int D, bool kStreamLoads>
+// softmax in registers, O += V^T P, for NR 16-row tiles of query rows (the
+// G heads of up to 16 NR / G query tokens, or of a group tile's members)
+// that share every K/V block the wave loads. Then either write the rows'
+// output (the wave saw the whole segment) or write a partial result into
+// the piece's slot (NR row tiles) for the merge pass.
+template <int kv, int D, bool kStreamLoads, int NR>
 __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td, const int kvh,
                                             const int j, const int take, const int piece,
                                             NewStage<kv, D>& stage) {
     using T = Tile<kv, D>;
-    constexpr int NT = 1, NR = 1;  // row tiles of a slot, and holding rows
+    constexpr int NT = NR;  // row tiles of a slot: those the wave holds
     constexpr bool kFp8Cache = kv == KV_FP8 || kv == KV_FP8Q;
     using QReg = typename std::conditional<
         kv == KV_F32, float[D / 4],
@@ -1229,8 +1229,8 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 }
 
 // One wave per workgroup; wave w streams pieces w, w + grid, ... of the
-// narrow stream.
-template <int kv, int D>
+// narrow stream (NR = 1) or of the group stream (NR = kGroupRowTiles).
+template <int kv, int D, int NR>
 __device__ __forceinline__ void attention_body(const AttnArgs& a) {
     const int* h = a.hdr + HDR_STREAM + 4 * a.stream;
     const int V = h[HDR_NPIECES];
@@ -1257,9 +1257,9 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
             // a decode's context and a cascade member's suffix are read by no
             // other tile of the call, so they are streamed past the caches
             if (PA_GROUP_L2 && td.flags == TILE_GROUP)
-                run_segment<kv, D, false>(a, td, kvh, j, take, v, stage);
+                run_segment<kv, D, false, NR>(a, td, kvh, j, take, v, stage);
             else
-                run_segment<kv, D, PA_NT_LOADS != 0>(a, td, kvh, j, take, v, stage);
+                run_segment<kv, D, PA_NT_LOADS != 0, NR>(a, td, kvh, j, take, v, stage);
             left -= take;
             j = 0;
             ++t;
@@ -1279,9 +1279,9 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
 #else
 #define PA_NARROW_OCCUPANCY
 #endif
-template <int kv, int D>
+template <int kv, int D, int NR>
 __global__ __launch_bounds__(64) PA_NARROW_OCCUPANCY void attention_narrow(AttnArgs a) {
-    attention_body<kv, D>(a);
+    attention_body<kv, D, NR>(a);
 }
 
 // ---- merge -------------------------------------------------------------------
@@ -1362,9 +1362,10 @@ __device__ __forceinline__ void merge_cascade(const MergeArgs& a, const CascadeR
             acc.add(a.cas_lse[kind][row], x);
             continue;
         }
-        // group tiles and suffix tiles hold one 16-row tile per slot
+        // group tiles hold kGroupRowTiles 16-row tiles per slot, suffix
+        // tiles one
         const int st = kind == CAS_PRE ? STREAM_GROUP : STREAM_NARROW;
-        const int nt = 1;
+        const int nt = slot_row_tiles(st);
         const int rr = (kind == CAS_PRE ? rc.pre_pos * G : 0) + n;  // row in the slot
         const float4* po = (const float4*)a.part_o[st];
         // four pieces per round trip: all their loads are issued first
@@ -1403,7 +1404,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int lane = threadIdx.x & 63;
     const int n = lane & 15, g = lane >> 4;  // the attention kernel's layout
     const int G = a.group;
-    const int nt = sp.stream == STREAM_WIDE ? a.wide_nt : 1;  // row tiles per slot
+    const int nt = slot_row_tiles(sp.stream);  // row tiles per slot
     const float* part_lse = a.part_lse[sp.stream];
     const float4* part_o = (const float4*)a.part_o[sp.stream];
     const int Hkv = a.num_kv_heads;
@@ -1525,7 +1526,7 @@ int resident_waves_d() {
         const int c = slot->load(std::memory_order_acquire);
         if (c > 0) return c;
     }
-    const int w = resident_waves_of(attention_narrow<kv, D>, PA_NARROW_MAX_WAVES);
+    const int w = resident_waves_of(attention_narrow<kv, D, 1>, PA_NARROW_MAX_WAVES);
     if (w <= 0) return 0;
     if (!slot) return w;
     int expected = 0;
@@ -1539,7 +1540,11 @@ hipError_t launch_narrow_d(const AttnArgs& a, int64_t max_pieces, hipStream_t s)
     if (grid <= 0) return hipErrorInvalidDevice;
     if (max_pieces < grid) grid = max_pieces;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((attention_narrow<kv, D>), dim3((unsigned)grid), dim3(64), 0, s, a);
+    if (a.stream == STREAM_GROUP)
+        hipLaunchKernelGGL((attention_narrow<kv, D, kGroupRowTiles>), dim3((unsigned)grid),
+                           dim3(64), 0, s, a);
+    else
+        hipLaunchKernelGGL((attention_narrow<kv, D, 1>), dim3((unsigned)grid), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

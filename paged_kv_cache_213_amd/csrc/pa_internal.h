@@ -77,6 +77,19 @@ constexpr int kSpanRowTiles = kSpanRows / 16;  // 16-row tiles of a wide tile (a
 #endif
 constexpr int kSpanWaves = PA_SPAN_WAVES;      // waves of a span workgroup
 static_assert(kSpanWaves == 4 || kSpanWaves == 8, "two or one row tiles per wave");
+// 16-row tiles of a shared-prefix group tile (and of the group stream's
+// partial slots): a group tile holds the single query tokens of
+// 16 * kGroupRowTiles / G members, and each of its waves reads the group's
+// prefix blocks once for all of them.
+#ifndef PA_GROUP_ROW_TILES
+#define PA_GROUP_ROW_TILES 2
+#endif
+constexpr int kGroupRowTiles = PA_GROUP_ROW_TILES;
+static_assert(kGroupRowTiles == 1 || kGroupRowTiles == 2, "one or two row tiles per group tile");
+// row tiles of a partial slot of stream st
+constexpr int slot_row_tiles(int st) {
+    return st == STREAM_WIDE ? kSpanRowTiles : st == STREAM_GROUP ? kGroupRowTiles : 1;
+}
 // Kernel kinds: the cache dtype, or an fp8 cache whose S = K q^T runs on
 // the fp8 matrix cores (pa_shape.fp8_qk).
 constexpr int KIND_FP8_QK = 3;
@@ -139,7 +152,7 @@ struct PlanArgs {
     // span stream always gets waves[STREAM_WIDE]); used when the single-token
     // streams' work is at least kSpanShareRatio times the span stream's
     int32_t span_shared;
-    int32_t min_blocks;          // smallest piece when balancing
+    int32_t min_blocks[NUM_STREAMS];  // smallest piece of each stream when balancing
     int32_t max_tiles;
     int64_t max_pieces[NUM_STREAMS];
     TileDesc* tiles;
@@ -283,6 +296,14 @@ constexpr int kSpanShareRatio = 2;
 #define PA_MIN_PIECE_BLOCKS 1
 #endif
 constexpr int kMinPieceBlocks = PA_MIN_PIECE_BLOCKS;
+// Smallest piece of the group stream when balancing. A piece that cuts a
+// group tile writes its 16 kGroupRowTiles rows of partial results (16 KB at
+// D = 128 with two row tiles) per cut, as much as two bf16 blocks of K and
+// V; shorter pieces would write more than they read.
+#ifndef PA_GROUP_MIN_PIECE_BLOCKS
+#define PA_GROUP_MIN_PIECE_BLOCKS 8
+#endif
+constexpr int kGroupMinPieceBlocks = PA_GROUP_MIN_PIECE_BLOCKS;
 
 }  // namespace pa
 

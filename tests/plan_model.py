@@ -69,6 +69,7 @@ class Layout:
     wide_nt: int
     part_cost: tuple
     span_shared: int = 0  # span workgroups beside the narrow launches (0: never)
+    group_nt: int = 2  # 16-row tiles of a group tile and of a group-stream slot
 
 
 SPAN_ROWS = 128  # query rows of a wide tile (four waves of 32)
@@ -78,11 +79,15 @@ PART_COST = (6, 0, 0)
 # the span stream is cut for span_shared workgroups when the other streams'
 # balanced cost is at least this many times its own
 SPAN_SHARE_RATIO = 2
+# 16-row tiles of a shared-prefix group tile (and of the group stream's slots)
+GROUP_NT = 2
+# smallest group-stream piece when balancing (blocks)
+GROUP_MIN_BLOCKS = 8
 
 
 def make_layout(*, G, Hkv, num_seqs, num_tokens, max_context_len, max_query_len, decode,
                 partition_size, cascade, waves, wide_nt=SPAN_ROWS // 16, f32=False,
-                part_cost=PART_COST, span_shared=0):
+                part_cost=PART_COST, span_shared=0, group_nt=None):
     """Workspace bounds of a batch, as the host sizes them."""
     narrow = 1 if decode else max(16 // G, 1)
     wide = max(SPAN_ROWS // G, 1)
@@ -90,7 +95,8 @@ def make_layout(*, G, Hkv, num_seqs, num_tokens, max_context_len, max_query_len,
     spans = (not decode) and max_query_len > narrow and not f32
     if not spans:
         wide = 0
-    mpt = max(16 // G, 1)
+    group_nt = GROUP_NT if group_nt is None else group_nt
+    mpt = max(16 * group_nt // G, 1)
     T = num_tokens
     tiles_of = [min(num_seqs + cdiv(num_tokens, wide), T) if spans else 0,
                 num_seqs if (spans or decode) else min(num_seqs + cdiv(num_tokens, narrow), T),
@@ -105,7 +111,7 @@ def make_layout(*, G, Hkv, num_seqs, num_tokens, max_context_len, max_query_len,
             splits += min(mp - Hkv, tiles_of[st] * Hkv)
     return Layout(narrow, wide, part, tuple(waves), sum(tiles_of),
                   tuple(max_pieces), splits, mpt, num_seqs * Hkv if cascade else 0, wide_nt,
-                  tuple(part_cost), span_shared if spans else 0)
+                  tuple(part_cost), span_shared if spans else 0, group_nt)
 
 
 @dataclass
@@ -125,7 +131,7 @@ class Plan:
 
 
 def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_len,
-               groups=None, min_blocks=1):
+               groups=None, min_blocks=(1, 1, GROUP_MIN_BLOCKS)):
     """The device plan's records for a batch. groups: (list of member
     lists, prefix blocks per group) or None."""
     S = len(context_lens)
@@ -226,7 +232,7 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
         waves = lay.span_shared if (share and st == 0) else lay.waves[st]
         r = lay.part_blocks
         if r <= 0:
-            r = max(cdiv(H * bc, max(waves, 1)), min_blocks + c)
+            r = max(cdiv(H * bc, max(waves, 1)), min_blocks[st] + c)
         K = cdiv(bc, r)
         kmax = lay.max_pieces[st] // H
         if kmax == 0:
@@ -286,6 +292,11 @@ def build_plan(lay: Layout, *, Hkv, context_lens, qsl, num_tokens, max_context_l
                 cas_pos, tp)
 
 
+def slot_nt(lay, st):
+    """16-row tiles of a partial slot (and held by a wave) in stream st."""
+    return lay.wide_nt if st == STREAM_WIDE else lay.group_nt if st == STREAM_GROUP else 1
+
+
 def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, group_members):
     """Replay the attention pass and the merge over the plan; assert the
     properties listed in the module docstring. Returns counts of what was
@@ -325,7 +336,7 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
         return res
 
     for st in STREAMS:
-        NT = lay.wide_nt if st == STREAM_WIDE else 1
+        NT = slot_nt(lay, st)
         max_slots = 2 * lay.max_pieces[st]
         assert len(plan.pieces[st]) <= lay.max_pieces[st], "pieces past their region"
         # the pieces of each head's substream cover its B blocks once, in order
@@ -367,7 +378,7 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
     # merge of cut segments
     n_read = 0
     for (row0, ntok, kvh, k0, k1, st) in plan.splits:
-        nt = lay.wide_nt if st == STREAM_WIDE else 1
+        nt = slot_nt(lay, st)
         for r in range(nt):
             for n in range(16):
                 rr = 16 * r + n
@@ -395,7 +406,7 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
                     n_read += 1
                     continue
                 st = STREAM_GROUP if kind == CAS_PRE else STREAM_NARROW
-                nt = 1
+                nt = slot_nt(lay, st)
                 rr = (pos * G if kind == CAS_PRE else 0) + n
                 for k in range(k0, k1 + 1):
                     slot = (k * Hkv + kvh) * 2 + (SLOT_TAIL if k == k0 else SLOT_HEAD)
@@ -424,7 +435,7 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
 
 
 def replay_workload(wl, *, waves, groups=None, partition_size=None, hybrid=None,
-                    part_cost=PART_COST, span_shared=0):
+                    part_cost=PART_COST, span_shared=0, group_nt=None):
     """Build and check the plan of a workload (``paged_kv_cache_213_amd.
     workloads``); returns (plan, layout, counts)."""
     G = wl.num_q_heads // wl.num_kv_heads
@@ -436,7 +447,7 @@ def replay_workload(wl, *, waves, groups=None, partition_size=None, hybrid=None,
                       max_query_len=wl.max_query_len if use_hybrid else 1,
                       decode=not use_hybrid, partition_size=P, cascade=groups is not None,
                       waves=waves, f32=wl.kv_dtype == "f32", part_cost=part_cost,
-                      span_shared=span_shared)
+                      span_shared=span_shared, group_nt=group_nt)
     plan = build_plan(lay, Hkv=wl.num_kv_heads, context_lens=wl.context_lens, qsl=qsl,
                       num_tokens=wl.num_tokens, max_context_len=wl.max_context_len, groups=groups)
     members = [int(i) for g in groups[0] for i in g] if groups is not None else []

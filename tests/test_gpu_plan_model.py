@@ -57,7 +57,7 @@ def _compare(wl, groups, P):
                          partition_size=P, cascade=groups is not None,
                          waves=tuple(info.waves), wide_nt=info.wide_row_tiles,
                          f32=wl.kv_dtype == "f32", part_cost=tuple(info.part_cost),
-                         span_shared=info.span_shared)
+                         span_shared=info.span_shared, group_nt=info.group_row_tiles)
     qsl = np.asarray(wl.query_start_loc) if hybrid else None
     plan = PM.build_plan(lay, Hkv=wl.num_kv_heads, context_lens=wl.context_lens, qsl=qsl,
                          num_tokens=wl.num_tokens, max_context_len=wl.max_context_len,

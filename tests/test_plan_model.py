@@ -184,7 +184,7 @@ def test_model_layout_equals_the_librarys(name, P, grouped):
                          max_query_len=wl.max_query_len if hybrid else 1, decode=not hybrid,
                          partition_size=P, cascade=grouped, waves=tuple(info.waves),
                          wide_nt=info.wide_row_tiles, f32=wl.kv_dtype == "f32",
-                         span_shared=info.span_shared)
+                         span_shared=info.span_shared, group_nt=info.group_row_tiles)
     assert (lay.narrow_tokens, lay.wide_tokens, lay.part_blocks, lay.members_per_tile) == (
         info.narrow_tokens, info.wide_tokens, info.part_blocks, info.members_per_tile)
     assert lay.max_tiles == info.max_tiles and lay.max_splits == info.max_splits
