@@ -182,7 +182,7 @@ def attention_source_sha256() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(config: str, cascade: bool, fp8_qk: bool = False):
+def recorded_traffic(config: str, cascade: bool, fp8_qk: bool = False, partition_size: int = 0):
     """HBM bytes per attention launch recorded by the profiler counters for
     this workload and method (profiles/), or None when none are recorded or
     the attention source has changed since they were taken."""
@@ -195,13 +195,15 @@ def recorded_traffic(config: str, cascade: bool, fp8_qk: bool = False):
         for line in fh:
             k, sep, v = line.partition(":")
             if sep and k in ("traffic_bytes_per_launch", "attention_source_sha256", "cascade",
-                             "fp8_qk"):
+                             "fp8_qk", "partition_size"):
                 fields[k] = v.strip()
     if fields.get("attention_source_sha256") != attention_source_sha256():
         return None
     if fields.get("cascade", "off") != ("on" if cascade else "off"):
         return None
     if fields.get("fp8_qk", "off") != ("on" if fp8_qk else "off"):
+        return None
+    if fields.get("partition_size", "0") != str(int(partition_size)):
         return None
     t = fields.get("traffic_bytes_per_launch")
     return int(t) if t and t.isdigit() else None
@@ -536,7 +538,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": recorded_traffic(wl.name, use_cascade, args.fp8_qk),
+            "traffic": recorded_traffic(wl.name, use_cascade, args.fp8_qk, P),
             "traffic_note": "HBM bytes per attention pass launch (calibrated FETCH_SIZE + "
                             "WRITE_SIZE, profiles/); null if not recorded for the current "
                             "attention source",
