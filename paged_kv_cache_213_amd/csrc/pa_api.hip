@@ -44,6 +44,11 @@ static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES]
 #ifndef PA_SIDE_STREAM
 #define PA_SIDE_STREAM 1
 #endif
+// A decode batch with shared-prefix groups runs its group and narrow streams
+// in one launch (1) or in one launch each (0).
+#ifndef PA_NARROW_PAIR
+#define PA_NARROW_PAIR 1
+#endif
 
 namespace {
 
@@ -405,7 +410,28 @@ int run_impl(const pa_shape* s, void* out, float* lse, const void* q, const void
                 return PA_EHIP;
         }
         bool failed = false;
-        for (int st = 0; st < pa::NUM_STREAMS && !failed; ++st) {
+        // no spans, group and narrow pieces: one launch for both streams
+        const bool pair = PA_NARROW_PAIR && l.max_pieces[pa::STREAM_WIDE] == 0 &&
+                          l.max_pieces[pa::STREAM_NARROW] > 0 &&
+                          l.max_pieces[pa::STREAM_GROUP] > 0;
+        if (pair) {
+            pa::AttnArgs ga = aa, na = aa;
+            ga.stream = pa::STREAM_GROUP;
+            na.stream = pa::STREAM_NARROW;
+            for (pa::AttnArgs* x : {&ga, &na}) {
+                x->pieces = (const pa::PieceStart*)(ws + l.off_pieces[x->stream]);
+                x->part_lse = (float*)(ws + l.off_lse[x->stream]);
+                x->part_o = (float*)(ws + l.off_o[x->stream]);
+            }
+            ga.k_new = ga.v_new = nullptr;
+            na.k_new = k_new;
+            na.v_new = v_new;
+            failed = pa::launch_narrow_pair(
+                         kernel_kind(s), s->head_dim, ga, na,
+                         std::max(l.max_pieces[pa::STREAM_GROUP], l.max_pieces[pa::STREAM_NARROW]),
+                         hs) != hipSuccess;
+        }
+        for (int st = 0; st < pa::NUM_STREAMS && !failed && !pair; ++st) {
             if (l.max_pieces[st] == 0) continue;
             aa.stream = st;
             aa.pieces = (const pa::PieceStart*)(ws + l.off_pieces[st]);

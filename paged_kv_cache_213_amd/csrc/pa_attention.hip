@@ -1231,21 +1231,9 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 // One wave per workgroup; wave w streams pieces w, w + grid, ... of the
 // narrow stream (NR = 1) or of the group stream (NR = kGroupRowTiles).
 template <int kv, int D, int NR>
-__device__ __forceinline__ void attention_body(const AttnArgs& a) {
+__device__ __forceinline__ void narrow_pieces(const AttnArgs& a, NewStage<kv, D>& stage) {
     const int* h = a.hdr + HDR_STREAM + 4 * a.stream;
     const int V = h[HDR_NPIECES];
-    // decode with append: the new keys' cache writes, staged until the end
-    using E = typename NewStage<kv, D>::E;
-    constexpr int kMax = NewStage<kv, D>::kMax;
-    __shared__ __align__(16) E s_new_k[kMax * D];
-    __shared__ __align__(16) E s_new_v[kMax * D];
-    __shared__ int64_t s_new_bh[kMax];
-    __shared__ int s_new_o[kMax];
-    NewStage<kv, D> stage;
-    stage.k = s_new_k;
-    stage.v = s_new_v;
-    stage.bh = s_new_bh;
-    stage.o = s_new_o;
     for (int v = blockIdx.x; v < V; v += gridDim.x) {
         const PieceStart ps = a.pieces[v];
         int t = ps.tile, j = ps.j;
@@ -1266,8 +1254,21 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
             if (left > 0) td = a.tiles[t];
         }
     }
-    stage.flush(a, threadIdx.x & 63);
 }
+
+// LDS stage of the new keys a wave appends (decode with append).
+#define PA_NEW_STAGE(kv, D, stage)                                       \
+    using E_ = typename NewStage<kv, D>::E;                              \
+    constexpr int kMax_ = NewStage<kv, D>::kMax;                         \
+    __shared__ __align__(16) E_ s_new_k[kMax_ * D];                      \
+    __shared__ __align__(16) E_ s_new_v[kMax_ * D];                      \
+    __shared__ int64_t s_new_bh[kMax_];                                  \
+    __shared__ int s_new_o[kMax_];                                       \
+    NewStage<kv, D> stage;                                               \
+    stage.k = s_new_k;                                                   \
+    stage.v = s_new_v;                                                   \
+    stage.bh = s_new_bh;                                                 \
+    stage.o = s_new_o
 
 // Single-token tiles: bound by HBM. PA_NARROW_MIN_WAVES > 0 would make the
 // compiler budget registers for that many waves per SIMD.
@@ -1279,9 +1280,27 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
 #else
 #define PA_NARROW_OCCUPANCY
 #endif
+
+// One wave per workgroup; wave w takes pieces w, w + grid, ... of a.stream:
+// the narrow stream (NR = 1) or the group stream (NR = kGroupRowTiles).
 template <int kv, int D, int NR>
 __global__ __launch_bounds__(64) PA_NARROW_OCCUPANCY void attention_narrow(AttnArgs a) {
-    attention_body<kv, D, NR>(a);
+    PA_NEW_STAGE(kv, D, stage);
+    narrow_pieces<kv, D, NR>(a, stage);
+    stage.flush(a, threadIdx.x & 63);  // decode with append: the staged cache writes
+}
+
+// A decode batch with shared-prefix groups: one launch in which each wave
+// takes its pieces of the group stream, then its pieces of the narrow
+// stream (the members' suffixes and the other decodes), rather than a
+// launch per stream. Both streams are cut for the same waves.
+template <int kv, int D>
+__global__ __launch_bounds__(64) PA_NARROW_OCCUPANCY void attention_narrow_pair(AttnArgs g,
+                                                                               AttnArgs n) {
+    PA_NEW_STAGE(kv, D, stage);
+    narrow_pieces<kv, D, kGroupRowTiles>(g, stage);
+    narrow_pieces<kv, D, 1>(n, stage);
+    stage.flush(n, threadIdx.x & 63);
 }
 
 // ---- merge -------------------------------------------------------------------
@@ -1548,7 +1567,33 @@ hipError_t launch_narrow_d(const AttnArgs& a, int64_t max_pieces, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int kv, int D>
+hipError_t launch_narrow_pair_d(const AttnArgs& g, const AttnArgs& n, int64_t max_pieces,
+                                hipStream_t s) {
+    int64_t grid = resident_waves_d<kv, D>();
+    if (grid <= 0) return hipErrorInvalidDevice;
+    if (max_pieces < grid) grid = max_pieces;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((attention_narrow_pair<kv, D>), dim3((unsigned)grid), dim3(64), 0, s, g, n);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_narrow_pair(int kind, int head_dim, const AttnArgs& g, const AttnArgs& n,
+                              int64_t max_pieces, hipStream_t s) {
+    switch (kind * 1000 + head_dim) {
+    case PA_F32 * 1000 + 64: return launch_narrow_pair_d<KV_F32, 64>(g, n, max_pieces, s);
+    case PA_F32 * 1000 + 128: return launch_narrow_pair_d<KV_F32, 128>(g, n, max_pieces, s);
+    case PA_BF16 * 1000 + 64: return launch_narrow_pair_d<KV_BF16, 64>(g, n, max_pieces, s);
+    case PA_BF16 * 1000 + 128: return launch_narrow_pair_d<KV_BF16, 128>(g, n, max_pieces, s);
+    case PA_FP8_E4M3FN * 1000 + 64: return launch_narrow_pair_d<KV_FP8, 64>(g, n, max_pieces, s);
+    case PA_FP8_E4M3FN * 1000 + 128: return launch_narrow_pair_d<KV_FP8, 128>(g, n, max_pieces, s);
+    case KIND_FP8_QK * 1000 + 64: return launch_narrow_pair_d<KV_FP8Q, 64>(g, n, max_pieces, s);
+    case KIND_FP8_QK * 1000 + 128: return launch_narrow_pair_d<KV_FP8Q, 128>(g, n, max_pieces, s);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 int resident_waves(int kind, int head_dim, int stream) {
     if (stream == STREAM_WIDE) return span_resident_groups(kind, head_dim);

@@ -270,6 +270,10 @@ hipError_t launch_span(int kind, int head_dim, const AttnArgs& a, int64_t max_pi
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_attention(int kind, int head_dim, const AttnArgs& a, int64_t max_pieces,
                             hipStream_t s);  // a.stream selects the wide or narrow kernel
+// The group stream (g) then the narrow stream (n) in one narrow launch
+// (decode batches with shared-prefix groups); max_pieces: the larger bound.
+hipError_t launch_narrow_pair(int kind, int head_dim, const AttnArgs& g, const AttnArgs& n,
+                              int64_t max_pieces, hipStream_t s);
 // Workgroups of the attention kernel of a stream that fit on the device at
 // once (narrow: waves; wide: span workgroups), or 0 if the device cannot be
 // queried.

@@ -142,3 +142,24 @@ def test_random_hybrid_batches_at_the_balanced_split(seed):
     post = H.oracle_append(wl, pre)
     ref, _ = oracle.run_workload(wl, post)
     H.assert_parity(out_f64(out), ref, H.tolerance_key(wl), f"random hybrid {seed}")
+
+
+@pytest.mark.parametrize("lens,qlens", [([4096], [512]), ([3000, 40, 100], [384, 1, 1]),
+                                        ([2048, 2048], [256, 256])])
+def test_span_heavy_batches(lens, qlens):
+    """Batches whose single-token work is below twice the span work (a
+    chunk alone, a chunk beside two short decodes, two chunks): the plan
+    keeps the span kernel's whole residency, the side stream still forks
+    and joins (its narrow launch has little or nothing to do); every row
+    against the oracle."""
+    wl = W.custom_workload(lens, qlens, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           q_dtype="bf16", kv_dtype="bf16", seed=len(lens) * 7 + qlens[0])
+    vals, pre = prepare(wl)
+    t = dev_tensors(wl, vals, pre)
+    pa.kv_append(t["k_cache"], t["v_cache"], t["k_new"], t["v_new"], t["slots"])
+    out, lse = _hybrid(wl, t)
+    torch.cuda.synchronize()
+    post = H.oracle_append(wl, pre)
+    ref, _ = oracle.run_workload(wl, post)
+    H.assert_parity(out_f64(out), ref, H.tolerance_key(wl), f"span-heavy {lens} {qlens}")
+    assert torch.isfinite(lse).all()
