@@ -850,6 +850,11 @@ struct NewStage {
     }
 };
 
+// An empty use of a register: the wait for its load is placed here (in
+// straight-line code, where the count of loads issued after it is known)
+// rather than at its first use inside a loop.
+__device__ __forceinline__ void take_reg(float x) { asm volatile("" ::"v"(x)); }
+
 // Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
 // each block through the block table, S = K q^T on the matrix cores, online
 // softmax in registers, O += V^T P, for NR 16-row tiles of query rows (the
@@ -1157,6 +1162,22 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 #pragma unroll
         for (int r = 0; r < PF; ++r)
             if (r < cnt) fetch(ring[r], r);
+        // The chunk's fp8 block scales, loaded before the ring's first
+        // blocks, are taken here, once. Left pending into the loop, their
+        // read in every block step waited for all the loads in flight behind
+        // them (the loop's entry and back edge disagree on how many follow
+        // them), draining the ring once per block. (The query operands,
+        // loaded at the segment's start, are left to the loop: their wait
+        // drains one block of the ring once per loop step, and the
+        // long-context batch measured faster with it than with the ring
+        // kept full.)
+        if constexpr (kFp8Cache) {
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                take_reg(my_ks_w[w]);
+                take_reg(my_vs_w[w]);
+            }
+        }
         int i0 = 0;
         for (; i0 + 2 * PF < cnt; i0 += PF + 1) {
 #pragma unroll
