@@ -850,11 +850,6 @@ struct NewStage {
     }
 };
 
-// An empty use of a register: the wait for its load is placed here (in
-// straight-line code, where the count of loads issued after it is known)
-// rather than at its first use inside a loop.
-__device__ __forceinline__ void take_reg(float x) { asm volatile("" ::"v"(x)); }
-
 // Blocks [j, j + take) of segment (tile td, KV head kvh), by one wave: gather
 // each block through the block table, S = K q^T on the matrix cores, online
 // softmax in registers, O += V^T P, for NR 16-row tiles of query rows (the

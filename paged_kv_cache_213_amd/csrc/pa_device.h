@@ -130,5 +130,12 @@ __device__ __forceinline__ float4 ld_kv(const float4* p) {
                        __uint_as_float(v.w));
 }
 
+// An empty use of a register: the wait for the load that wrote it is
+// placed here, in straight-line code where the count of loads issued after
+// it is known, rather than at a later use (a loop's head, or the join of
+// paths of which only some read it), where the compiler, unable to count,
+// waits for every load in flight.
+__device__ __forceinline__ void take_reg(float x) { asm volatile("" ::"v"(x)); }
+
 }  // namespace dev
 }  // namespace pa
