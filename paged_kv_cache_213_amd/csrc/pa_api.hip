@@ -22,12 +22,21 @@
 // starts by loading 128 query rows and ends by writing 128 output rows, some
 // six blocks' worth of K/V traffic; a narrow segment's setup hides under its
 // first loads (measured: a cost of 2 to 5 left the decode batches' times
-// unchanged or slower, while the span kernel gained 7% at 6).
+// unchanged or slower, while the span kernel gained 7% at 6). A group
+// tile's segment starts with a chain of dependent loads (its members'
+// entries, their query rows, the block ids, the first blocks and their
+// scales): timed per wave on the parallel-sampling batch, 5.9 us per segment
+// against 0.73 us per fp8 block, so about eight blocks. It is charged where
+// the group and narrow pieces share one launch (batches without spans),
+// whose end is its slowest wave's; beside a span launch it measured slower.
 #ifndef PA_PART_COST
 #define PA_PART_COST 0
 #endif
 #ifndef PA_PART_COST_WIDE
 #define PA_PART_COST_WIDE 6
+#endif
+#ifndef PA_PART_COST_GROUP
+#define PA_PART_COST_GROUP 8
 #endif
 
 // Scratch of pa_paged_attn_hybrid_noalloc, in static device memory: each
@@ -152,7 +161,9 @@ Layout make_layout(const pa_shape* s, int num_seqs, int num_tokens, int max_cont
     for (int st = 0; st < pa::NUM_STREAMS; ++st) {
         const int w = pa::resident_waves(kernel_kind(s), s->head_dim, st);
         l.waves[st] = w > 0 ? w : kWaveBound;
-        l.part_cost[st] = st == pa::STREAM_WIDE ? PA_PART_COST_WIDE : PA_PART_COST;
+        l.part_cost[st] = st == pa::STREAM_WIDE                ? PA_PART_COST_WIDE
+                          : st == pa::STREAM_GROUP && !spans ? PA_PART_COST_GROUP
+                                                              : PA_PART_COST;
         // pieces per KV head substream: ceil(B / R) with B <= tiles * blocks
         // per tile, and R = P / 16, or R >= Hkv * B / waves when balanced
         const int64_t H = s->num_kv_heads;

@@ -74,8 +74,9 @@ class Layout:
 
 SPAN_ROWS = 128  # query rows of a wide tile (four waves of 32)
 # when balancing, the cost of a segment's start in blocks of work, per stream
-# (wide, narrow, group)
+# (wide, narrow, group); the group stream's applies to batches without spans
 PART_COST = (6, 0, 0)
+GROUP_COST_NO_SPANS = 8
 # the span stream is cut for span_shared workgroups when the other streams'
 # balanced cost is at least this many times its own
 SPAN_SHARE_RATIO = 2
@@ -87,12 +88,16 @@ GROUP_MIN_BLOCKS = 8
 
 def make_layout(*, G, Hkv, num_seqs, num_tokens, max_context_len, max_query_len, decode,
                 partition_size, cascade, waves, wide_nt=SPAN_ROWS // 16, f32=False,
-                part_cost=PART_COST, span_shared=0, group_nt=None):
-    """Workspace bounds of a batch, as the host sizes them."""
+                part_cost=None, span_shared=0, group_nt=None):
+    """Workspace bounds of a batch, as the host sizes them (part_cost None:
+    the library's per-stream start costs)."""
     narrow = 1 if decode else max(16 // G, 1)
     wide = max(SPAN_ROWS // G, 1)
     part = partition_size // 16
     spans = (not decode) and max_query_len > narrow and not f32
+    if part_cost is None:
+        part_cost = (PART_COST[0], PART_COST[1],
+                     PART_COST[2] if spans else GROUP_COST_NO_SPANS)
     if not spans:
         wide = 0
     group_nt = GROUP_NT if group_nt is None else group_nt
@@ -435,7 +440,7 @@ def check_plan(plan: Plan, lay: Layout, *, G, Hkv, num_seqs, num_tokens, qsl, gr
 
 
 def replay_workload(wl, *, waves, groups=None, partition_size=None, hybrid=None,
-                    part_cost=PART_COST, span_shared=0, group_nt=None):
+                    part_cost=None, span_shared=0, group_nt=None):
     """Build and check the plan of a workload (``paged_kv_cache_213_amd.
     workloads``); returns (plan, layout, counts)."""
     G = wl.num_q_heads // wl.num_kv_heads

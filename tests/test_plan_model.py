@@ -195,3 +195,30 @@ def test_model_layout_equals_the_librarys(name, P, grouped):
     mq = wl.max_query_len if hybrid else 1
     assert info.total <= pa.workspace_bytes(shape, wl.num_seqs, wl.num_tokens,
                                             wl.max_context_len, mq)
+
+
+def test_group_start_cost_only_without_spans():
+    """A decode batch with groups charges each group segment's start eight
+    blocks of work, so group pieces that start more segments hold fewer
+    blocks; a hybrid batch (spans) charges none."""
+    wl = W.make_config("c5")
+    plan, lay, _ = PM.replay_workload(wl, waves=(512, 1024, 1024), groups=_groups(wl),
+                                      partition_size=0)
+    assert lay.part_cost == (6, 0, 8)
+    # segments each group piece touches, against its blocks
+    segs = {}
+    for k, (t, kvh, j, n) in enumerate(plan.pieces[2]):
+        tiles = [t]
+        left = n - min(n, plan.tiles[t].nb - j)
+        while left > 0:
+            t += 1
+            tiles.append(t)
+            left -= min(left, plan.tiles[t].nb)
+        segs.setdefault(len(tiles), []).append(n)
+    assert len(segs) > 1
+    ks = sorted(segs)
+    assert max(segs[ks[-1]]) < max(segs[ks[0]])
+    hyb = W.make_config("c4")
+    _, lay4, _ = PM.replay_workload(hyb, waves=(512, 1024, 1024), groups=_groups(hyb),
+                                    partition_size=0)
+    assert lay4.part_cost == (6, 0, 0)
