@@ -363,7 +363,8 @@ typedef struct pa_layout_info {
     int32_t wide_row_tiles;    /* 16-row tiles of a wide slot */
     int32_t header_words;      /* int32 words of the header */
     int32_t part_cost[3];      /* when balancing: a segment's start in blocks
-                                  of work, per stream */
+                                  of work, per stream (the group stream's is
+                                  nonzero only in batches without spans) */
     int32_t span_shared;       /* span workgroups when the span launch runs
                                   beside the narrow and group launches (one
                                   per compute unit; 0: never) */
@@ -392,7 +393,9 @@ const char* pa_status_string(int status);
  * pa_paged_attn_decode_append; 209 runs a batch's span launch beside its
  * narrow and group launches (a second stream of the library's) and gave
  * pa_layout_info span_shared; 210 gave shared-prefix group tiles two
- * 16-row tiles (pa_layout_info.group_row_tiles). */
+ * 16-row tiles (pa_layout_info.group_row_tiles); 211 charges each group
+ * segment a start cost when pieces are balanced in batches without spans
+ * (plans change, calls and results do not). */
 int pa_version(void);
 
 #ifdef __cplusplus

@@ -834,6 +834,6 @@ const char* pa_status_string(int status) {
     }
 }
 
-int pa_version(void) { return 210; }
+int pa_version(void) { return 211; }
 
 }  // extern "C"
