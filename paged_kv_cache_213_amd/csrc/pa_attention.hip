@@ -736,9 +736,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 // 64 times this many blocks. Measured (decode step with append, three
 // alternating runs each): 2 left the Llama-3-8B-shaped step unchanged within
 // its run-to-run spread and made the 256-sequence long-context step 4%
-// slower than 1.
+// slower than 1. An fp8 chunk carries half the bytes of a bf16 one for the
+// same drain and refill of the ring at its end: with 2, the fp8
+// parallel-sampling pass went from 114.9-118.1 to 112.1-112.9 us (the same
+// batch without its groups 369 -> 368 us); 4 gave no more.
 #ifndef PA_ID_WINDOWS
 #define PA_ID_WINDOWS 1
+#endif
+#ifndef PA_ID_WINDOWS_FP8
+#define PA_ID_WINDOWS_FP8 2
 #endif
 #ifndef PA_PREFETCH_FP8
 #define PA_PREFETCH_FP8 2
@@ -985,7 +991,7 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
     // blocks are taken in chunks of up to 64 NW, their ids (and fp8 scales)
     // held one per lane in NW registers; the ring drains at a chunk's end
     // and refills after the next chunk's ids arrive
-    constexpr int NW = PA_ID_WINDOWS;
+    constexpr int NW = kFp8Cache ? PA_ID_WINDOWS_FP8 : PA_ID_WINDOWS;
     for (int c0 = 0; c0 < take; c0 += 64 * NW) {
         const int cnt = min(64 * NW, take - c0);
         // ids outside the pool are clamped into it: a wrong table gives
