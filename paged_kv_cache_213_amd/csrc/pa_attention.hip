@@ -1184,6 +1184,12 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
 #pragma unroll
             for (int r = 0; r <= PF; ++r) {
                 fetch(ring[(r + PF) % (PF + 1)], i0 + r + PF);
+                // fp8: the refill is issued before the step waits for its
+                // block (the scheduler otherwise placed it after the wait
+                // for the block's K, so a wave stalled there had one block
+                // fewer in flight); the parallel-sampling pass measured
+                // 113-114 -> 111.7 us. The bf16 loop measured slower with it.
+                if constexpr (kFp8Cache) __builtin_amdgcn_sched_barrier(0);
                 consume(ring[r], i0 + r);
                 // keep the steps in order: the scheduler would otherwise hoist
                 // later steps' products above their loads' waits
