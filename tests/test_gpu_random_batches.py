@@ -48,10 +48,12 @@ def test_random_hybrid_batch(seed):
           f"P={wl.partition_size}: {e}", flush=True)
 
 
-def _random_sharing_batch(seed: int):
+def _random_sharing_batch(seed: int, decode: bool = False):
     """Random shared-prefix groups (copy-on-write sharing of whole leading
     blocks, "03 -- Engines Papers", section 2) next to unshared sequences;
-    members' own tokens lie past their group's prefix."""
+    members' own tokens lie past their group's prefix. decode: every
+    sequence carries one new token and pieces are balanced (no partition
+    size), the layout of a parallel-sampling decode step."""
     rng = np.random.default_rng(1000 + seed)
     G = int(rng.choice([1, 2, 4, 8, 16]))
     Hkv = int(rng.choice([1, 2]))
@@ -65,6 +67,7 @@ def _random_sharing_batch(seed: int):
         members = []
         for _ in range(int(rng.integers(2, 21))):
             n = 1 if rng.random() < 0.85 else int(rng.integers(2, 40))
+            n = 1 if decode else n
             L = 16 * pb + n + int(rng.integers(0, 600))
             members.append(len(lens))
             lens.append(L)
@@ -74,11 +77,12 @@ def _random_sharing_batch(seed: int):
     for _ in range(int(rng.integers(0, 8))):  # sequences outside every group
         L = int(rng.integers(1, 2000))
         lens.append(L)
-        ql.append(1 if rng.random() < 0.8 else int(rng.integers(1, min(L, 60) + 1)))
+        q1 = 1 if rng.random() < 0.8 else int(rng.integers(1, min(L, 60) + 1))
+        ql.append(1 if decode else q1)
     wl = W.custom_workload(np.array(lens, np.int32), np.array(ql, np.int32),
                            num_q_heads=G * Hkv, num_kv_heads=Hkv, head_dim=D, q_dtype=q_dtype,
-                           kv_dtype=kv_dtype, partition_size=P, seed=seed,
-                           name=f"random-sharing-{seed}")
+                           kv_dtype=kv_dtype, partition_size=0 if decode else P, seed=seed,
+                           name=f"random-sharing-{'decode-' if decode else ''}{seed}")
     for members, pb in zip(groups, prefix):
         lead = wl.block_tables[members[0], :pb].copy()
         for i in members:
@@ -93,6 +97,19 @@ def test_random_sharing_batch_cascade(seed):
     print(f"seed {seed}: S={wl.num_seqs} T={wl.num_tokens} Hq={wl.num_q_heads} "
           f"Hkv={wl.num_kv_heads} D={wl.head_dim} {wl.q_dtype}/{wl.kv_dtype} "
           f"P={wl.partition_size} groups={[len(g) for g in groups[0]]} "
+          f"prefix blocks={groups[1]}: {e}", flush=True)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_sharing_decode_batch_cascade(seed):
+    """The sharing batches as decode steps at the balanced split: the group
+    and decode pieces share one launch, and the plan charges each group
+    segment's start as work when it cuts the group stream."""
+    wl, groups = _random_sharing_batch(seed, decode=True)
+    assert wl.is_decode
+    e, _, _ = check_step(wl, groups=groups)
+    print(f"seed {seed}: S={wl.num_seqs} Hq={wl.num_q_heads} Hkv={wl.num_kv_heads} "
+          f"D={wl.head_dim} {wl.q_dtype}/{wl.kv_dtype} groups={[len(g) for g in groups[0]]} "
           f"prefix blocks={groups[1]}: {e}", flush=True)
 
 

@@ -52,6 +52,16 @@ def test_random_sharing_batches(seed):
         PM.replay_workload(wl, waves=waves, groups=groups)
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_random_sharing_decode_batches(seed):
+    """The GPU suite's sharing batches as decode steps: the group stream is
+    cut with its segment start cost."""
+    wl, groups = _random_sharing_batch(seed, decode=True)
+    for waves in ((512, 1024, 1024), (37, 13, 29), (8192, 8192, 8192)):
+        _, lay, _ = PM.replay_workload(wl, waves=waves, groups=groups)
+        assert lay.part_cost[2] == PM.GROUP_COST_NO_SPANS
+
+
 @pytest.mark.parametrize("name,P", [("c1", None), ("c2", None), ("c3", None), ("c3", 0),
                                     ("c4", None), ("c4", 0), ("c5", 0)])
 def test_full_configs_without_groups(name, P):
