@@ -1160,9 +1160,6 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         // the last (at most 2 PF) blocks of the chunk are finished by a short
         // tail that refills only while blocks remain.
         T ring[PF + 1];
-#pragma unroll
-        for (int r = 0; r < PF; ++r)
-            if (r < cnt) fetch(ring[r], r);
         // The chunk's fp8 block scales, loaded before the ring's first
         // blocks, are taken here, once. Left pending into the loop, their
         // read in every block step waited for all the loads in flight behind
@@ -1172,29 +1169,58 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         // drains one block of the ring once per loop step, and the
         // long-context batch measured faster with it than with the ring
         // kept full.)
-        if constexpr (kFp8Cache) {
+        auto take_scales = [&]() {
+            if constexpr (kFp8Cache) {
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                take_reg(my_ks_w[w]);
-                take_reg(my_vs_w[w]);
+                for (int w = 0; w < NW; ++w) {
+                    take_reg(my_ks_w[w]);
+                    take_reg(my_vs_w[w]);
+                }
             }
-        }
+        };
         int i0 = 0;
-        for (; i0 + 2 * PF < cnt; i0 += PF + 1) {
+        auto steady = [&]() {
+            for (; i0 + 2 * PF < cnt; i0 += PF + 1) {
 #pragma unroll
-            for (int r = 0; r <= PF; ++r) {
-                fetch(ring[(r + PF) % (PF + 1)], i0 + r + PF);
-                // fp8: the refill is issued before the step waits for its
-                // block (the scheduler otherwise placed it after the wait
-                // for the block's K, so a wave stalled there had one block
-                // fewer in flight); the parallel-sampling pass measured
-                // 113-114 -> 111.7 us. The bf16 loop measured slower with it.
-                if constexpr (kFp8Cache) __builtin_amdgcn_sched_barrier(0);
-                consume(ring[r], i0 + r);
-                // keep the steps in order: the scheduler would otherwise hoist
-                // later steps' products above their loads' waits
+                for (int r = 0; r <= PF; ++r) {
+                    fetch(ring[(r + PF) % (PF + 1)], i0 + r + PF);
+                    // fp8: the refill is issued before the step waits for
+                    // its block (the scheduler otherwise placed it after the
+                    // wait for the block's K, so a wave stalled there had one
+                    // block fewer in flight); the parallel-sampling pass
+                    // measured 113-114 -> 111.7 us
+                    if constexpr (kFp8Cache) __builtin_amdgcn_sched_barrier(0);
+                    consume(ring[r], i0 + r);
+                    // keep the steps in order: the scheduler would otherwise
+                    // hoist later steps' products above their loads' waits
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        // bf16 and f32: a chunk long enough for the steady loop fetches its
+        // first PF blocks unconditionally and in order, and runs the loop
+        // inside that branch. Entered after the conditional fetches (or with
+        // the first block's loads scheduled after the second's), the loop's
+        // head took the first block for the newest in flight and waited
+        // for every load but the step's refill, draining the ring once per
+        // loop step; with exact waits C2's pass went from 84.2 to 83.8 us
+        // and C3's from 677 to 675 (alternating runs, each after a pause).
+        // The fp8 loop's waits were already exact, and it measured slower.
+        constexpr bool kOrdered = !kFp8Cache;
+        if (kOrdered && cnt > 2 * PF) {
+#pragma unroll
+            for (int r = 0; r < PF; ++r) {
+                fetch(ring[r], r);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            take_scales();
+            steady();
+        } else {
+#pragma unroll
+            for (int r = 0; r < PF; ++r)
+                if (r < cnt) fetch(ring[r], r);
+            take_scales();
+            if constexpr (!kOrdered) steady();
         }
 #pragma unroll
         for (int r = 0; r <= 2 * PF; ++r) {
