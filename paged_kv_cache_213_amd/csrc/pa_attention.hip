@@ -733,10 +733,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 #define PA_PREFETCH 2
 #endif
 // Registers of block ids per lane: a chunk of the narrow kernel holds up to
-// 64 times this many blocks. Measured (decode step with append, three
-// alternating runs each): 2 left the Llama-3-8B-shaped step unchanged within
-// its run-to-run spread and made the 256-sequence long-context step 4%
-// slower than 1. An fp8 chunk carries half the bytes of a bf16 one for the
+// 64 times this many blocks. For bf16 caches 2 left the Llama-3-8B-shaped
+// and the long-context passes within 1 us of 1 (alternating runs, each
+// after a pause). An fp8 chunk carries half the bytes of a bf16 one for the
 // same drain and refill of the ring at its end: with 2, the fp8
 // parallel-sampling pass went from 114.9-118.1 to 112.1-112.9 us (the same
 // batch without its groups 369 -> 368 us); 4 gave no more.
@@ -1165,10 +1164,8 @@ __device__ __forceinline__ void run_segment(const AttnArgs& a, const TileDesc td
         // read in every block step waited for all the loads in flight behind
         // them (the loop's entry and back edge disagree on how many follow
         // them), draining the ring once per block. (The query operands,
-        // loaded at the segment's start, are left to the loop: their wait
-        // drains one block of the ring once per loop step, and the
-        // long-context batch measured faster with it than with the ring
-        // kept full.)
+        // loaded at the segment's start, are older than every block of the
+        // ring: the first step's wait covers them.)
         auto take_scales = [&]() {
             if constexpr (kFp8Cache) {
 #pragma unroll
@@ -1566,7 +1563,10 @@ __global__ void fp8_decode_kernel(const uint8_t* in, float* out, int n) {
 // registers would allow two or three. One wave per SIMD with two blocks in
 // flight beyond the one in use measured fastest: half the pieces of two
 // waves per SIMD, so fewer segments are cut (a cheaper merge) and fewer
-// waves restart their block ring at a segment boundary.
+// waves restart their block ring at a segment boundary. With registers
+// budgeted for two waves per SIMD and twice the grid (alternating runs, each
+// after a pause): Llama-3-8B-shaped decode 83.5 -> 97.6 us, long-context
+// 675 -> 725 us, fp8 parallel sampling 110.5 -> 113.6 us.
 #ifndef PA_NARROW_MAX_WAVES
 #define PA_NARROW_MAX_WAVES 1
 #endif
