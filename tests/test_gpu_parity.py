@@ -256,6 +256,22 @@ def test_other_head_shapes(D, G):
     _check_step(wl)
 
 
+@pytest.mark.parametrize("kv,span", [("bf16", 1), ("fp8", 1), ("bf16", 64)])
+def test_very_long_context(kv, span):
+    """A 128k-token context (8192 blocks, four times the longest of the
+    long-context batch) beside shorter ones, at the balanced split: its
+    segment is cut into hundreds of pieces, each taking its block ids in
+    many chunks, and the merge combines them; with span 64 the last 64
+    tokens of the long sequence are a chunked-prefill span."""
+    lens = [131072, 70001, 4097, 5]
+    ql = [span, 1, 1, 1]
+    wl = W.custom_workload(lens, ql, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                           q_dtype="bf16", kv_dtype=kv, partition_size=0, seed=77,
+                           name=f"long-{kv}-{span}")
+    e, _, _ = _check_step(wl, partition_size=0, hybrid=span > 1)
+    print(f"128k context {kv} span {span}: {e}", flush=True)
+
+
 def test_fp32_hybrid_span():
     wl = W.custom_workload([50, 33, 120], [20, 1, 33], num_q_heads=2, num_kv_heads=1, head_dim=64,
                            q_dtype="f32", kv_dtype="f32", seed=11, partition_size=32)
