@@ -272,6 +272,18 @@ def test_very_long_context(kv, span):
     print(f"128k context {kv} span {span}: {e}", flush=True)
 
 
+def test_many_sequences():
+    """6000 single-token decodes over 1 to 300 keys (6000 tiles, near the
+    8192-tile limit of a call), at the balanced split: the plan's loops over
+    tiles and pieces and the merge's record list at their widest."""
+    rng = np.random.default_rng(91)
+    lens = rng.integers(1, 301, 6000)
+    wl = W.custom_workload(lens, num_q_heads=8, num_kv_heads=2, head_dim=64, q_dtype="bf16",
+                           kv_dtype="bf16", partition_size=0, seed=92, name="many-seqs")
+    e, _, _ = _check_step(wl, partition_size=0)
+    print(f"6000 sequences: {e}", flush=True)
+
+
 def test_fp32_hybrid_span():
     wl = W.custom_workload([50, 33, 120], [20, 1, 33], num_q_heads=2, num_kv_heads=1, head_dim=64,
                            q_dtype="f32", kv_dtype="f32", seed=11, partition_size=32)
