@@ -20,9 +20,11 @@
 // The cost of a segment's start, in blocks of work, when pieces are
 // balanced (the plan cuts pieces at equal blocks + cost). A span segment
 // starts by loading 128 query rows and ends by writing 128 output rows, some
-// six blocks' worth of K/V traffic; a narrow segment's setup hides under its
-// first loads (measured: a cost of 2 to 5 left the decode batches' times
-// unchanged or slower, while the span kernel gained 7% at 6). A group
+// six blocks' worth of K/V traffic (the span kernel gained 7% at 6). A
+// narrow segment's setup mostly hides under its first loads: a cost of 3,
+// measured with a pause before each run, left the Llama-3-8B-shaped batch
+// unchanged, gained 0.3-1% on the long-context and fp8 batches and lost 1%
+// on the hybrid batch and 10% on a tiny one, so narrow segments carry none. A group
 // tile's segment starts with a chain of dependent loads (its members'
 // entries, their query rows, the block ids, the first blocks and their
 // scales): timed per wave on the parallel-sampling batch, 5.9 us per segment
