@@ -24,8 +24,8 @@
 // narrow segment's setup mostly hides under its first loads: a cost of 3,
 // measured with a pause before each run, left the Llama-3-8B-shaped batch
 // unchanged, gained 0.3-1% on the long-context and fp8 batches and lost 1%
-// on the hybrid batch and 10% on a tiny one, so narrow segments carry none. A group
-// tile's segment starts with a chain of dependent loads (its members'
+// on the hybrid batch and 10% on a tiny one, so narrow segments carry none.
+// A group tile's segment starts with a chain of dependent loads (its members'
 // entries, their query rows, the block ids, the first blocks and their
 // scales): timed per wave on the parallel-sampling batch, 5.9 us per segment
 // against 0.73 us per fp8 block, so about eight blocks. It is charged where
